@@ -1,0 +1,153 @@
+"""CPU oracle for the Q4_K weight-only matmul -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding) never
+imports, links or calls anything here, and this package shares no code with it.
+
+Contents
+  * ctypes wrappers over ``q4k_oracle.c`` (fp16/bf16 scalars, field unpack,
+    fp32 dequant, bf16 of the fp32 weight, fp64 contraction with sum |w*x|);
+  * ``q4k_pack`` -- an independent bit-writer that packs fields into blocks,
+    and the min/max quantiser used for the round-trip invariant.
+
+The format and the arithmetic are stated in the header of ``q4k_oracle.c``
+(GGUF's Q4_K block, the format of the Qwen3-4B-Q4_K_M model named in the
+genie-ai-runtime README, "At a glance").
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+BLOCK_BYTES = 144
+QK = 256
+
+_lib = None
+
+
+def lib():
+    """Load liboracle_q4k.so, compiling it first only if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_half_to_double.restype = ctypes.c_double
+        L.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_float.restype = ctypes.c_float
+        L.oracle_float_to_bf16_rne.argtypes = [ctypes.c_float]
+        L.oracle_float_to_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_unpack_fields.argtypes = [u8p, ctypes.c_long, u8p, u8p, u8p,
+                                           u16p, u16p]
+        L.oracle_unpack_fields.restype = None
+        L.oracle_dequant_f32.argtypes = [u8p, ctypes.c_long, f32p]
+        L.oracle_dequant_f32.restype = None
+        L.oracle_dequant_bf16.argtypes = [u8p, ctypes.c_long, u16p]
+        L.oracle_dequant_bf16.restype = None
+        L.oracle_gemm.argtypes = [u8p, u16p, f64p, f64p, ctypes.c_long,
+                                  ctypes.c_long, ctypes.c_long]
+        L.oracle_gemm.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _blocks(W):
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    if W.size % BLOCK_BYTES:
+        raise ValueError("weight bytes are not a whole number of 144-byte blocks")
+    return W, W.size // BLOCK_BYTES
+
+
+def half_to_double(h: int) -> float:
+    return lib().oracle_half_to_double(int(h))
+
+
+def bf16_to_float(b: int) -> float:
+    return lib().oracle_bf16_to_float(int(b))
+
+
+def float_to_bf16_rne(x) -> np.ndarray:
+    """Vector of binary32 values -> bf16 bit patterns (uint16)."""
+    x = np.asarray(x, dtype=np.float32).ravel()
+    f = lib().oracle_float_to_bf16_rne
+    return np.array([f(float(v)) for v in x], dtype=np.uint16)
+
+
+def unpack_fields(W):
+    """Per-block fields: q[nb,256], sc[nb,8], m[nb,8], d_bits[nb], dmin_bits[nb]."""
+    W, nb = _blocks(W)
+    q = np.zeros((nb, QK), np.uint8)
+    sc = np.zeros((nb, 8), np.uint8)
+    m = np.zeros((nb, 8), np.uint8)
+    d = np.zeros(nb, np.uint16)
+    dm = np.zeros(nb, np.uint16)
+    lib().oracle_unpack_fields(_ptr(W, ctypes.c_uint8), nb, _ptr(q, ctypes.c_uint8),
+                               _ptr(sc, ctypes.c_uint8), _ptr(m, ctypes.c_uint8),
+                               _ptr(d, ctypes.c_uint16), _ptr(dm, ctypes.c_uint16))
+    return q, sc, m, d, dm
+
+
+def dequant_f32(W) -> np.ndarray:
+    """fp32 weights, 256 per block, in block order."""
+    W, nb = _blocks(W)
+    w = np.zeros(nb * QK, np.float32)
+    lib().oracle_dequant_f32(_ptr(W, ctypes.c_uint8), nb, _ptr(w, ctypes.c_float))
+    return w
+
+
+def dequant_bf16(W) -> np.ndarray:
+    """bf16 (round-to-nearest-even) of the fp32 weights, as uint16 bits."""
+    W, nb = _blocks(W)
+    w = np.zeros(nb * QK, np.uint16)
+    lib().oracle_dequant_bf16(_ptr(W, ctypes.c_uint8), nb, _ptr(w, ctypes.c_uint16))
+    return w
+
+
+def gemm(W, X_bf16, N: int, K: int):
+    """Y = X . Wdq^T in fp64 and A = sum |w*x| (M x N each).
+
+    W: uint8 bytes of N rows x K/256 blocks; X_bf16: uint16 array (M, K).
+    """
+    W, nb = _blocks(W)
+    X = np.ascontiguousarray(X_bf16, dtype=np.uint16)
+    if X.ndim == 1:
+        X = X.reshape(1, -1)
+    M = X.shape[0]
+    if X.shape[1] != K or nb != N * (K // QK) or K % QK:
+        raise ValueError("shape mismatch between W, X, N and K")
+    Y = np.zeros((M, N), np.float64)
+    A = np.zeros((M, N), np.float64)
+    rc = lib().oracle_gemm(_ptr(W, ctypes.c_uint8), _ptr(X, ctypes.c_uint16),
+                           _ptr(Y, ctypes.c_double), _ptr(A, ctypes.c_double),
+                           M, N, K)
+    if rc != 0:
+        raise RuntimeError("oracle_gemm failed")
+    return Y, A
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def tolerance(A: np.ndarray) -> np.ndarray:
+    """Per-element bound on |y_gpu - y_ref|: 2e-3 * sum|w*x| + 1e-5."""
+    return 2e-3 * A + 1e-5
+
+
+def within_tolerance(y, Y_ref, A) -> np.ndarray:
+    """Boolean mask of the elements that satisfy the bound (NaN never does)."""
+    y = np.asarray(y, np.float64)
+    return np.abs(y - Y_ref) <= tolerance(A)
