@@ -1,0 +1,246 @@
+"""Benchmark of the Q4_K weight-only matmul on one MI355X.
+
+Headline (value): M = 1 weight bandwidth over one Qwen3-4B decode layer -- the
+seven Q4_K projections q, k, v, o, gate, up, down at one token, each a GEMV
+(0.5625 bytes per weight).  A step is one pass over the seven projections.
+Second figure (prefill): TFLOP/s of the same seven projections at M = 2048
+tokens on the MFMA path.
+
+Protocol.  Inputs are seeded synthetic tensors resident in HBM before timing.
+Weights rotate over enough identical copies (>= 1 GiB) that no step finds its
+weights in the 256 MB last-level cache.  W warm-up steps run untimed; the K
+timed steps are captured in a HIP graph (launch overhead out of the timed
+region, kernels back to back) and bracketed by HIP events recorded on the
+stream the kernels run on.  The CPU oracle is timed on a bounded sample of the
+same workload for the cpu_baseline field.
+
+    python bench.py [--steps K] [--warmup W] [--prefill-steps P] [--no-cpu]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import q4k_inputs as qi  # noqa: E402
+
+METRIC = "Q4_K matmul: M=1 weight GB/s (% HBM peak); M=2048 TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+BYTES_PER_WEIGHT = 144 / 256
+ROTATION_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    return ap.parse_args()
+
+
+def timed(torch, fn, steps, warmup, use_graph):
+    """Run fn(i) for warm-up, then time `steps` calls; returns seconds."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(steps):
+                    fn(warmup + i)
+        torch.cuda.synchronize()
+        g.replay()                              # first replay uploads the graph
+        torch.cuda.synchronize()
+        run = g.replay
+    else:
+        def run():
+            for i in range(steps):
+                fn(warmup + i)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    run()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3
+
+
+def decode_leg(torch, jq4k, args):
+    layer = qi.decode_layer(1, 0, 1)
+    layer_bytes = sum(W.nbytes for _, _, _, W, _ in layer)
+    copies = max(2, math.ceil(ROTATION_BYTES / layer_bytes))
+    Ws = [[torch.from_numpy(W).to("cuda:0") for _, _, _, W, _ in layer]]
+    for _ in range(copies - 1):
+        Ws.append([w.clone() for w in Ws[0]])
+    Xs = [torch.from_numpy(X.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+          for _, _, _, _, X in layer]
+    Ys = [torch.empty((1, N), dtype=torch.float32, device="cuda:0") for _, N, _, _, _ in layer]
+    L = jq4k.raw()
+
+    def step(i):
+        Wc = Ws[i % copies]
+        s = torch.cuda.current_stream().cuda_stream
+        for p, (_, N, K, _, _) in enumerate(layer):
+            rc = L.jq4k_gemv(Wc[p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(), 1, N, K, s)
+            if rc:
+                raise RuntimeError(jq4k.strerror(rc))
+
+    secs = timed(torch, step, args.steps, args.warmup, not args.eager)
+    per_proj = {}
+    for p, (name, N, K, W, _) in enumerate(layer):
+        def one(i, p=p, N=N, K=K):
+            s = torch.cuda.current_stream().cuda_stream
+            L.jq4k_gemv(Ws[i % copies][p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(),
+                        1, N, K, s)
+        t = timed(torch, one, args.steps, 4, not args.eager)
+        per_proj[name] = {"N": N, "K": K, "us": round(t / args.steps * 1e6, 3),
+                          "GB_s": round(W.nbytes * args.steps / t / 1e9, 1)}
+    return layer, layer_bytes, copies, secs, per_proj
+
+
+def prefill_leg(torch, jq4k, args):
+    M = 2048
+    projs = [qi.prefill_projection(3, 0, p, M) for p in range(7)]
+    flops = sum(2.0 * M * N * K for _, N, K, _, _ in projs)
+    copies = 2
+    Ws = [[torch.from_numpy(W).to("cuda:0") for _, _, _, W, _ in projs]]
+    Ws.append([w.clone() for w in Ws[0]])
+    Xs = [torch.from_numpy(X.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+          for _, _, _, _, X in projs]
+    Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda:0") for _, N, _, _, _ in projs]
+    L = jq4k.raw()
+
+    def step(i):
+        Wc = Ws[i % copies]
+        s = torch.cuda.current_stream().cuda_stream
+        for p, (_, N, K, _, _) in enumerate(projs):
+            rc = L.jq4k_gemm(Wc[p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(), M, N, K, s)
+            if rc:
+                raise RuntimeError(jq4k.strerror(rc))
+
+    secs = timed(torch, step, args.prefill_steps, 2, not args.eager)
+    per_proj = {}
+    for p, (name, N, K, _, _) in enumerate(projs):
+        def one(i, p=p, N=N, K=K):
+            s = torch.cuda.current_stream().cuda_stream
+            L.jq4k_gemm(Ws[i % copies][p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(),
+                        M, N, K, s)
+        t = timed(torch, one, args.prefill_steps, 1, not args.eager)
+        per_proj[name] = {"N": N, "K": K, "us": round(t / args.prefill_steps * 1e6, 2),
+                          "TFLOP_s": round(2.0 * M * N * K * args.prefill_steps / t / 1e12, 1)}
+    return flops, secs, per_proj
+
+
+def cpu_baseline(layer, budget_s=12.0):
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for _, N, K, W, X in layer:
+            oracle.gemm(W, X, N, K)
+        reps += 1
+    secs = time.perf_counter() - t0
+    weights = sum(N * K for _, N, K, _, _ in layer) * reps
+    return {"value": round(weights * BYTES_PER_WEIGHT / secs / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} passes of the full decode layer (7 projections, M=1) "
+                      f"in {secs:.1f} s, fp32 dequant + fp64 accumulate"}
+
+
+def cpu_baseline_prefill(budget_rows=64):
+    import oracle
+    M = 2048
+    t0 = time.perf_counter()
+    flops = 0.0
+    for p in range(7):
+        _, N, K, W, X = qi.prefill_projection(3, 0, p, M)
+        oracle.gemm(W[:budget_rows], X, budget_rows, K)
+        flops += 2.0 * M * budget_rows * K
+    secs = time.perf_counter() - t0
+    return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {budget_rows} rows of each of the 7 projections at M=2048 "
+                      f"({flops / 1e9:.1f} GFLOP in {secs:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the matmul shards by rows of W, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import q4_weight_only_amd as jq4k
+    jq4k.raw()
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+
+    layer, layer_bytes, copies, secs, per_proj = decode_leg(torch, jq4k, args)
+    gbs = layer_bytes * args.steps / secs / 1e9
+    flops, psecs, p_per = prefill_leg(torch, jq4k, args)
+    tflops = flops * args.prefill_steps / psecs / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(secs / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-4B decode layer, 7 Q4_K projections at M=1 "
+                        "(q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up 9728x2560, "
+                        "down 2560x9728), seeds [1,0,p]",
+            "weight_bytes_per_step": layer_bytes,
+            "rotation_copies": copies,
+            "launch": "eager" if args.eager else "hip-graph",
+            "device": torch.cuda.get_device_name(0),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "q4k_gemv_kernel",
+            "avg_launch_us": round(secs / (args.steps * 7) * 1e6, 3),
+            "bytes_per_launch": layer_bytes / 7,
+        },
+        "per_projection": per_proj,
+        "prefill": {
+            "workload": "Qwen3-4B layer, 7 Q4_K projections at M=2048, seeds [3,0,p]",
+            "value": round(tflops, 1), "unit": "TFLOP/s", "steps": args.prefill_steps,
+            "ms_per_step": round(psecs / args.prefill_steps * 1e3, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "q4k_gemm_mfma_kernel"},
+            "per_projection": p_per,
+        },
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(layer)
+        out["prefill"]["cpu_baseline"] = cpu_baseline_prefill()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

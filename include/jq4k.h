@@ -1,0 +1,146 @@
+/*
+ * jq4k.h -- Q4_K weight-only matmul for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  The genie-ai-runtime README ("At a glance"; "Project
+ * layout", src/kernels/) names the two hot kernels of its GGUF engine: an
+ * "INT4 dequant-fused GEMV" for decode and a "tensor-core MMQ Q4_K prefill"
+ * matmul, run on the Qwen3-4B-Q4_K_M model.  Both compute, for every linear
+ * projection of the model,
+ *
+ *        Y[m][n] = sum_k  w[n][k] * x[m][k]        (Y = X . W^T)
+ *
+ * where W is stored in GGUF's Q4_K format and dequantised on the fly.
+ *
+ * Q4_K block (GGUF): 256 weights in 144 bytes,
+ *     d, dmin        binary16 super-block scale and min (little-endian)
+ *     scales[12]     eight 6-bit sub-block scales sc_j and eight 6-bit mins
+ *                    m_j: j < 4 in the low six bits of scales[j] / scales[j+4];
+ *                    j >= 4 low nibbles in scales[j+4] (sc low, m high) and
+ *                    top two bits in bits 6..7 of scales[j-4] (sc) / scales[j] (m)
+ *     qs[128]        4-bit quants: weight i in byte 32*(i/64) + i%32, low
+ *                    nibble when (i/32) is even, high nibble otherwise
+ *     w_i = d * sc_s * q_i - dmin * m_s,   s = i / 32.
+ *
+ * Layouts (all dense, row-major, no leading-dimension arguments):
+ *     W  N rows x K/256 blocks; row n is output feature n:  W[n*(K/256) + kb]
+ *     X  M x K bfloat16 (raw bit patterns)
+ *     Y  M x N fp32
+ *
+ * Numerics.  Y is overwritten (never accumulated into).  Results are
+ * deterministic: the same inputs on the same device give bit-identical Y.
+ * Every element meets |y - y_exact| <= 2e-3 * sum_k |w*x| + 1e-5 where w is
+ * the fp32 dequantised weight (see jq4k_dequant_f32).  The GEMM path for M > 1
+ * contracts bfloat16 tiles of w (round-to-nearest-even of the fp32 weight,
+ * exactly what jq4k_dequant_bf16 returns) on the matrix cores with fp32
+ * accumulation; the M = 1 path works on the 4-bit codes directly with fp32
+ * accumulation.  Inf/NaN in d or dmin propagate per IEEE.  The M = 1 kernel
+ * forms sum (128+q)*x per 32-weight sub-block, so activations beyond about
+ * 1e35 in magnitude can overflow there.
+ *
+ * Ownership and execution.  All pointers are device pointers owned by the
+ * caller; the library allocates no memory and keeps no state beyond a cache
+ * of device attributes.  Work is enqueued on `stream` (0 = the null stream);
+ * nothing synchronises with the host, so errors raised while the kernel runs
+ * surface at the caller's next synchronisation.  Calls are thread-safe.
+ *
+ * Return codes.  0 on success.  JQ4K_EINVAL / JQ4K_EALIGN when the arguments
+ * are rejected -- checked before any HIP call, so nothing is launched.  A
+ * positive value is the hipError_t reported when the launch failed.
+ */
+#ifndef JQ4K_H
+#define JQ4K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same declaration as in HIP's runtime headers. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef struct {
+    uint16_t d;          /* binary16 bits */
+    uint16_t dmin;       /* binary16 bits */
+    uint8_t scales[12];
+    uint8_t qs[128];
+} block_q4_K;
+
+#ifdef __cplusplus
+static_assert(sizeof(block_q4_K) == 144, "block_q4_K must be 144 bytes");
+#else
+_Static_assert(sizeof(block_q4_K) == 144, "block_q4_K must be 144 bytes");
+#endif
+
+typedef uint16_t jq4k_bf16; /* bfloat16 bit pattern */
+
+#define JQ4K_OK 0
+#define JQ4K_EINVAL (-1) /* bad size, null pointer with a nonzero size,  */
+                         /* K not a positive multiple of 256, M != 1 for */
+                         /* the GEMV, K above the GEMV limit, bad path   */
+#define JQ4K_EALIGN (-2) /* W or X not 16-byte aligned, Y not 4-byte    */
+
+/* Largest K the M = 1 kernel accepts (it keeps x in LDS). */
+#define JQ4K_GEMV_MAX_K 16384
+
+/* Decode GEMV, M must be 1: Y[0..N) = sum_k w[n][k] * X[k].
+ * The genie-ai-runtime README, "At a glance": INT4 dequant-fused GEMV.
+ * W: N*(K/256) blocks, 16-byte aligned.  X: K bf16, 16-byte aligned.
+ * Y: N floats, 4-byte aligned.  N == 0 returns 0 without launching.
+ * Errors: JQ4K_EINVAL for M != 1, N < 0, K <= 0, K % 256 != 0,
+ * K > JQ4K_GEMV_MAX_K, or a null pointer; JQ4K_EALIGN for misalignment. */
+int jq4k_gemv(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
+              int M, int N, int K, hipStream_t stream);
+
+/* Matmul for any M >= 0: Y (M x N) = X (M x K) . W^T.
+ * The genie-ai-runtime README, "At a glance": tensor-core MMQ Q4_K prefill.
+ * M == 1 runs the decode GEMV when K <= JQ4K_GEMV_MAX_K; larger M runs the
+ * dequantise-to-LDS bf16 MFMA kernels.  M == 0 or N == 0 returns 0 without
+ * launching.  Same pointer, alignment and K rules as jq4k_gemv. */
+int jq4k_gemm(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
+              int M, int N, int K, hipStream_t stream);
+
+/* Kernel paths for jq4k_gemm_path (tests and benchmarks reach every path). */
+#define JQ4K_PATH_AUTO 0 /* what jq4k_gemm picks                        */
+#define JQ4K_PATH_GEMV 1 /* the M = 1 kernel (M must be 1)               */
+#define JQ4K_PATH_MFMA 2 /* the MFMA kernel, tile chosen by shape        */
+#define JQ4K_PATH_MFMA_T64 3  /* MFMA kernel, 64-row M tile              */
+#define JQ4K_PATH_MFMA_T128 4 /* MFMA kernel, 128-row M tile             */
+#define JQ4K_PATH_MFMA_T256 5 /* MFMA kernel, 256-row M tile             */
+
+/* jq4k_gemm with an explicit kernel path; JQ4K_EINVAL for an unknown path
+ * or JQ4K_PATH_GEMV with M != 1.  Results meet the same bound on every path. */
+int jq4k_gemm_path(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
+                   int M, int N, int K, int path, hipStream_t stream);
+
+/* Test exports.  They run the same device unpacking code as the matmul
+ * kernels, one block per 256 outputs, so their outputs pin that code.
+ *   jq4k_unpack_fields: q[256*nblocks] (0..15), sc[8*nblocks], m[8*nblocks]
+ *                       (0..63), in block order; byte outputs need no
+ *                       alignment.
+ *   jq4k_dequant_f32:   w[256*nblocks], the fp32 weight d*sc*q - dmin*m
+ *                       rounded once (round-to-nearest-even); 4-byte aligned.
+ *   jq4k_dequant_bf16:  w[256*nblocks], bfloat16 of that fp32 weight
+ *                       (round-to-nearest-even), the values the MFMA path
+ *                       multiplies; 4-byte aligned.
+ * W must be 16-byte aligned.  nblocks == 0 returns 0; nblocks < 0 or null
+ * pointers give JQ4K_EINVAL. */
+int jq4k_unpack_fields(const block_q4_K *W, long nblocks, uint8_t *q,
+                       uint8_t *sc, uint8_t *m, hipStream_t stream);
+int jq4k_dequant_f32(const block_q4_K *W, long nblocks, float *w,
+                     hipStream_t stream);
+int jq4k_dequant_bf16(const block_q4_K *W, long nblocks, jq4k_bf16 *w,
+                      hipStream_t stream);
+
+/* Text for a return code (static storage). */
+const char *jq4k_strerror(int code);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int jq4k_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JQ4K_H */

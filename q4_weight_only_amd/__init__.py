@@ -1,0 +1,165 @@
+"""Python binding of libjq4k (Q4_K weight-only matmul for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libjq4k.so; torch supplies device memory and the current stream.
+There is no fallback -- if the library is not built, loading fails loudly.
+
+    import q4_weight_only_amd as jq4k
+    jq4k.gemm(W, X, Y)     # W uint8 (N, K/256*144), X bf16 (M, K), Y fp32 (M, N)
+
+The C entry points (include/jq4k.h) are also exposed with the same names and
+raw integer pointers in ``jq4k.raw``.
+"""
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libjq4k.so")
+HEADER = os.path.join(HERE, "..", "include", "jq4k.h")
+
+OK, EINVAL, EALIGN = 0, -1, -2
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_T64, PATH_MFMA_T128, PATH_MFMA_T256 = range(6)
+GEMV_MAX_K = 16384
+BLOCK_BYTES = 144
+QK = 256
+
+
+class Jq4kError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+_raw = None
+
+
+def _load():
+    global _raw
+    if _raw is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"libjq4k.so is not built ({LIB_PATH}); run "
+                "`python q4_weight_only_amd/build.py` or __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, l = ctypes.c_void_p, ctypes.c_int, ctypes.c_long
+        for name in ("jq4k_gemv", "jq4k_gemm"):
+            f = getattr(L, name)
+            f.argtypes = [vp, vp, vp, i, i, i, vp]
+            f.restype = i
+        L.jq4k_gemm_path.argtypes = [vp, vp, vp, i, i, i, i, vp]
+        L.jq4k_gemm_path.restype = i
+        L.jq4k_unpack_fields.argtypes = [vp, l, vp, vp, vp, vp]
+        L.jq4k_unpack_fields.restype = i
+        L.jq4k_dequant_f32.argtypes = [vp, l, vp, vp]
+        L.jq4k_dequant_f32.restype = i
+        L.jq4k_dequant_bf16.argtypes = [vp, l, vp, vp]
+        L.jq4k_dequant_bf16.restype = i
+        L.jq4k_strerror.argtypes = [i]
+        L.jq4k_strerror.restype = ctypes.c_char_p
+        L.jq4k_version.argtypes = []
+        L.jq4k_version.restype = i
+        _raw = L
+    return _raw
+
+
+def raw():
+    """The loaded ctypes library (C names, raw pointers)."""
+    return _load()
+
+
+def declared_symbols():
+    """Function names that include/jq4k.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(jq4k_\w+)\s*\(", text, re.M)))
+
+
+def strerror(code: int) -> str:
+    return _load().jq4k_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return _load().jq4k_version()
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise Jq4kError(rc, where)
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _shapes(W, X, Y):
+    import torch
+    if X.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("X must hold bfloat16 values (bf16 or raw 16-bit)")
+    if W.dtype != torch.uint8 or Y.dtype != torch.float32:
+        raise TypeError("W must be uint8 block bytes and Y float32")
+    for name, t in (("W", W), ("X", X), ("Y", Y)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if X.dim() == 1:
+        M, K, N = 1, X.numel(), Y.numel()
+    else:
+        M, K = X.shape
+        N = Y.shape[-1] if Y.dim() == 2 else Y.numel() // max(M, 1)
+    if W.numel() != N * (K // QK) * BLOCK_BYTES or Y.numel() != M * N:
+        raise ValueError("W, X, Y sizes disagree")
+    return int(M), int(N), int(K)
+
+
+def gemv(W, X, Y, stream=None):
+    """Y[0, :] = X[0, :] . W^T for one token (jq4k_gemv)."""
+    M, N, K = _shapes(W, X, Y)
+    _check(_load().jq4k_gemv(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K,
+                             _stream(stream)), "jq4k_gemv")
+    return Y
+
+
+def gemm(W, X, Y, stream=None, path=PATH_AUTO):
+    """Y = X . W^T (jq4k_gemm, or jq4k_gemm_path with an explicit kernel path)."""
+    M, N, K = _shapes(W, X, Y)
+    L = _load()
+    if path == PATH_AUTO:
+        rc = L.jq4k_gemm(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K, _stream(stream))
+    else:
+        rc = L.jq4k_gemm_path(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K, int(path),
+                              _stream(stream))
+    _check(rc, "jq4k_gemm")
+    return Y
+
+
+def _nblocks(W):
+    if W.numel() % BLOCK_BYTES:
+        raise ValueError("W is not a whole number of 144-byte blocks")
+    return W.numel() // BLOCK_BYTES
+
+
+def unpack_fields(W, q, sc, m, stream=None):
+    nb = _nblocks(W)
+    if q.numel() != nb * QK or sc.numel() != nb * 8 or m.numel() != nb * 8:
+        raise ValueError("output sizes disagree with W")
+    _check(_load().jq4k_unpack_fields(W.data_ptr(), nb, q.data_ptr(), sc.data_ptr(),
+                                      m.data_ptr(), _stream(stream)), "jq4k_unpack_fields")
+
+
+def dequant_f32(W, w, stream=None):
+    nb = _nblocks(W)
+    if w.numel() != nb * QK:
+        raise ValueError("output size disagrees with W")
+    _check(_load().jq4k_dequant_f32(W.data_ptr(), nb, w.data_ptr(), _stream(stream)),
+           "jq4k_dequant_f32")
+
+
+def dequant_bf16(W, w, stream=None):
+    nb = _nblocks(W)
+    if w.numel() != nb * QK:
+        raise ValueError("output size disagrees with W")
+    _check(_load().jq4k_dequant_bf16(W.data_ptr(), nb, w.data_ptr(), _stream(stream)),
+           "jq4k_dequant_bf16")

@@ -1,0 +1,215 @@
+// gemm.hip -- Q4_K matmul on the gfx950 matrix cores, for M > 1 (prefill).
+//
+// Y (M x N) = X (M x K) . W^T with W in Q4_K (genie-ai-runtime README, "At a
+// glance": "tensor-core MMQ Q4_K prefill").  Each workgroup computes a BM x BN
+// tile of Y.  The K loop advances one quarter block (64 weights = sub-blocks
+// 2c, 2c+1 of block kb) per stage:
+//   * the BN x 64 slab of W is fetched as header + 32 quant bytes per row,
+//     dequantised in registers to fp32 (fma(d*sc, q, -dmin*m), the exact
+//     value rounded once), rounded to bf16 (RNE) and written to LDS;
+//   * the BM x 64 slab of X (bf16) is copied to LDS;
+//   * four waves multiply the slabs with v_mfma_f32_32x32x16_bf16 into fp32
+//     accumulators.
+// LDS is double-buffered, so one barrier per stage suffices: the global loads
+// of stage s+1 are in flight while stage s is on the matrix cores.
+// LDS rows are 128 bytes (8 chunks of 16 bytes); chunk i of row r is stored
+// at i ^ (r & 7) so the 32 rows an MFMA operand read touches hit distinct
+// bank groups.
+//
+// Operand layouts (v_mfma_f32_32x32x16_bf16): lane l supplies row l % 32 of
+// A and column l % 32 of B, k = 8 (l / 32) .. +7 of the 16-wide k step; the
+// 16 accumulators of lane l hold column l % 32, rows 8 (r / 4) + 4 (l / 32)
+// + r % 4 for r = 0..15.
+#include "q4k_device.h"
+
+namespace jq4k {
+
+constexpr int kGemmThreads = 256;
+constexpr int kBK = 64;               // K per stage: one quarter block
+constexpr int kRowChunks = kBK / 8;   // 16-byte chunks per LDS row
+constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
+
+__device__ __forceinline__ int lds_chunk(int row, int chunk) {
+    return row * kRowChunks + (chunk ^ (row & 7));
+}
+
+template <int BM, int BN, int WM, int WN>
+struct GemmCfg {
+    static_assert(WM * WN == 4, "four waves");
+    static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
+    static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "32x32 MFMA tiles");
+    static constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;
+    static constexpr int kXChunks = BM * kRowChunks / kGemmThreads;  // per thread
+    static_assert(kXChunks >= 1 && BM * kRowChunks % kGemmThreads == 0, "X slab split");
+    static constexpr int kThreadsPerRow = kGemmThreads / BN;          // W slab split
+    static_assert(kThreadsPerRow == 1 || kThreadsPerRow == 2 || kThreadsPerRow == 4, "BN");
+    static constexpr int kQBytes = 32 / kThreadsPerRow;               // quant bytes / thread
+    static constexpr int kLdsChunks = (BM + BN) * kRowChunks;         // per buffer
+};
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(
+    const uint8_t* __restrict__ W, const uint16_t* __restrict__ X, float* __restrict__ Y,
+    int M, int N, int K, int ntiles, int per_xcd) {
+    using C = GemmCfg<BM, BN, WM, WN>;
+    __shared__ uint4 lds[2][C::kLdsChunks];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    // XCD-aware tile order: workgroup i runs on XCD i % 8; XCD x takes the
+    // contiguous tile range [x * per_xcd, (x + 1) * per_xcd) of the n-fastest
+    // tile order, so the workgroups resident on one XCD share rows of X (and
+    // its L2) while they sweep the columns of W.
+    const int ntile_n = (N + BN - 1) / BN;
+    const int lin = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (lin >= ntiles) return;
+    const int n0 = (lin % ntile_n) * BN, m0 = (lin / ntile_n) * BM;
+    const int nb = K / kQK;
+    const int nstage = K / kBK;
+
+    // ---- W slab assignment: row wr of the tile, quant bytes [qoff, qoff + kQBytes)
+    const int wr = t / C::kThreadsPerRow;
+    const int qoff = (t % C::kThreadsPerRow) * C::kQBytes;
+    const bool w_live = (n0 + wr) < N;
+    const uint8_t* wrow = W + static_cast<long>(min(n0 + wr, N - 1)) * nb * kBlockBytes;
+
+    // ---- X slab assignment: chunk g = t + 256 j -> row g / 8, chunk g % 8
+    const uint16_t* xbase = X;
+
+    uint4 xreg[C::kXChunks];
+    uint4 hreg;
+    uint32_t qreg[C::kQBytes / 4];
+
+    auto load_stage = [&](int s) {
+        const int kb = s >> 2, c = s & 3;
+#pragma unroll
+        for (int j = 0; j < C::kXChunks; ++j) {
+            const int g = t + j * kGemmThreads;
+            const int row = g >> 3, ch = g & 7;
+            const int m = m0 + row;
+            xreg[j] = (m < M) ? *reinterpret_cast<const uint4*>(
+                                    xbase + static_cast<long>(m) * K + s * kBK + ch * 8)
+                              : make_uint4(0, 0, 0, 0);
+        }
+        const uint8_t* blk = wrow + kb * kBlockBytes;
+        hreg = *reinterpret_cast<const uint4*>(blk);
+        const uint8_t* q = blk + 16 + 32 * c + qoff;
+        if constexpr (C::kQBytes == 32) {
+            const uint4 a = *reinterpret_cast<const uint4*>(q);
+            const uint4 b = *reinterpret_cast<const uint4*>(q + 16);
+            qreg[0] = a.x; qreg[1] = a.y; qreg[2] = a.z; qreg[3] = a.w;
+            qreg[4] = b.x; qreg[5] = b.y; qreg[6] = b.z; qreg[7] = b.w;
+        } else if constexpr (C::kQBytes == 16) {
+            const uint4 a = *reinterpret_cast<const uint4*>(q);
+            qreg[0] = a.x; qreg[1] = a.y; qreg[2] = a.z; qreg[3] = a.w;
+        } else {
+            const uint2 a = *reinterpret_cast<const uint2*>(q);
+            qreg[0] = a.x; qreg[1] = a.y;
+        }
+    };
+
+    auto store_stage = [&](int s, uint4* buf) {
+        const int c = s & 3;
+#pragma unroll
+        for (int j = 0; j < C::kXChunks; ++j) {
+            const int g = t + j * kGemmThreads;
+            buf[lds_chunk(g >> 3, g & 7)] = xreg[j];
+        }
+        uint4* wbuf = buf + BM * kRowChunks;
+        if (w_live) {
+            const QuarterScales sc = quarter_scales(hreg, static_cast<uint32_t>(c));
+            // 8 quant bytes -> one 16-byte chunk of the even sub-block (k offset
+            // qoff + 0..7) and one of the odd sub-block (k offset 32 + qoff + 0..7)
+#pragma unroll
+            for (int j = 0; j < C::kQBytes / 8; ++j) {
+                uint32_t lo_a[2], hi_a[2], lo_b[2], hi_b[2];
+                dequant_dword_bf16(qreg[2 * j], sc, lo_a, hi_a);
+                dequant_dword_bf16(qreg[2 * j + 1], sc, lo_b, hi_b);
+                const int ch = (qoff >> 3) + j;
+                wbuf[lds_chunk(wr, ch)] = make_uint4(lo_a[0], lo_a[1], lo_b[0], lo_b[1]);
+                wbuf[lds_chunk(wr, 4 + ch)] = make_uint4(hi_a[0], hi_a[1], hi_b[0], hi_b[1]);
+            }
+        }
+    };
+
+    float16_t acc[C::kTM][C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) acc[i][j] = float16_t{};
+
+    const int arow = wm * C::kWaveM + (lane & 31);  // A row within the tile (+32 i)
+    const int bcol = wn * C::kWaveN + (lane & 31);  // B column within the tile (+32 j)
+    const int khalf = lane >> 5;
+
+    load_stage(0);
+    for (int s = 0; s < nstage; ++s) {
+        uint4* buf = lds[s & 1];
+        store_stage(s, buf);
+        if (s + 1 < nstage) load_stage(s + 1);
+        __syncthreads();
+        const uint4* xb = buf;
+        const uint4* wb = buf + BM * kRowChunks;
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            const int ch = 2 * ks + khalf;
+            bf16x8_t a[C::kTM], b[C::kTN];
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i)
+                a[i] = __builtin_bit_cast(bf16x8_t, xb[lds_chunk(arow + 32 * i, ch)]);
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j)
+                b[j] = __builtin_bit_cast(bf16x8_t, wb[lds_chunk(bcol + 32 * j, ch)]);
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j],
+                                                                         0, 0, 0);
+        }
+    }
+
+    // ---- epilogue: fp32 Y, row-major
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) {
+            const int n = n0 + wn * C::kWaveN + 32 * j + (lane & 31);
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * C::kWaveM + 32 * i + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                if (m < M) Y[static_cast<long>(m) * N + n] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_cfg(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
+                             hipStream_t stream) {
+    const long ntiles = static_cast<long>((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+    const long per_xcd = (ntiles + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((q4k_gemm_mfma_kernel<BM, BN, WM, WN>), dim3(per_xcd * kXcds),
+                       dim3(kGemmThreads), 0, stream, W, X, Y, M, N, K,
+                       static_cast<int>(ntiles), static_cast<int>(per_xcd));
+    return hipGetLastError();
+}
+
+long gemm_tile_count(int M, int N, int tile) {
+    const int bn = tile == 64 ? 256 : 128;
+    return static_cast<long>((N + bn - 1) / bn) * ((M + tile - 1) / tile);
+}
+
+// tile: 64, 128 or 256 rows of M per workgroup.
+hipError_t launch_gemm_mfma(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
+                            int tile, hipStream_t stream) {
+    switch (tile) {
+        case 64: return launch_cfg<64, 256, 1, 4>(W, X, Y, M, N, K, stream);
+        case 128: return launch_cfg<128, 128, 2, 2>(W, X, Y, M, N, K, stream);
+        default: return launch_cfg<256, 128, 2, 2>(W, X, Y, M, N, K, stream);
+    }
+}
+
+}  // namespace jq4k

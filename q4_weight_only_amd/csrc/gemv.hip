@@ -1,0 +1,194 @@
+// gemv.hip -- the M = 1 (decode) Q4_K GEMV for gfx950.
+//
+// y[n] = sum_k w[n][k] x[k], weights dequantised in registers and never
+// materialised (genie-ai-runtime README, "At a glance": INT4 dequant-fused
+// GEMV).  HBM-bound: each weight byte is read once (0.5625 B per weight).
+//
+// Work decomposition.  A workgroup owns R consecutive rows, i.e. R*nb
+// consecutive blocks of W (nb = K/256) -- one contiguous span of memory.  The
+// span is cut into tasks of one quarter block each (header + 32 quant bytes
+// = 64 weights, sub-blocks 2c and 2c+1); 256 threads sweep the tasks in
+// rounds, so lanes 4j..4j+3 of a round take the four quarters of one block
+// and every round reads 64 consecutive blocks.  A thread's quarter c = t & 3
+// never changes.
+//
+// Arithmetic per quarter.  With s = a sub-block, the kernel uses
+//   sum_{k in s} w_k x_k = d*sc_s * sum (q_k x_k) - dmin*m_s * X_s,
+//   X_s = sum_{k in s} x_k,
+// and forms sum q_k x_k as sum (128 + q_k) x_k - 128 X_s: a byte permute puts
+// each 4-bit code q under the bf16 exponent of 128 (0x43 in the high byte
+// gives the exact bf16 value 128 + q), and v_dot2_f32_bf16 multiplies two
+// such codes by two bf16 activations per instruction with fp32 accumulation.
+// X_s and -128 X_s are computed once per workgroup in LDS.  Per 8 weights:
+// 3 mask/shift, 4 permutes, 4 dot2 -- no per-weight float conversion.
+//
+// Reduction.  The four lanes of a block are summed with two DPP quad
+// permutes; one value per block goes to LDS; after all rounds each row sums
+// its nb block values in order (deterministic, no atomics).
+//
+// LDS layout of x.  x is stored as 16-byte chunks, chunk g = 32 kb + 8 c + i
+// (i = 0..3 the even sub-block, 4..7 the odd one), with i XOR-ed by
+// (c + 4 (kb & 1)) so that the eight lanes of two neighbouring blocks read
+// eight different bank groups.
+#include "q4k_device.h"
+
+namespace jq4k {
+
+constexpr int kGemvThreads = 256;
+
+__device__ __forceinline__ int x_chunk_phys(int kb, int c, int i) {
+    return (kb << 5) | (c << 3) | (i ^ ((c + ((kb & 1) << 2)) & 7));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// 128 + q as bf16 for bytes 0,1 (SEL01) or 2,3 (SEL23) of a quant word
+// whose bytes hold one code each: result lanes (128 + q_lo, 128 + q_hi).
+constexpr uint32_t kBf16Exp128 = 0x43434343u;
+constexpr uint32_t kSel01 = 0x04010400u;
+constexpr uint32_t kSel23 = 0x04030402u;
+
+__device__ __forceinline__ float quant_dot8(uint32_t q4, uint32_t xa, uint32_t xb, float acc) {
+    acc = dot2_bf16(__builtin_amdgcn_perm(kBf16Exp128, q4, kSel01), xa, acc);
+    acc = dot2_bf16(__builtin_amdgcn_perm(kBf16Exp128, q4, kSel23), xb, acc);
+    return acc;
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+    // quad_perm [1,0,3,2] then [2,3,0,1]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    return v;
+}
+
+struct QuarterLoad {
+    uint4 hdr, qa, qb;
+};
+
+__device__ __forceinline__ QuarterLoad load_quarter(const uint8_t* blk, int c) {
+    QuarterLoad r;
+    r.hdr = load_stream16(blk);
+    r.qa = load_stream16(blk + 16 + 32 * c);
+    r.qb = load_stream16(blk + 32 + 32 * c);
+    return r;
+}
+
+// Contribution of one quarter block to its row: 64 weights.
+__device__ __forceinline__ float quarter_dot(const QuarterLoad& ld, int c, const uint4* xs,
+                                             int kb, float4 xsum) {
+    const float d = half_bits_to_float(ld.hdr.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(ld.hdr.x >> 16);
+    uint32_t scp, mp;
+    scale_min_pair(static_cast<uint32_t>(c), ld.hdr.y, ld.hdr.z, ld.hdr.w, &scp, &mp);
+
+    float acc0 = xsum.x;  // -128 X_(2c)
+    float acc1 = xsum.y;  // -128 X_(2c+1)
+    const uint32_t qw[8] = {ld.qa.x, ld.qa.y, ld.qa.z, ld.qa.w,
+                            ld.qb.x, ld.qb.y, ld.qb.z, ld.qb.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 xl = xs[x_chunk_phys(kb, c, i)];
+        const uint4 xh = xs[x_chunk_phys(kb, c, 4 + i)];
+        const uint32_t v0 = qw[2 * i], v1 = qw[2 * i + 1];
+        acc0 = quant_dot8(low_quants(v0), xl.x, xl.y, acc0);
+        acc0 = quant_dot8(low_quants(v1), xl.z, xl.w, acc0);
+        acc1 = quant_dot8(high_quants(v0), xh.x, xh.y, acc1);
+        acc1 = quant_dot8(high_quants(v1), xh.z, xh.w, acc1);
+    }
+    const float sc0 = ubyte_to_float<0>(scp), sc1 = ubyte_to_float<1>(scp);
+    const float m0 = ubyte_to_float<0>(mp), m1 = ubyte_to_float<1>(mp);
+    const float qx = sc0 * acc0 + sc1 * acc1;
+    const float mx = m0 * xsum.z + m1 * xsum.w;
+    return d * qx - dmin * mx;
+}
+
+// LDS: x chunks (nb*32 x 16 B), per-(kb, quarter) sums (nb*4 x 16 B),
+// per-block partials (R*nb floats).
+__global__ __launch_bounds__(kGemvThreads) void q4k_gemv_kernel(
+    const uint8_t* __restrict__ W, const uint4* __restrict__ X, float* __restrict__ Y,
+    int N, int nb, int R) {
+    extern __shared__ uint4 smem[];
+    uint4* xs = smem;
+    float4* xsum = reinterpret_cast<float4*>(xs + nb * 32);
+    float* part = reinterpret_cast<float*>(xsum + nb * 4);
+
+    const int t = threadIdx.x;
+    const int c = t & 3;
+    const long row0 = static_cast<long>(blockIdx.x) * R;
+    const int rows = static_cast<int>(min(static_cast<long>(R), N - row0));
+    const int ntask = rows * nb * 4;
+    const uint8_t* Wt = W + row0 * nb * kBlockBytes;
+
+    // First task's weights are requested before x is staged.
+    int b = t >> 2;
+    QuarterLoad cur = {};
+    if (t < ntask) cur = load_quarter(Wt + static_cast<long>(b) * kBlockBytes, c);
+
+    for (int g = t; g < nb * 32; g += kGemvThreads) {
+        const int kb = g >> 5, cc = (g >> 3) & 3, i = g & 7;
+        xs[x_chunk_phys(kb, cc, i)] = X[g];
+    }
+    __syncthreads();
+    for (int u = t; u < nb * 4; u += kGemvThreads) {
+        const int kb = u >> 2, cc = u & 3;
+        float s[2] = {0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 v = xs[x_chunk_phys(kb, cc, 4 * h + i)];
+                s[h] += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) +
+                        bf16_lo(v.z) + bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+            }
+        }
+        xsum[u] = make_float4(-128.f * s[0], -128.f * s[1], s[0], s[1]);
+    }
+    __syncthreads();
+
+    // Rounds: block index b advances by 64 (256 threads / 4 lanes per block).
+    const int kb_step = 64 % nb;
+    int kb = b % nb;
+    for (int tau = t; tau < ntask; tau += kGemvThreads) {
+        const int nb_next = b + 64;
+        QuarterLoad nxt = {};
+        if (tau + kGemvThreads < ntask)
+            nxt = load_quarter(Wt + static_cast<long>(nb_next) * kBlockBytes, c);
+        float p = quarter_dot(cur, c, xs, kb, xsum[kb * 4 + c]);
+        p = quad_sum(p);
+        if (c == 0) part[b] = p;
+        cur = nxt;
+        b = nb_next;
+        kb += kb_step;
+        if (kb >= nb) kb -= nb;
+    }
+    __syncthreads();
+    for (int r = t; r < rows; r += kGemvThreads) {
+        float s = 0.f;
+        for (int j = 0; j < nb; ++j) s += part[r * nb + j];
+        Y[row0 + r] = s;
+    }
+}
+
+size_t gemv_lds_bytes(int nb, int R) {
+    return static_cast<size_t>(nb) * 32 * 16 + static_cast<size_t>(nb) * 4 * 16 +
+           static_cast<size_t>(R) * nb * 4;
+}
+
+hipError_t launch_gemv(const uint8_t* W, const uint16_t* X, float* Y, int N, int K, int R,
+                       hipStream_t stream) {
+    const int nb = K / kQK;
+    const unsigned grid = static_cast<unsigned>((static_cast<long>(N) + R - 1) / R);
+    hipLaunchKernelGGL(q4k_gemv_kernel, dim3(grid), dim3(kGemvThreads), gemv_lds_bytes(nb, R),
+                       stream, W, reinterpret_cast<const uint4*>(X), Y, N, nb, R);
+    return hipGetLastError();
+}
+
+}  // namespace jq4k

@@ -1,0 +1,128 @@
+// q4k_device.h -- device-side Q4_K unpacking shared by every kernel of
+// libjq4k (the M = 1 GEMV, the MFMA GEMM and the test exports), so that the
+// exports' bit-exact checks exercise the hot path's own code.
+//
+// Format: GGUF's Q4_K super-block (genie-ai-runtime README, "At a glance":
+// GGUF models, Qwen3-4B-Q4_K_M; kernels "INT4 dequant-fused GEMV" and
+// "tensor-core MMQ Q4_K prefill").  A 144-byte block is nine 16-byte chunks:
+//   chunk 0      header: d | dmin << 16, then scales[0..3], [4..7], [8..11]
+//   chunks 1..8  qs[128]; the 32 bytes of "quarter" c (bytes 32c..32c+31)
+//                hold weights 64c + l in their low nibbles and 64c + 32 + l in
+//                their high nibbles (l = 0..31), i.e. sub-blocks 2c and 2c+1.
+//   w = d * sc_s * q - dmin * m_s.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jq4k {
+
+constexpr int kQK = 256;          // weights per block
+constexpr int kBlockBytes = 144;  // bytes per block
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) float float2_t;
+typedef __attribute__((ext_vector_type(16))) float float16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+// 16-byte load that bypasses cache allocation for data read exactly once.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// binary16 bit pattern (low 16 bits) -> fp32, exact.
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+// Scales and mins of sub-blocks 2c and 2c+1 (c = quarter, 0..3) from the
+// scale dwords s0 = scales[0..3], s1 = scales[4..7], s2 = scales[8..11].
+// Returns sc_(2c) | sc_(2c+1) << 8 in *sc and the same for the mins in *m.
+// Sub-blocks j < 4 (c < 2): the low six bits of scales[j] and scales[j+4].
+// Sub-blocks j >= 4 (c >= 2): low four bits from scales[j+4] (scale in the
+// low nibble, min in the high one), top two bits from bits 6..7 of
+// scales[j-4] (scale) and scales[j] (min).  Both cases read the byte pair at
+// shift 16 * (c & 1); the choice between them is a select, so the routine is
+// branch-free whether c is uniform or differs across lanes.
+__device__ __forceinline__ void scale_min_pair(uint32_t c, uint32_t s0, uint32_t s1,
+                                               uint32_t s2, uint32_t* sc, uint32_t* m) {
+    const uint32_t sh = (c & 1u) << 4;
+    const uint32_t a = s0 >> sh, b = s1 >> sh, e = s2 >> sh;
+    const uint32_t sc_lo = a & 0x3F3Fu;
+    const uint32_t m_lo = b & 0x3F3Fu;
+    const uint32_t sc_hi = (e & 0x0F0Fu) | ((a >> 2) & 0x3030u);
+    const uint32_t m_hi = ((e >> 4) & 0x0F0Fu) | ((b >> 2) & 0x3030u);
+    const bool high = c >= 2u;
+    *sc = high ? sc_hi : sc_lo;
+    *m = high ? m_hi : m_lo;
+}
+
+// The quant nibbles of one qs dword (4 bytes), one quant per byte:
+// low nibbles -> the 4 weights of the even sub-block, high -> the odd one.
+__device__ __forceinline__ uint32_t low_quants(uint32_t v) { return v & 0x0F0F0F0Fu; }
+__device__ __forceinline__ uint32_t high_quants(uint32_t v) { return (v >> 4) & 0x0F0F0F0Fu; }
+
+// Byte k of a 32-bit word as fp32 (selected to one v_cvt_f32_ubyte{k}).
+template <int k>
+__device__ __forceinline__ float ubyte_to_float(uint32_t v) {
+    return static_cast<float>((v >> (8 * k)) & 0xFFu);
+}
+
+// Per-sub-block affine constants of a quarter: w = ds * q - dm.
+struct QuarterScales {
+    float ds0, dm0;  // even sub-block 2c
+    float ds1, dm1;  // odd sub-block 2c+1
+};
+
+// From the 16-byte header chunk and the quarter index.  d*sc and dmin*m are
+// exact in fp32 (at most 11 + 6 significant bits), so fma(ds, q, -dm) is the
+// exact value rounded once.
+__device__ __forceinline__ QuarterScales quarter_scales(uint4 hdr, uint32_t c) {
+    const float d = half_bits_to_float(hdr.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(hdr.x >> 16);
+    uint32_t scp, mp;
+    scale_min_pair(c, hdr.y, hdr.z, hdr.w, &scp, &mp);
+    QuarterScales s;
+    s.ds0 = d * ubyte_to_float<0>(scp);
+    s.ds1 = d * ubyte_to_float<1>(scp);
+    s.dm0 = dmin * ubyte_to_float<0>(mp);
+    s.dm1 = dmin * ubyte_to_float<1>(mp);
+    return s;
+}
+
+// fp32 weights of one qs dword: lo[0..3] are weights 64c + p + 0..3 and
+// hi[0..3] are weights 64c + 32 + p + 0..3, p = byte offset within the quarter.
+__device__ __forceinline__ void dequant_dword_f32(uint32_t v, const QuarterScales& s,
+                                                  float lo[4], float hi[4]) {
+    const uint32_t ql = low_quants(v), qh = high_quants(v);
+    lo[0] = __builtin_fmaf(s.ds0, ubyte_to_float<0>(ql), -s.dm0);
+    lo[1] = __builtin_fmaf(s.ds0, ubyte_to_float<1>(ql), -s.dm0);
+    lo[2] = __builtin_fmaf(s.ds0, ubyte_to_float<2>(ql), -s.dm0);
+    lo[3] = __builtin_fmaf(s.ds0, ubyte_to_float<3>(ql), -s.dm0);
+    hi[0] = __builtin_fmaf(s.ds1, ubyte_to_float<0>(qh), -s.dm1);
+    hi[1] = __builtin_fmaf(s.ds1, ubyte_to_float<1>(qh), -s.dm1);
+    hi[2] = __builtin_fmaf(s.ds1, ubyte_to_float<2>(qh), -s.dm1);
+    hi[3] = __builtin_fmaf(s.ds1, ubyte_to_float<3>(qh), -s.dm1);
+}
+
+// Two fp32 -> packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const float2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// bf16 weights of one qs dword, as two packed pairs per half:
+// lo2[0] = (w0, w1), lo2[1] = (w2, w3) of the even sub-block; hi2 likewise.
+__device__ __forceinline__ void dequant_dword_bf16(uint32_t v, const QuarterScales& s,
+                                                   uint32_t lo2[2], uint32_t hi2[2]) {
+    float lo[4], hi[4];
+    dequant_dword_f32(v, s, lo, hi);
+    lo2[0] = pack_bf16x2(lo[0], lo[1]);
+    lo2[1] = pack_bf16x2(lo[2], lo[3]);
+    hi2[0] = pack_bf16x2(hi[0], hi[1]);
+    hi2[1] = pack_bf16x2(hi[2], hi[3]);
+}
+
+}  // namespace jq4k

@@ -1,0 +1,118 @@
+"""The C ABI of libjq4k on the CPU: the library loads, exports every symbol
+include/jq4k.h declares, and rejects bad arguments before any HIP call (so
+none of these tests launches anything)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import q4_weight_only_amd as jq4k
+
+ALIGNED = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced
+ALIGNED2 = 0x20000
+ALIGNED3 = 0x30000
+
+
+@pytest.fixture(scope="module")
+def L():
+    return jq4k.raw()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = jq4k.declared_symbols()
+    assert {"jq4k_gemv", "jq4k_gemm", "jq4k_gemm_path", "jq4k_unpack_fields",
+            "jq4k_dequant_f32", "jq4k_dequant_bf16", "jq4k_strerror",
+            "jq4k_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", jq4k.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_c_and_block_is_144_bytes(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "jq4k.h"\n'
+                   'int size_ok[sizeof(block_q4_K) == 144 ? 1 : -1];\n'
+                   'int main(void) { return 0; }\n')
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", jq4k.HEADER.rsplit("/", 1)[0],
+                    str(src), "-o", str(tmp_path / "t")], check=True)
+
+
+def test_version_and_strerror(L):
+    assert jq4k.version() == 100
+    assert jq4k.strerror(0) == "success"
+    assert jq4k.strerror(-1) == "invalid argument"
+    assert jq4k.strerror(-2) == "misaligned pointer"
+    assert jq4k.strerror(-77) == "unknown error"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 0), (1, 8, -256), (1, 8, 100), (1, 8, 257),
+                                   (-1, 8, 256), (1, -8, 256)])
+def test_bad_sizes_are_rejected(L, M, N, K):
+    for f in (L.jq4k_gemm, L.jq4k_gemv):
+        assert f(ALIGNED, ALIGNED2, ALIGNED3, M, N, K, None) == jq4k.EINVAL
+
+
+def test_gemv_requires_one_token_and_bounded_k(L):
+    assert L.jq4k_gemv(ALIGNED, ALIGNED2, ALIGNED3, 2, 8, 256, None) == jq4k.EINVAL
+    assert L.jq4k_gemv(ALIGNED, ALIGNED2, ALIGNED3, 0, 8, 256, None) == jq4k.EINVAL
+    assert L.jq4k_gemv(ALIGNED, ALIGNED2, ALIGNED3, 1, 8, jq4k.GEMV_MAX_K + 256,
+                       None) == jq4k.EINVAL
+    assert L.jq4k_gemm_path(ALIGNED, ALIGNED2, ALIGNED3, 2, 8, 256, jq4k.PATH_GEMV,
+                            None) == jq4k.EINVAL
+
+
+def test_unknown_path_is_rejected(L):
+    for path in (-1, 6, 99):
+        assert L.jq4k_gemm_path(ALIGNED, ALIGNED2, ALIGNED3, 4, 8, 256, path,
+                                None) == jq4k.EINVAL
+
+
+def test_null_pointers_are_rejected(L):
+    for W, X, Y in ((0, ALIGNED2, ALIGNED3), (ALIGNED, 0, ALIGNED3), (ALIGNED, ALIGNED2, 0)):
+        assert L.jq4k_gemm(W, X, Y, 3, 8, 256, None) == jq4k.EINVAL
+        assert L.jq4k_gemv(W, X, Y, 1, 8, 256, None) == jq4k.EINVAL
+
+
+def test_misaligned_pointers_are_rejected(L):
+    cases = ((ALIGNED + 8, ALIGNED2, ALIGNED3), (ALIGNED, ALIGNED2 + 2, ALIGNED3),
+             (ALIGNED, ALIGNED2, ALIGNED3 + 2), (ALIGNED + 1, ALIGNED2, ALIGNED3))
+    for W, X, Y in cases:
+        assert L.jq4k_gemm(W, X, Y, 3, 8, 256, None) == jq4k.EALIGN
+        assert L.jq4k_gemv(W, X, Y, 1, 8, 256, None) == jq4k.EALIGN
+    # Y needs only 4-byte alignment
+    assert L.jq4k_gemm(ALIGNED, ALIGNED2, ALIGNED3 + 4, 0, 8, 256, None) == jq4k.OK
+
+
+def test_empty_problems_return_without_launching(L):
+    # null pointers are fine when there is nothing to compute
+    assert L.jq4k_gemm(0, 0, 0, 0, 8, 256, None) == jq4k.OK
+    assert L.jq4k_gemm(0, 0, 0, 5, 0, 256, None) == jq4k.OK
+    assert L.jq4k_gemv(0, 0, 0, 1, 0, 256, None) == jq4k.OK
+    for path in range(6):
+        M = 1 if path == jq4k.PATH_GEMV else 0
+        assert L.jq4k_gemm_path(0, 0, 0, M, 0, 512, path, None) == jq4k.OK
+
+
+def test_export_argument_checks(L):
+    assert L.jq4k_unpack_fields(ALIGNED, -1, ALIGNED2, ALIGNED3, ALIGNED3, None) == jq4k.EINVAL
+    assert L.jq4k_unpack_fields(0, 0, 0, 0, 0, None) == jq4k.OK
+    assert L.jq4k_unpack_fields(0, 3, ALIGNED2, ALIGNED3, ALIGNED3, None) == jq4k.EINVAL
+    assert L.jq4k_unpack_fields(ALIGNED, 3, ALIGNED2, 0, ALIGNED3, None) == jq4k.EINVAL
+    assert L.jq4k_unpack_fields(ALIGNED + 4, 3, ALIGNED2, ALIGNED3, ALIGNED3,
+                                None) == jq4k.EALIGN
+    for f in (L.jq4k_dequant_f32, L.jq4k_dequant_bf16):
+        assert f(ALIGNED, -5, ALIGNED2, None) == jq4k.EINVAL
+        assert f(ALIGNED, 0, 0, None) == jq4k.OK
+        assert f(ALIGNED, 2, 0, None) == jq4k.EINVAL
+        assert f(ALIGNED, 2, ALIGNED2 + 2, None) == jq4k.EALIGN
+        assert f(ALIGNED + 8, 2, ALIGNED2, None) == jq4k.EALIGN
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(jq4k, "_raw", None)
+    monkeypatch.setattr(jq4k, "LIB_PATH", "/nonexistent/libjq4k.so")
+    with pytest.raises(ImportError):
+        jq4k.raw()

@@ -1,0 +1,212 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer fields and the fp32 / bf16 dequantised weights must match bit for
+bit; matmul outputs must meet |y - y_ref| <= 2e-3 * sum|w*x| + 1e-5 on every
+element.  Inputs are the seeded synthetic workloads (Qwen3-4B shapes; the
+genie-ai-runtime README's CLI banner gives 36 layers and a 2560 hidden size)
+plus structured blocks built by the oracle-side encoder.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import q4k_inputs as qi
+from oracle import q4k_pack as pk
+from tests import golden_blocks
+from tests.gpu_util import announce, dev, host, parity, run_gemm
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import q4_weight_only_amd as jq4k
+    jq4k.raw()                                      # fails loudly if not built
+    return jq4k
+
+
+def _special_blocks(g, nb):
+    """Random blocks whose d/dmin cover subnormal, negative, zero and large
+    binary16 values (finite)."""
+    W = g.integers(0, 256, (nb, 144), dtype=np.uint8)
+    hdr = g.integers(0, 0x7C00, (nb, 2)).astype(np.uint16)
+    hdr |= (g.integers(0, 2, (nb, 2)) << 15).astype(np.uint16)
+    hdr[0:8] = [[0x0001, 0x0001], [0x03FF, 0x8001], [0x0000, 0x0000], [0x8000, 0x7BFF],
+                [0x7BFF, 0x7BFF], [0x0400, 0x03FF], [0x3C00, 0x0000], [0x0000, 0x3C00]]
+    W[:, 0:4] = hdr.view(np.uint8).reshape(nb, 4)
+    return W
+
+
+# ------------------------------------------------------------ exports
+
+def test_unpack_fields_bit_exact(gpu):
+    g = np.random.default_rng(100)
+    W = np.concatenate([g.integers(0, 256, (3000, 144), dtype=np.uint8)] +
+                       [b["bytes"][None] for b in golden_blocks.load()])
+    nb = W.shape[0]
+    announce(f"unpack_fields nblocks={nb}")
+    q = torch.zeros(nb * 256, dtype=torch.uint8, device="cuda:0")
+    sc = torch.zeros(nb * 8, dtype=torch.uint8, device="cuda:0")
+    m = torch.zeros(nb * 8, dtype=torch.uint8, device="cuda:0")
+    gpu.unpack_fields(dev(W), q, sc, m)
+    rq, rsc, rm, _, _ = oracle.unpack_fields(W)
+    assert np.array_equal(host(q).reshape(nb, 256), rq)
+    assert np.array_equal(host(sc).reshape(nb, 8), rsc)
+    assert np.array_equal(host(m).reshape(nb, 8), rm)
+
+
+def test_dequant_f32_bit_exact(gpu):
+    g = np.random.default_rng(101)
+    W = np.concatenate([_special_blocks(g, 2000), qi.weight_bytes(g, 64, 2560).reshape(-1, 144)]
+                       + [b["bytes"][None] for b in golden_blocks.load()])
+    nb = W.shape[0]
+    announce(f"dequant_f32 nblocks={nb}")
+    w = torch.zeros(nb * 256, dtype=torch.float32, device="cuda:0")
+    gpu.dequant_f32(dev(W), w)
+    ref = oracle.dequant_f32(W)
+    got = host(w)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_bf16_bit_exact(gpu):
+    g = np.random.default_rng(102)
+    W = np.concatenate([_special_blocks(g, 2000), qi.weight_bytes(g, 64, 2560).reshape(-1, 144)])
+    nb = W.shape[0]
+    announce(f"dequant_bf16 nblocks={nb}")
+    w = torch.zeros(nb * 256, dtype=torch.int16, device="cuda:0")
+    gpu.dequant_bf16(dev(W), w)
+    assert np.array_equal(host(w).view(np.uint16), oracle.dequant_bf16(W))
+
+
+# ------------------------------------------------------------ M = 1
+
+def test_gemv_single_2560x2560(gpu):
+    W, X = qi.single_gemv(0)
+    announce("gemv 2560x2560 seed 0")
+    y = run_gemm(W, X, 2560, 2560, path="gemv")
+    Y, A = oracle.gemm(W, X, 2560, 2560)
+    parity(y, Y, A, "gemv 2560x2560")
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (3, 256), (17, 512), (255, 768), (1000, 2560),
+                                 (129, 4096), (333, 9728), (64, 16384), (5, 1280)])
+def test_gemv_ragged_shapes(gpu, N, K):
+    g = np.random.default_rng([103, N, K])
+    W = qi.weight_bytes(g, N, K)
+    X = qi.activations(g, 1, K)
+    announce(f"gemv N={N} K={K}")
+    y = run_gemm(W, X, N, K, path="gemv")
+    Y, A = oracle.gemm(W, X, N, K)
+    parity(y, Y, A, f"gemv N={N} K={K}")
+
+
+def test_gemv_decode_layer(gpu):
+    for name, N, K, W, X in qi.decode_layer(1, 0, 1):
+        announce(f"gemv decode layer {name} {N}x{K}")
+        y = run_gemm(W, X, N, K, path="gemv")
+        Y, A = oracle.gemm(W, X, N, K)
+        parity(y, Y, A, f"decode {name}")
+
+
+def test_gemv_one_hot_isolates_weights(gpu):
+    """x = e_k gives y = column k of the fp32 weights, exactly."""
+    g = np.random.default_rng(104)
+    N, K = 40, 512
+    W = qi.weight_bytes(g, N, K)
+    w = oracle.dequant_f32(W).reshape(N, K)
+    for k in (0, 31, 32, 63, 64, 255, 256, 300, 511):
+        X = np.zeros((1, K), np.uint16)
+        X[0, k] = 0x3F80
+        announce(f"gemv one-hot k={k}")
+        y = run_gemm(W, X, N, K, path="gemv")
+        assert np.array_equal(y[0], w[:, k]), k
+
+
+def test_gemv_closed_form_constant_blocks(gpu):
+    blk = [b for b in golden_blocks.load() if b["name"] == "closed_form"][0]["bytes"]
+    N, K = 70, 2560
+    W = np.tile(blk, (N, K // 256))
+    X = np.full((1, K), 0x3F80, np.uint16)
+    announce("gemv closed form")
+    y = run_gemm(W, X, N, K, path="gemv")
+    assert np.all(y == -10.0)
+
+
+# ------------------------------------------------------------ M > 1 (MFMA)
+
+PATHS = ["mfma64", "mfma128", "mfma256"]
+
+
+def _path(name):
+    import q4_weight_only_amd as jq4k
+    return {"mfma": jq4k.PATH_MFMA, "mfma64": jq4k.PATH_MFMA_T64,
+            "mfma128": jq4k.PATH_MFMA_T128, "mfma256": jq4k.PATH_MFMA_T256}[name]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("M,N,K", [(1, 37, 256), (2, 128, 256), (3, 130, 512), (17, 256, 768),
+                                   (33, 300, 2560), (64, 129, 512), (65, 257, 256),
+                                   (128, 64, 1024), (200, 383, 512), (300, 140, 256)])
+def test_mfma_paths_ragged(gpu, path, M, N, K):
+    g = np.random.default_rng([105, M, N, K])
+    W = qi.weight_bytes(g, N, K)
+    X = qi.activations(g, M, K)
+    announce(f"{path} M={M} N={N} K={K}")
+    y = run_gemm(W, X, N, K, path=_path(path))
+    Y, A = oracle.gemm(W, X, N, K)
+    parity(y, Y, A, f"{path} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_mfma_identity_probe(gpu, path):
+    """X = I_K gives Y = bf16(w)^T exactly: every output is one weight."""
+    g = np.random.default_rng(106)
+    N, K = 48, 512
+    W = qi.weight_bytes(g, N, K)
+    X = np.zeros((K, K), np.uint16)
+    X[np.arange(K), np.arange(K)] = 0x3F80
+    announce(f"{path} identity probe")
+    y = run_gemm(W, X, N, K, path=_path(path))
+    wb = oracle.dequant_bf16(W).reshape(N, K)
+    ref = (wb.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(y, ref.T)
+
+
+@pytest.mark.parametrize("M", [2, 33, 300])
+def test_gemm_auto_and_determinism(gpu, M):
+    g = np.random.default_rng([107, M])
+    N, K = 520, 2560
+    W = qi.weight_bytes(g, N, K)
+    X = qi.activations(g, M, K)
+    announce(f"gemm auto M={M} twice")
+    y1 = run_gemm(W, X, N, K)
+    y2 = run_gemm(W, X, N, K)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    Y, A = oracle.gemm(W, X, N, K)
+    parity(y1, Y, A, f"auto M={M}")
+
+
+def test_prefill_m33_one_layer(gpu):
+    for p in range(7):
+        name, N, K, W, X = qi.prefill_projection(2, 0, p, 33)
+        announce(f"prefill M=33 layer 0 {name} {N}x{K}")
+        y = run_gemm(W, X, N, K)
+        Y, A = oracle.gemm(W, X, N, K)
+        parity(y, Y, A, f"M=33 {name}")
+
+
+def test_prefill_m2048_sampled(gpu):
+    g = np.random.default_rng(108)
+    for p in range(7):
+        name, N, K, W, X = qi.prefill_projection(3, 0, p, 2048)
+        announce(f"prefill M=2048 {name} {N}x{K}")
+        y = run_gemm(W, X, N, K)
+        rows = np.sort(g.choice(N, 48, replace=False))
+        ms = np.sort(g.choice(2048, 24, replace=False))
+        Y, A = oracle.gemm(W[rows], X[ms], len(rows), K)
+        parity(y[np.ix_(ms, rows)], Y, A, f"M=2048 {name} sampled")
+        assert np.all(np.isfinite(y))
