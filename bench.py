@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--profile", action="store_true",
+                    help="a few eager launches of each kernel for rocprofv3, no JSON line")
     return ap.parse_args()
 
 
@@ -80,7 +82,17 @@ def timed(torch, fn, steps, warmup, use_graph):
     return start.elapsed_time(stop) / 1e3
 
 
+DEPENDENCY_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]   # q|k|v, o, gate|up, down
+
+
 def decode_leg(torch, jq4k, args):
+    """Seven Q4_K GEMVs of one decode layer, timed three ways:
+    batched_1     one jq4k_gemv_batched launch for all seven (they are
+                  independent in this workload) -- the headline value;
+    dependency_4  the launches a real decode step can make (q|k|v, o, gate|up,
+                  down: later groups consume earlier outputs);
+    separate_7    seven jq4k_gemv launches."""
+    import ctypes
     layer = qi.decode_layer(1, 0, 1)
     layer_bytes = sum(W.nbytes for _, _, _, W, _ in layer)
     copies = max(2, math.ceil(ROTATION_BYTES / layer_bytes))
@@ -92,25 +104,76 @@ def decode_leg(torch, jq4k, args):
     Ys = [torch.empty((1, N), dtype=torch.float32, device="cuda:0") for _, N, _, _, _ in layer]
     L = jq4k.raw()
 
-    def step(i):
+    def descs(c, idx):
+        arr = (jq4k.GemvDesc * len(idx))()
+        for j, p in enumerate(idx):
+            _, N, K, _, _ = layer[p]
+            arr[j] = jq4k.GemvDesc(Ws[c][p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(), N, K)
+        return arr
+    all7 = [descs(c, range(7)) for c in range(copies)]
+    grouped = [[descs(c, gi) for gi in DEPENDENCY_GROUPS] for c in range(copies)]
+
+    def check(rc):
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+
+    def step_batched(i):
+        check(L.jq4k_gemv_batched(ctypes.addressof(all7[i % copies]), 7,
+                                  torch.cuda.current_stream().cuda_stream))
+
+    def step_grouped(i):
+        s = torch.cuda.current_stream().cuda_stream
+        for arr, gi in zip(grouped[i % copies], DEPENDENCY_GROUPS):
+            check(L.jq4k_gemv_batched(ctypes.addressof(arr), len(gi), s))
+
+    def step_separate(i):
         Wc = Ws[i % copies]
         s = torch.cuda.current_stream().cuda_stream
         for p, (_, N, K, _, _) in enumerate(layer):
-            rc = L.jq4k_gemv(Wc[p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(), 1, N, K, s)
-            if rc:
-                raise RuntimeError(jq4k.strerror(rc))
+            check(L.jq4k_gemv(Wc[p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(), 1, N, K, s))
 
-    secs = timed(torch, step, args.steps, args.warmup, not args.eager)
+    graph = not args.eager
+    secs = timed(torch, step_batched, args.steps, args.warmup, graph)
+    modes = {}
+    for name, fn, launches in (("batched_1", None, 1), ("dependency_4", step_grouped, 4),
+                               ("separate_7", step_separate, 7)):
+        t = secs if fn is None else timed(torch, fn, args.steps, args.warmup, graph)
+        modes[name] = {"launches_per_step": launches, "us_per_step": round(t / args.steps * 1e6, 2),
+                       "GB_s": round(layer_bytes * args.steps / t / 1e9, 1)}
     per_proj = {}
     for p, (name, N, K, W, _) in enumerate(layer):
         def one(i, p=p, N=N, K=K):
             s = torch.cuda.current_stream().cuda_stream
-            L.jq4k_gemv(Ws[i % copies][p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(),
-                        1, N, K, s)
-        t = timed(torch, one, args.steps, 4, not args.eager)
+            check(L.jq4k_gemv(Ws[i % copies][p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(),
+                              1, N, K, s))
+        t = timed(torch, one, args.steps, 4, graph)
         per_proj[name] = {"N": N, "K": K, "us": round(t / args.steps * 1e6, 3),
                           "GB_s": round(W.nbytes * args.steps / t / 1e9, 1)}
-    return layer, layer_bytes, copies, secs, per_proj
+    return layer, layer_bytes, copies, secs, modes, per_proj
+
+
+def lm_head_leg(torch, jq4k, args):
+    """The 151936 x 2560 Q4_K LM head at M = 1: one 219 MB GEMV, the largest
+    single-kernel bandwidth case (context for the headline)."""
+    W, X = qi.lm_head(4, 1)
+    N, K = 151936, 2560
+    copies = max(2, math.ceil(ROTATION_BYTES / W.nbytes))
+    Wd = [torch.from_numpy(W).to("cuda:0")]
+    Wd += [Wd[0].clone() for _ in range(copies - 1)]
+    Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+    Yd = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    L = jq4k.raw()
+
+    def one(i):
+        rc = L.jq4k_gemv(Wd[i % copies].data_ptr(), Xd.data_ptr(), Yd.data_ptr(), 1, N, K,
+                         torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+    steps = max(10, args.steps // 10)
+    t = timed(torch, one, steps, 3, not args.eager)
+    return {"N": N, "K": K, "weight_bytes": int(W.nbytes), "us": round(t / steps * 1e6, 2),
+            "GB_s": round(W.nbytes * steps / t / 1e9, 1),
+            "frac_of_hbm_peak": round(W.nbytes * steps / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def prefill_leg(torch, jq4k, args):
@@ -144,6 +207,47 @@ def prefill_leg(torch, jq4k, args):
         per_proj[name] = {"N": N, "K": K, "us": round(t / args.prefill_steps * 1e6, 2),
                           "TFLOP_s": round(2.0 * M * N * K * args.prefill_steps / t / 1e12, 1)}
     return flops, secs, per_proj
+
+
+def profile_run(torch, jq4k):
+    """Launches for rocprofv3 runs: a 512 MiB device copy (the reference for
+    scaling FETCH_SIZE / WRITE_SIZE), then 20 batched decode-layer GEMVs, 20
+    LM-head GEMVs and 3 passes of the M=2048 layer, eagerly, synchronised."""
+    import ctypes
+    a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    L = jq4k.raw()
+    s = torch.cuda.current_stream().cuda_stream
+    layer = qi.decode_layer(1, 0, 1)
+    dev = [(torch.from_numpy(W).to("cuda:0"), torch.from_numpy(X.view(np.int16)).to("cuda:0"),
+            torch.empty(N, dtype=torch.float32, device="cuda:0")) for _, N, K, W, X in layer]
+    arr = (jq4k.GemvDesc * 7)()
+    for p, ((_, N, K, _, _), (W, X, Y)) in enumerate(zip(layer, dev)):
+        arr[p] = jq4k.GemvDesc(W.data_ptr(), X.data_ptr(), Y.data_ptr(), N, K)
+    for _ in range(20):
+        assert L.jq4k_gemv_batched(ctypes.addressof(arr), 7, s) == 0
+    torch.cuda.synchronize()
+    W, X = qi.lm_head(4, 1)
+    Wd = torch.from_numpy(W).to("cuda:0")
+    Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+    Yd = torch.empty(151936, dtype=torch.float32, device="cuda:0")
+    for _ in range(20):
+        assert L.jq4k_gemv(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), 1, 151936, 2560, s) == 0
+    torch.cuda.synchronize()
+    M = 2048
+    for p in range(7):
+        _, N, K, W, X = qi.prefill_projection(3, 0, p, M)
+        Wd = torch.from_numpy(W).to("cuda:0")
+        Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+        Yd = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        for _ in range(3):
+            assert L.jq4k_gemm(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K, s) == 0
+        torch.cuda.synchronize()
+    print("profile run done", flush=True)
 
 
 def cpu_baseline(layer, budget_s=12.0):
@@ -190,8 +294,12 @@ def main():
         sys.exit("bench.py needs a GPU")
     torch.cuda.set_device(0)
 
-    layer, layer_bytes, copies, secs, per_proj = decode_leg(torch, jq4k, args)
+    if args.profile:
+        profile_run(torch, jq4k)
+        return
+    layer, layer_bytes, copies, secs, modes, per_proj = decode_leg(torch, jq4k, args)
     gbs = layer_bytes * args.steps / secs / 1e9
+    lm = lm_head_leg(torch, jq4k, args)
     flops, psecs, p_per = prefill_leg(torch, jq4k, args)
     tflops = flops * args.prefill_steps / psecs / 1e12
 
@@ -211,7 +319,8 @@ def main():
         "config": {
             "workload": "Qwen3-4B decode layer, 7 Q4_K projections at M=1 "
                         "(q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up 9728x2560, "
-                        "down 2560x9728), seeds [1,0,p]",
+                        "down 2560x9728), seeds [1,0,p]; one jq4k_gemv_batched launch "
+                        "per step (the seven are independent here)",
             "weight_bytes_per_step": layer_bytes,
             "rotation_copies": copies,
             "launch": "eager" if args.eager else "hip-graph",
@@ -220,11 +329,13 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "q4k_gemv_kernel",
-            "avg_launch_us": round(secs / (args.steps * 7) * 1e6, 3),
-            "bytes_per_launch": layer_bytes / 7,
+            "kernel": "q4k_gemv_batched_kernel",
+            "avg_launch_us": round(secs / args.steps * 1e6, 3),
+            "bytes_per_launch": layer_bytes,
         },
+        "decode_modes": modes,
         "per_projection": per_proj,
+        "lm_head_m1": lm,
         "prefill": {
             "workload": "Qwen3-4B layer, 7 Q4_K projections at M=2048, seeds [3,0,p]",
             "value": round(tflops, 1), "unit": "TFLOP/s", "steps": args.prefill_steps,

@@ -93,6 +93,37 @@ typedef uint16_t jq4k_bf16; /* bfloat16 bit pattern */
 int jq4k_gemv(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
               int M, int N, int K, hipStream_t stream);
 
+/* jq4k_gemv for one token with an explicit number of rows of W per
+ * workgroup (a tuning knob; 0 picks the same value jq4k_gemv uses).  Larger
+ * values stage x fewer times, smaller ones spread a small matrix over more
+ * compute units.  JQ4K_EINVAL for rows_per_block < 0 or a value whose LDS
+ * need exceeds 64 KiB; otherwise the same rules as jq4k_gemv with M = 1. */
+int jq4k_gemv_rows(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
+                   int N, int K, int rows_per_block, hipStream_t stream);
+
+/* One problem of a batched decode GEMV: Y[0..N) = sum_k w[n][k] * X[k]. */
+typedef struct {
+    const block_q4_K *W;  /* N*(K/256) blocks, 16-byte aligned */
+    const jq4k_bf16 *X;   /* K bf16, 16-byte aligned           */
+    float *Y;             /* N floats, 4-byte aligned          */
+    int N;
+    int K;                /* positive multiple of 256, <= JQ4K_GEMV_MAX_K */
+} jq4k_gemv_desc;
+
+#define JQ4K_GEMV_BATCH_MAX 16
+
+/* Up to JQ4K_GEMV_BATCH_MAX independent decode GEMVs in one kernel launch
+ * (the genie-ai-runtime README, "At a glance": INT4 dequant-fused GEMV; one
+ * launch for the projections of a layer that do not depend on each other,
+ * such as q, k and v, or gate and up).  Each problem gets exactly the result
+ * jq4k_gemv gives for it; problems with N == 0 are skipped.  `problems` is a
+ * host array read before the call returns (the descriptors are passed to the
+ * kernel by value; nothing is allocated).  Outputs must not overlap any
+ * input.  Errors: JQ4K_EINVAL for count < 0, count > JQ4K_GEMV_BATCH_MAX, a
+ * null `problems` with count > 0, or any problem that jq4k_gemv rejects
+ * (JQ4K_EALIGN likewise); nothing is launched then. */
+int jq4k_gemv_batched(const jq4k_gemv_desc *problems, int count, hipStream_t stream);
+
 /* Matmul for any M >= 0: Y (M x N) = X (M x K) . W^T.
  * The genie-ai-runtime README, "At a glance": tensor-core MMQ Q4_K prefill.
  * M == 1 runs the decode GEMV when K <= JQ4K_GEMV_MAX_K; larger M runs the

@@ -25,6 +25,15 @@ BLOCK_BYTES = 144
 QK = 256
 
 
+class GemvDesc(ctypes.Structure):
+    """jq4k_gemv_desc: one problem of jq4k_gemv_batched."""
+    _fields_ = [("W", ctypes.c_void_p), ("X", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
+GEMV_BATCH_MAX = 16
+
+
 class Jq4kError(RuntimeError):
     def __init__(self, code, where):
         self.code = code
@@ -47,6 +56,10 @@ def _load():
             f = getattr(L, name)
             f.argtypes = [vp, vp, vp, i, i, i, vp]
             f.restype = i
+        L.jq4k_gemv_rows.argtypes = [vp, vp, vp, i, i, i, vp]
+        L.jq4k_gemv_rows.restype = i
+        L.jq4k_gemv_batched.argtypes = [vp, i, vp]
+        L.jq4k_gemv_batched.restype = i
         L.jq4k_gemm_path.argtypes = [vp, vp, vp, i, i, i, i, vp]
         L.jq4k_gemm_path.restype = i
         L.jq4k_unpack_fields.argtypes = [vp, l, vp, vp, vp, vp]
@@ -120,6 +133,24 @@ def gemv(W, X, Y, stream=None):
     _check(_load().jq4k_gemv(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K,
                              _stream(stream)), "jq4k_gemv")
     return Y
+
+
+def gemv_descs(problems):
+    """ctypes array of GemvDesc from (W, X, Y) torch tensor triples."""
+    arr = (GemvDesc * max(len(problems), 1))()
+    for i, (W, X, Y) in enumerate(problems):
+        M, N, K = _shapes(W, X, Y)
+        if M != 1:
+            raise ValueError("batched GEMV problems have one token")
+        arr[i] = GemvDesc(W.data_ptr(), X.data_ptr(), Y.data_ptr(), N, K)
+    return arr
+
+
+def gemv_batched(problems, stream=None):
+    """One launch for several independent GEMVs: problems = [(W, X, Y), ...]."""
+    arr = gemv_descs(problems)
+    _check(_load().jq4k_gemv_batched(ctypes.addressof(arr), len(problems), _stream(stream)),
+           "jq4k_gemv_batched")
 
 
 def gemm(W, X, Y, stream=None, path=PATH_AUTO):

@@ -11,6 +11,9 @@ namespace jq4k {
 hipError_t launch_gemv(const uint8_t* W, const uint16_t* X, float* Y, int N, int K, int R,
                        hipStream_t stream);
 size_t gemv_lds_bytes(int nb, int R);
+hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X,
+                               float* const* Y, const int* N, const int* K, const int* R,
+                               int count, hipStream_t stream);
 hipError_t launch_gemm_mfma(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
                             int tile, hipStream_t stream);
 long gemm_tile_count(int M, int N, int tile);
@@ -24,8 +27,11 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int kQuickReturn = 1;
-constexpr int kGemvMaxRows = 64;
+constexpr int kGemvMaxRows = 1024;
+constexpr int kGemvSmallRowsPerCu = 64;  // below this many rows per CU: small-matrix rule
+constexpr int kGemvBlocksPerCu = 4;
 constexpr size_t kGemvLdsLimit = 64 * 1024;
+constexpr int kBatchBlocksPerWg = 160;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -54,23 +60,43 @@ int check_matmul(const void* W, const void* X, const void* Y, int M, int N, int 
     return 0;
 }
 
-// Rows per workgroup of the GEMV: enough workgroups to cover every compute
-// unit about twice, at most 64 rows, within the LDS budget.
+// Rows per workgroup of the GEMV.  Small matrices take few rows per
+// workgroup so that every compute unit has loads in flight; large ones take
+// as many rows as one resident wave of workgroups (kGemvBlocksPerCu per compute
+// unit) needs, so that no tail of half-filled workgroup waves remains and the
+// per-workgroup staging of x is paid once.  Bounded by the LDS budget.
 int gemv_rows_per_block(int N, int K) {
     const int nb = K / jq4k::kQK;
-    const long want = 2L * cu_count();
-    long R = (N + want - 1) / want;
+    const long cus = cu_count();
+    long R;
+    if (N <= kGemvSmallRowsPerCu * cus)
+        R = (N + 2 * cus - 1) / (2 * cus);
+    else
+        R = (N + kGemvBlocksPerCu * cus - 1) / (kGemvBlocksPerCu * cus);
     if (R < 1) R = 1;
     if (R > kGemvMaxRows) R = kGemvMaxRows;
     while (R > 1 && jq4k::gemv_lds_bytes(nb, static_cast<int>(R)) > kGemvLdsLimit) --R;
     return static_cast<int>(R);
 }
 
-int run_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K,
+int run_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K, int R,
              hipStream_t stream) {
-    const hipError_t e = jq4k::launch_gemv(reinterpret_cast<const uint8_t*>(W), X, Y, N, K,
-                                           gemv_rows_per_block(N, K), stream);
+    if (R <= 0) R = gemv_rows_per_block(N, K);
+    const hipError_t e = jq4k::launch_gemv(reinterpret_cast<const uint8_t*>(W), X, Y, N, K, R,
+                                           stream);
     return static_cast<int>(e);
+}
+
+// Rows per workgroup inside a batched launch: the whole batch fills the GPU,
+// so each workgroup takes about kBatchBlocksPerWg blocks of W (2.5 rounds of
+// quarter tasks) whatever the row length.
+int gemv_batch_rows(int N, int K) {
+    const int nb = K / jq4k::kQK;
+    int R = (kBatchBlocksPerWg + nb - 1) / nb;
+    if (R > N) R = N;
+    if (R < 1) R = 1;
+    while (R > 1 && jq4k::gemv_lds_bytes(nb, R) > kGemvLdsLimit) --R;
+    return R;
 }
 
 int mfma_tile_for(int M, int N) {
@@ -105,7 +131,48 @@ int jq4k_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, i
     if (M != 1 || K > JQ4K_GEMV_MAX_K) return JQ4K_EINVAL;
     const int rc = check_matmul(W, X, Y, M, N, K);
     if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
-    return run_gemv(W, X, Y, N, K, stream);
+    return run_gemv(W, X, Y, N, K, 0, stream);
+}
+
+int jq4k_gemv_rows(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K,
+                   int rows_per_block, hipStream_t stream) {
+    if (rows_per_block < 0 || K > JQ4K_GEMV_MAX_K) return JQ4K_EINVAL;
+    const int rc = check_matmul(W, X, Y, 1, N, K);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    if (rows_per_block > 0 &&
+        jq4k::gemv_lds_bytes(K / jq4k::kQK, rows_per_block) > kGemvLdsLimit)
+        return JQ4K_EINVAL;
+    return run_gemv(W, X, Y, N, K, rows_per_block, stream);
+}
+
+int jq4k_gemv_batched(const jq4k_gemv_desc* problems, int count, hipStream_t stream) {
+    if (count < 0 || count > JQ4K_GEMV_BATCH_MAX) return JQ4K_EINVAL;
+    if (count == 0) return JQ4K_OK;
+    if (problems == nullptr) return JQ4K_EINVAL;
+    const uint8_t* W[JQ4K_GEMV_BATCH_MAX];
+    const uint16_t* X[JQ4K_GEMV_BATCH_MAX];
+    float* Y[JQ4K_GEMV_BATCH_MAX];
+    int N[JQ4K_GEMV_BATCH_MAX], K[JQ4K_GEMV_BATCH_MAX], R[JQ4K_GEMV_BATCH_MAX];
+    int live = 0;
+    long wgs = 0;
+    for (int i = 0; i < count; ++i) {
+        const jq4k_gemv_desc& d = problems[i];
+        if (d.K > JQ4K_GEMV_MAX_K) return JQ4K_EINVAL;
+        const int rc = check_matmul(d.W, d.X, d.Y, 1, d.N, d.K);
+        if (rc == kQuickReturn) continue;
+        if (rc != 0) return rc;
+        W[live] = reinterpret_cast<const uint8_t*>(d.W);
+        X[live] = d.X;
+        Y[live] = d.Y;
+        N[live] = d.N;
+        K[live] = d.K;
+        R[live] = gemv_batch_rows(d.N, d.K);
+        wgs += (static_cast<long>(d.N) + R[live] - 1) / R[live];
+        ++live;
+    }
+    if (live == 0) return JQ4K_OK;
+    if (wgs > 0x7FFFFFFFL) return JQ4K_EINVAL;
+    return static_cast<int>(jq4k::launch_gemv_batched(W, X, Y, N, K, R, live, stream));
 }
 
 int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,
@@ -115,13 +182,13 @@ int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int
     const int rc = check_matmul(W, X, Y, M, N, K);
     if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
     switch (path) {
-        case JQ4K_PATH_GEMV: return run_gemv(W, X, Y, N, K, stream);
+        case JQ4K_PATH_GEMV: return run_gemv(W, X, Y, N, K, 0, stream);
         case JQ4K_PATH_MFMA: return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, N), stream);
         case JQ4K_PATH_MFMA_T64: return run_mfma(W, X, Y, M, N, K, 64, stream);
         case JQ4K_PATH_MFMA_T128: return run_mfma(W, X, Y, M, N, K, 128, stream);
         case JQ4K_PATH_MFMA_T256: return run_mfma(W, X, Y, M, N, K, 256, stream);
         default:
-            if (M == 1 && K <= JQ4K_GEMV_MAX_K) return run_gemv(W, X, Y, N, K, stream);
+            if (M == 1 && K <= JQ4K_GEMV_MAX_K) return run_gemv(W, X, Y, N, K, 0, stream);
             return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, N), stream);
     }
 }

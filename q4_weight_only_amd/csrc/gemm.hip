@@ -10,8 +10,9 @@
 //   * the BM x 64 slab of X (bf16) is copied to LDS;
 //   * four waves multiply the slabs with v_mfma_f32_32x32x16_bf16 into fp32
 //     accumulators.
-// LDS is double-buffered, so one barrier per stage suffices: the global loads
-// of stage s+1 are in flight while stage s is on the matrix cores.
+// LDS is double-buffered and the loop is software-pipelined: while stage s
+// is on the matrix cores, stage s+1 is dequantised into the other buffer and
+// the global loads of stages s+2 and s+3 are in flight; one barrier per stage.
 // LDS rows are 128 bytes (8 chunks of 16 bytes); chunk i of row r is stored
 // at i ^ (r & 7) so the 32 rows an MFMA operand read touches hit distinct
 // bank groups.
@@ -71,65 +72,69 @@ __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(
     // ---- W slab assignment: row wr of the tile, quant bytes [qoff, qoff + kQBytes)
     const int wr = t / C::kThreadsPerRow;
     const int qoff = (t % C::kThreadsPerRow) * C::kQBytes;
-    const bool w_live = (n0 + wr) < N;
+    // rows past N are clamped to row N-1: they only feed output columns that
+    // are never stored
     const uint8_t* wrow = W + static_cast<long>(min(n0 + wr, N - 1)) * nb * kBlockBytes;
 
     // ---- X slab assignment: chunk g = t + 256 j -> row g / 8, chunk g % 8
     const uint16_t* xbase = X;
 
-    uint4 xreg[C::kXChunks];
-    uint4 hreg;
-    uint32_t qreg[C::kQBytes / 4];
+    // Global data of one stage, held in registers until it is stored to LDS.
+    struct StageRegs {
+        uint4 x[C::kXChunks];
+        uint4 hdr;
+        uint32_t q[C::kQBytes / 4];
+    };
+    StageRegs rs[2];
 
-    auto load_stage = [&](int s) {
+    auto load_stage = [&](int s, StageRegs& r) {
         const int kb = s >> 2, c = s & 3;
 #pragma unroll
         for (int j = 0; j < C::kXChunks; ++j) {
             const int g = t + j * kGemmThreads;
             const int row = g >> 3, ch = g & 7;
-            const int m = m0 + row;
-            xreg[j] = (m < M) ? *reinterpret_cast<const uint4*>(
-                                    xbase + static_cast<long>(m) * K + s * kBK + ch * 8)
-                              : make_uint4(0, 0, 0, 0);
+            // rows past M are clamped to row M-1: they only feed output rows
+            // that are never stored
+            const int m = min(m0 + row, M - 1);
+            r.x[j] = *reinterpret_cast<const uint4*>(xbase + static_cast<long>(m) * K +
+                                                     s * kBK + ch * 8);
         }
         const uint8_t* blk = wrow + kb * kBlockBytes;
-        hreg = *reinterpret_cast<const uint4*>(blk);
+        r.hdr = *reinterpret_cast<const uint4*>(blk);
         const uint8_t* q = blk + 16 + 32 * c + qoff;
         if constexpr (C::kQBytes == 32) {
             const uint4 a = *reinterpret_cast<const uint4*>(q);
             const uint4 b = *reinterpret_cast<const uint4*>(q + 16);
-            qreg[0] = a.x; qreg[1] = a.y; qreg[2] = a.z; qreg[3] = a.w;
-            qreg[4] = b.x; qreg[5] = b.y; qreg[6] = b.z; qreg[7] = b.w;
+            r.q[0] = a.x; r.q[1] = a.y; r.q[2] = a.z; r.q[3] = a.w;
+            r.q[4] = b.x; r.q[5] = b.y; r.q[6] = b.z; r.q[7] = b.w;
         } else if constexpr (C::kQBytes == 16) {
             const uint4 a = *reinterpret_cast<const uint4*>(q);
-            qreg[0] = a.x; qreg[1] = a.y; qreg[2] = a.z; qreg[3] = a.w;
+            r.q[0] = a.x; r.q[1] = a.y; r.q[2] = a.z; r.q[3] = a.w;
         } else {
             const uint2 a = *reinterpret_cast<const uint2*>(q);
-            qreg[0] = a.x; qreg[1] = a.y;
+            r.q[0] = a.x; r.q[1] = a.y;
         }
     };
 
-    auto store_stage = [&](int s, uint4* buf) {
+    auto store_stage = [&](int s, const StageRegs& r, uint4* buf) {
         const int c = s & 3;
 #pragma unroll
         for (int j = 0; j < C::kXChunks; ++j) {
             const int g = t + j * kGemmThreads;
-            buf[lds_chunk(g >> 3, g & 7)] = xreg[j];
+            buf[lds_chunk(g >> 3, g & 7)] = r.x[j];
         }
         uint4* wbuf = buf + BM * kRowChunks;
-        if (w_live) {
-            const QuarterScales sc = quarter_scales(hreg, static_cast<uint32_t>(c));
-            // 8 quant bytes -> one 16-byte chunk of the even sub-block (k offset
-            // qoff + 0..7) and one of the odd sub-block (k offset 32 + qoff + 0..7)
+        const QuarterScales sc = quarter_scales(r.hdr, static_cast<uint32_t>(c));
+        // 8 quant bytes -> one 16-byte chunk of the even sub-block (k offset
+        // qoff + 0..7) and one of the odd sub-block (k offset 32 + qoff + 0..7)
 #pragma unroll
-            for (int j = 0; j < C::kQBytes / 8; ++j) {
-                uint32_t lo_a[2], hi_a[2], lo_b[2], hi_b[2];
-                dequant_dword_bf16(qreg[2 * j], sc, lo_a, hi_a);
-                dequant_dword_bf16(qreg[2 * j + 1], sc, lo_b, hi_b);
-                const int ch = (qoff >> 3) + j;
-                wbuf[lds_chunk(wr, ch)] = make_uint4(lo_a[0], lo_a[1], lo_b[0], lo_b[1]);
-                wbuf[lds_chunk(wr, 4 + ch)] = make_uint4(hi_a[0], hi_a[1], hi_b[0], hi_b[1]);
-            }
+        for (int j = 0; j < C::kQBytes / 8; ++j) {
+            uint32_t lo_a[2], hi_a[2], lo_b[2], hi_b[2];
+            dequant_dword_bf16(r.q[2 * j], sc, lo_a, hi_a);
+            dequant_dword_bf16(r.q[2 * j + 1], sc, lo_b, hi_b);
+            const int ch = (qoff >> 3) + j;
+            wbuf[lds_chunk(wr, ch)] = make_uint4(lo_a[0], lo_a[1], lo_b[0], lo_b[1]);
+            wbuf[lds_chunk(wr, 4 + ch)] = make_uint4(hi_a[0], hi_a[1], hi_b[0], hi_b[1]);
         }
     };
 
@@ -143,31 +148,57 @@ __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(
     const int bcol = wn * C::kWaveN + (lane & 31);  // B column within the tile (+32 j)
     const int khalf = lane >> 5;
 
-    load_stage(0);
-    for (int s = 0; s < nstage; ++s) {
-        uint4* buf = lds[s & 1];
-        store_stage(s, buf);
-        if (s + 1 < nstage) load_stage(s + 1);
-        __syncthreads();
+    // Software pipeline, one barrier per stage.  While the matrix cores work
+    // on stage s from LDS buffer s & 1, the same instruction stream
+    // dequantises stage s + 1 (from register set (s + 1) & 1) into the other
+    // buffer and requests stage s + 3 into the register set it just freed, so
+    // global data has two stages of work to arrive.  Stage indices past the
+    // end are clamped (harmless repeats), keeping the body one basic block.
+    // Within a stage the operand fragments of k-step ks + 1 are read from LDS
+    // while the MFMAs of k-step ks run.
+    auto read_frags = [&](const uint4* buf, int ks, bf16x8_t* a, bf16x8_t* b) {
         const uint4* xb = buf;
         const uint4* wb = buf + BM * kRowChunks;
+        const int ch = 2 * ks + khalf;
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i)
+            a[i] = __builtin_bit_cast(bf16x8_t, xb[lds_chunk(arow + 32 * i, ch)]);
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j)
+            b[j] = __builtin_bit_cast(bf16x8_t, wb[lds_chunk(bcol + 32 * j, ch)]);
+    };
+    auto mfma_stage = [&](const uint4* buf) {
+        bf16x8_t a[2][C::kTM], b[2][C::kTN];
+        read_frags(buf, 0, a[0], b[0]);
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
-            const int ch = 2 * ks + khalf;
-            bf16x8_t a[C::kTM], b[C::kTN];
-#pragma unroll
-            for (int i = 0; i < C::kTM; ++i)
-                a[i] = __builtin_bit_cast(bf16x8_t, xb[lds_chunk(arow + 32 * i, ch)]);
-#pragma unroll
-            for (int j = 0; j < C::kTN; ++j)
-                b[j] = __builtin_bit_cast(bf16x8_t, wb[lds_chunk(bcol + 32 * j, ch)]);
+            if (ks + 1 < kBK / 16) read_frags(buf, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i)
 #pragma unroll
                 for (int j = 0; j < C::kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j],
-                                                                         0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0, 0);
         }
+    };
+    auto last = [&](int s) { return min(s, nstage - 1); };
+
+    load_stage(0, rs[0]);
+    load_stage(last(1), rs[1]);
+    store_stage(0, rs[0], lds[0]);
+    load_stage(last(2), rs[0]);
+    __syncthreads();
+    for (int s = 0; s < nstage; s += 2) {
+        // even stage s: fragments from lds[0], next stage from rs[1]
+        mfma_stage(lds[0]);
+        store_stage(last(s + 1), rs[1], lds[1]);
+        load_stage(last(s + 3), rs[1]);
+        __syncthreads();
+        // odd stage (nstage = K / 64 is a multiple of 4, so s + 1 < nstage) s + 1: fragments from lds[1], next stage from rs[0]
+        mfma_stage(lds[1]);
+        store_stage(last(s + 2), rs[0], lds[0]);
+        load_stage(last(s + 4), rs[0]);
+        __syncthreads();
     }
 
     // ---- epilogue: fp32 Y, row-major

@@ -19,7 +19,7 @@
 // each 4-bit code q under the bf16 exponent of 128 (0x43 in the high byte
 // gives the exact bf16 value 128 + q), and v_dot2_f32_bf16 multiplies two
 // such codes by two bf16 activations per instruction with fp32 accumulation.
-// X_s and -128 X_s are computed once per workgroup in LDS.  Per 8 weights:
+// X_s is computed once per workgroup, while x is staged in LDS.  Per 8 weights:
 // 3 mask/shift, 4 permutes, 4 dot2 -- no per-weight float conversion.
 //
 // Reduction.  The four lanes of a block are summed with two DPP quad
@@ -35,6 +35,9 @@
 namespace jq4k {
 
 constexpr int kGemvThreads = 256;
+constexpr int kGemvBatchMax = 16;  // problems per batched launch
+
+size_t gemv_lds_bytes(int nb, int R);
 
 __device__ __forceinline__ int x_chunk_phys(int kb, int c, int i) {
     return (kb << 5) | (c << 3) | (i ^ ((c + ((kb & 1) << 2)) & 7));
@@ -83,14 +86,14 @@ __device__ __forceinline__ QuarterLoad load_quarter(const uint8_t* blk, int c) {
 
 // Contribution of one quarter block to its row: 64 weights.
 __device__ __forceinline__ float quarter_dot(const QuarterLoad& ld, int c, const uint4* xs,
-                                             int kb, float4 xsum) {
+                                             int kb, float2 xsum) {
     const float d = half_bits_to_float(ld.hdr.x & 0xFFFFu);
     const float dmin = half_bits_to_float(ld.hdr.x >> 16);
     uint32_t scp, mp;
     scale_min_pair(static_cast<uint32_t>(c), ld.hdr.y, ld.hdr.z, ld.hdr.w, &scp, &mp);
 
-    float acc0 = xsum.x;  // -128 X_(2c)
-    float acc1 = xsum.y;  // -128 X_(2c+1)
+    float acc0 = -128.f * xsum.x;  // -128 X_(2c)
+    float acc1 = -128.f * xsum.y;  // -128 X_(2c+1)
     const uint32_t qw[8] = {ld.qa.x, ld.qa.y, ld.qa.z, ld.qa.w,
                             ld.qb.x, ld.qb.y, ld.qb.z, ld.qb.w};
 #pragma unroll
@@ -106,68 +109,84 @@ __device__ __forceinline__ float quarter_dot(const QuarterLoad& ld, int c, const
     const float sc0 = ubyte_to_float<0>(scp), sc1 = ubyte_to_float<1>(scp);
     const float m0 = ubyte_to_float<0>(mp), m1 = ubyte_to_float<1>(mp);
     const float qx = sc0 * acc0 + sc1 * acc1;
-    const float mx = m0 * xsum.z + m1 * xsum.w;
+    const float mx = m0 * xsum.x + m1 * xsum.y;
     return d * qx - dmin * mx;
 }
 
-// LDS: x chunks (nb*32 x 16 B), per-(kb, quarter) sums (nb*4 x 16 B),
-// per-block partials (R*nb floats).
-__global__ __launch_bounds__(kGemvThreads) void q4k_gemv_kernel(
-    const uint8_t* __restrict__ W, const uint4* __restrict__ X, float* __restrict__ Y,
-    int N, int nb, int R) {
-    extern __shared__ uint4 smem[];
+// LDS: x chunks (nb*32 x 16 B), per-sub-block sums X_s (nb*8 floats, as a
+// float2 (even, odd) per (kb, quarter)), per-block partials (R*nb floats).
+constexpr int kGemvDepth = 4;  // quarter tasks in flight per thread
+constexpr int kGemvMaxK = 16384;
+constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
+
+// One workgroup's share of a GEMV: rows [tile * R, tile * R + R) of W.
+__device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
+                                          const uint4* __restrict__ X, float* __restrict__ Y,
+                                          int N, int nb, int R, long tile, uint4* smem) {
     uint4* xs = smem;
-    float4* xsum = reinterpret_cast<float4*>(xs + nb * 32);
+    float2* xsum = reinterpret_cast<float2*>(xs + nb * 32);
     float* part = reinterpret_cast<float*>(xsum + nb * 4);
 
     const int t = threadIdx.x;
     const int c = t & 3;
-    const long row0 = static_cast<long>(blockIdx.x) * R;
+    const long row0 = tile * R;
     const int rows = static_cast<int>(min(static_cast<long>(R), N - row0));
     const int ntask = rows * nb * 4;
     const uint8_t* Wt = W + row0 * nb * kBlockBytes;
+    const int b0 = t >> 2;  // this thread's first block; +64 per round
 
-    // First task's weights are requested before x is staged.
-    int b = t >> 2;
-    QuarterLoad cur = {};
-    if (t < ntask) cur = load_quarter(Wt + static_cast<long>(b) * kBlockBytes, c);
-
-    for (int g = t; g < nb * 32; g += kGemvThreads) {
-        const int kb = g >> 5, cc = (g >> 3) & 3, i = g & 7;
-        xs[x_chunk_phys(kb, cc, i)] = X[g];
+    // Memory requests in the order they are needed (vmcnt retires in order):
+    // x first, then the first kGemvDepth rounds of weights, so that staging
+    // x waits only for x and each round waits only for its own weights.
+    const int nxc = nb * 32;  // 16-byte chunks of x, at most 2048 (K <= 16384)
+    uint4 xv[kGemvMaxXChunksPerThread];
+#pragma unroll
+    for (int j = 0; j < kGemvMaxXChunksPerThread; ++j)
+        if (t + j * kGemvThreads < nxc) xv[j] = X[t + j * kGemvThreads];
+    QuarterLoad ld[kGemvDepth];
+#pragma unroll
+    for (int u = 0; u < kGemvDepth; ++u) {
+        ld[u] = {};
+        if (t + u * kGemvThreads < ntask)
+            ld[u] = load_quarter(Wt + static_cast<long>(b0 + 64 * u) * kBlockBytes, c);
     }
-    __syncthreads();
-    for (int u = t; u < nb * 4; u += kGemvThreads) {
-        const int kb = u >> 2, cc = u & 3;
-        float s[2] = {0.f, 0.f};
+
+    // Stage x; each quad of lanes holds one half sub-block (4 chunks of 8),
+    // so two DPP steps give X_s for every sub-block.
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = xs[x_chunk_phys(kb, cc, 4 * h + i)];
-                s[h] += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) +
-                        bf16_lo(v.z) + bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
-            }
+    for (int j = 0; j < kGemvMaxXChunksPerThread; ++j) {
+        const int g = t + j * kGemvThreads;
+        if (g < nxc) {
+            const int kb = g >> 5, cc = (g >> 3) & 3, i = g & 7;
+            const uint4 v = xv[j];
+            xs[x_chunk_phys(kb, cc, i)] = v;
+            float sum = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+                        ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+            sum = quad_sum(sum);
+            if ((g & 3) == 0) reinterpret_cast<float*>(xsum)[g >> 2] = sum;
         }
-        xsum[u] = make_float4(-128.f * s[0], -128.f * s[1], s[0], s[1]);
     }
     __syncthreads();
 
-    // Rounds: block index b advances by 64 (256 threads / 4 lanes per block).
     const int kb_step = 64 % nb;
-    int kb = b % nb;
-    for (int tau = t; tau < ntask; tau += kGemvThreads) {
-        const int nb_next = b + 64;
-        QuarterLoad nxt = {};
-        if (tau + kGemvThreads < ntask)
-            nxt = load_quarter(Wt + static_cast<long>(nb_next) * kBlockBytes, c);
-        float p = quarter_dot(cur, c, xs, kb, xsum[kb * 4 + c]);
-        p = quad_sum(p);
-        if (c == 0) part[b] = p;
-        cur = nxt;
-        b = nb_next;
-        kb += kb_step;
-        if (kb >= nb) kb -= nb;
+    int kb = b0 % nb;
+    for (int r0 = 0; t + r0 * kGemvThreads < ntask; r0 += kGemvDepth) {
+#pragma unroll
+        for (int u = 0; u < kGemvDepth; ++u) {
+            const int tau = t + (r0 + u) * kGemvThreads;
+            if (tau < ntask) {
+                const int b = b0 + 64 * (r0 + u);
+                const float2 xsm = xsum[kb * 4 + c];
+                float p = quarter_dot(ld[u], c, xs, kb, xsm);
+                p = quad_sum(p);
+                if (c == 0) part[b] = p;
+                if (tau + kGemvDepth * kGemvThreads < ntask)
+                    ld[u] = load_quarter(Wt + static_cast<long>(b + 64 * kGemvDepth) * kBlockBytes,
+                                         c);
+            }
+            kb += kb_step;
+            if (kb >= nb) kb -= nb;
+        }
     }
     __syncthreads();
     for (int r = t; r < rows; r += kGemvThreads) {
@@ -177,8 +196,58 @@ __global__ __launch_bounds__(kGemvThreads) void q4k_gemv_kernel(
     }
 }
 
+__global__ __launch_bounds__(kGemvThreads) void q4k_gemv_kernel(
+    const uint8_t* __restrict__ W, const uint4* __restrict__ X, float* __restrict__ Y,
+    int N, int nb, int R) {
+    extern __shared__ uint4 smem[];
+    gemv_tile(W, X, Y, N, nb, R, blockIdx.x, smem);
+}
+
+// Several independent GEMVs in one launch: workgroups [first[p], first[p+1])
+// belong to problem p.  The descriptors travel in the kernel arguments.
+struct GemvProblem {
+    const uint8_t* W;
+    const uint4* X;
+    float* Y;
+    int N, nb, R;
+};
+
+struct GemvBatch {
+    GemvProblem p[kGemvBatchMax];
+    int first[kGemvBatchMax + 1];
+    int count;
+};
+
+__global__ __launch_bounds__(kGemvThreads) void q4k_gemv_batched_kernel(const GemvBatch batch) {
+    extern __shared__ uint4 smem[];
+    const int wg = blockIdx.x;
+    int p = 0;
+    while (p + 1 < batch.count && wg >= batch.first[p + 1]) ++p;
+    const GemvProblem& pr = batch.p[p];
+    gemv_tile(pr.W, pr.X, pr.Y, pr.N, pr.nb, pr.R, wg - batch.first[p], smem);
+}
+
+hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X,
+                               float* const* Y, const int* N, const int* K, const int* R,
+                               int count, hipStream_t stream) {
+    GemvBatch b = {};
+    size_t lds = 0;
+    int total = 0;
+    b.count = count;
+    for (int i = 0; i < count; ++i) {
+        const int nb = K[i] / kQK;
+        b.p[i] = {W[i], reinterpret_cast<const uint4*>(X[i]), Y[i], N[i], nb, R[i]};
+        b.first[i] = total;
+        total += static_cast<int>((static_cast<long>(N[i]) + R[i] - 1) / R[i]);
+        lds = gemv_lds_bytes(nb, R[i]) > lds ? gemv_lds_bytes(nb, R[i]) : lds;
+    }
+    b.first[count] = total;
+    hipLaunchKernelGGL(q4k_gemv_batched_kernel, dim3(total), dim3(kGemvThreads), lds, stream, b);
+    return hipGetLastError();
+}
+
 size_t gemv_lds_bytes(int nb, int R) {
-    return static_cast<size_t>(nb) * 32 * 16 + static_cast<size_t>(nb) * 4 * 16 +
+    return static_cast<size_t>(nb) * 32 * 16 + static_cast<size_t>(nb) * 4 * 8 +
            static_cast<size_t>(R) * nb * 4;
 }
 

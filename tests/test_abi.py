@@ -116,3 +116,41 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(jq4k, "LIB_PATH", "/nonexistent/libjq4k.so")
     with pytest.raises(ImportError):
         jq4k.raw()
+
+
+def test_gemv_rows_argument_checks(L):
+    f = L.jq4k_gemv_rows
+    assert f(ALIGNED, ALIGNED2, ALIGNED3, 8, 256, -1, None) == jq4k.EINVAL
+    assert f(ALIGNED, ALIGNED2, ALIGNED3, 8, 100, 4, None) == jq4k.EINVAL
+    assert f(ALIGNED, ALIGNED2, ALIGNED3, 8, jq4k.GEMV_MAX_K + 256, 4, None) == jq4k.EINVAL
+    # 4096 rows of K = 16384 need 1 MiB of partials: beyond the LDS budget
+    assert f(ALIGNED, ALIGNED2, ALIGNED3, 8, 16384, 4096, None) == jq4k.EINVAL
+    assert f(ALIGNED + 4, ALIGNED2, ALIGNED3, 8, 256, 4, None) == jq4k.EALIGN
+    assert f(0, 0, 0, 0, 256, 4, None) == jq4k.OK
+
+
+def _descs(*rows):
+    arr = (jq4k.GemvDesc * max(len(rows), 1))()
+    for i, r in enumerate(rows):
+        arr[i] = jq4k.GemvDesc(*r)
+    return arr
+
+
+def test_gemv_batched_argument_checks(L):
+    f = L.jq4k_gemv_batched
+    good = (ALIGNED, ALIGNED2, ALIGNED3, 8, 256)
+    assert f(None, 0, None) == jq4k.OK
+    assert f(None, 2, None) == jq4k.EINVAL
+    assert f(ctypes.addressof(_descs(good)), -1, None) == jq4k.EINVAL
+    many = _descs(*([good] * 17))
+    assert f(ctypes.addressof(many), 17, None) == jq4k.EINVAL
+    for bad, code in (((ALIGNED, ALIGNED2, ALIGNED3, 8, 100), jq4k.EINVAL),
+                      ((ALIGNED, ALIGNED2, ALIGNED3, -8, 256), jq4k.EINVAL),
+                      ((ALIGNED, ALIGNED2, ALIGNED3, 8, jq4k.GEMV_MAX_K + 256), jq4k.EINVAL),
+                      ((0, ALIGNED2, ALIGNED3, 8, 256), jq4k.EINVAL),
+                      ((ALIGNED + 8, ALIGNED2, ALIGNED3, 8, 256), jq4k.EALIGN),
+                      ((ALIGNED, ALIGNED2, ALIGNED3 + 1, 8, 256), jq4k.EALIGN)):
+        arr = _descs(good, bad)          # one bad problem rejects the whole batch
+        assert f(ctypes.addressof(arr), 2, None) == code, bad
+    empty = _descs((0, 0, 0, 0, 256), (0, 0, 0, 0, 512))
+    assert f(ctypes.addressof(empty), 2, None) == jq4k.OK

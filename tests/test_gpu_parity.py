@@ -43,6 +43,18 @@ def _special_blocks(g, nb):
 
 # ------------------------------------------------------------ exports
 
+def _assert_same_weights(got_bits, ref_bits, zero_mask_got, zero_mask_ref, W, what):
+    """Bit equality, with +0 and -0 taken as the same weight: the exact value
+    d*sc*q - dmin*m = 0 has no sign (the GPU's fma can return -0 when d < 0)."""
+    same = (got_bits == ref_bits) | (zero_mask_got & zero_mask_ref)
+    if not same.all():
+        idx = np.flatnonzero(~same)[:8]
+        rows = [(int(i) // 256, int(i) % 256, hex(int(W[i // 256, 0]) | int(W[i // 256, 1]) << 8),
+                 hex(int(W[i // 256, 2]) | int(W[i // 256, 3]) << 8), hex(int(got_bits[i])),
+                 hex(int(ref_bits[i]))) for i in idx]
+        raise AssertionError(f"{what}: {int((~same).sum())} weights differ; "
+                             f"(block, i, d, dmin, gpu, ref): {rows}")
+
 def test_unpack_fields_bit_exact(gpu):
     g = np.random.default_rng(100)
     W = np.concatenate([g.integers(0, 256, (3000, 144), dtype=np.uint8)] +
@@ -69,7 +81,8 @@ def test_dequant_f32_bit_exact(gpu):
     gpu.dequant_f32(dev(W), w)
     ref = oracle.dequant_f32(W)
     got = host(w)
-    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    _assert_same_weights(got.view(np.uint32), ref.view(np.uint32), got == 0, ref == 0, W,
+                         "dequant_f32")
 
 
 def test_dequant_bf16_bit_exact(gpu):
@@ -79,7 +92,9 @@ def test_dequant_bf16_bit_exact(gpu):
     announce(f"dequant_bf16 nblocks={nb}")
     w = torch.zeros(nb * 256, dtype=torch.int16, device="cuda:0")
     gpu.dequant_bf16(dev(W), w)
-    assert np.array_equal(host(w).view(np.uint16), oracle.dequant_bf16(W))
+    got = host(w).view(np.uint16)
+    ref = oracle.dequant_bf16(W)
+    _assert_same_weights(got, ref, (got & 0x7FFF) == 0, (ref & 0x7FFF) == 0, W, "dequant_bf16")
 
 
 # ------------------------------------------------------------ M = 1
@@ -134,6 +149,31 @@ def test_gemv_closed_form_constant_blocks(gpu):
     announce("gemv closed form")
     y = run_gemm(W, X, N, K, path="gemv")
     assert np.all(y == -10.0)
+
+
+def test_gemv_batched_decode_layer(gpu):
+    """One launch for the seven independent projections: every output equals
+    the per-problem GEMV bit for bit, and meets the oracle bound."""
+    layer = qi.decode_layer(1, 0, 1)
+    g = np.random.default_rng(109)
+    extra = [("odd", 77, 768, qi.weight_bytes(g, 77, 768), qi.activations(g, 1, 768)),
+             ("empty", 0, 512, np.zeros((0, 288), np.uint8), qi.activations(g, 1, 512))]
+    probs = layer + extra
+    Wd = [dev(W) for _, N, K, W, _ in probs]
+    Xd = [dev(X).view(torch.bfloat16) for *_, X in probs]
+    Yb = [torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda:0")
+          for _, N, *_ in probs]
+    announce(f"gemv batched {len(probs)} problems")
+    gpu.gemv_batched(list(zip(Wd, Xd, Yb)))
+    for (name, N, K, W, X), wd, xd, yb in zip(probs, Wd, Xd, Yb):
+        if N == 0:
+            continue
+        ys = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+        gpu.gemv(wd, xd, ys)
+        got, single = host(yb), host(ys)
+        assert np.array_equal(got.view(np.uint32), single.view(np.uint32)), name
+        Y, A = oracle.gemm(W, X, N, K)
+        parity(got, Y, A, f"batched {name}")
 
 
 # ------------------------------------------------------------ M > 1 (MFMA)
