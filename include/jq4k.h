@@ -138,7 +138,8 @@ int jq4k_gemm(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
 #define JQ4K_PATH_MFMA 2 /* the MFMA kernel, tile chosen by shape        */
 #define JQ4K_PATH_MFMA_T64 3  /* MFMA kernel, 64-row M tile              */
 #define JQ4K_PATH_MFMA_T128 4 /* MFMA kernel, 128-row M tile             */
-#define JQ4K_PATH_MFMA_T256 5 /* MFMA kernel, 256-row M tile             */
+#define JQ4K_PATH_MFMA_T256 5 /* MFMA kernel, 256-row M tile, eight waves  */
+                              /* (four dequantise, four multiply)         */
 
 /* jq4k_gemm with an explicit kernel path; JQ4K_EINVAL for an unknown path
  * or JQ4K_PATH_GEMV with M != 1.  Results meet the same bound on every path. */

@@ -18,7 +18,7 @@ template <ExportKind kind>
 __global__ __launch_bounds__(kExportThreads) void q4k_export_kernel(
     const uint8_t* __restrict__ W, long nblocks, uint8_t* __restrict__ q,
     uint8_t* __restrict__ sc, uint8_t* __restrict__ m, float* __restrict__ wf,
-    uint32_t* __restrict__ wh) {
+    uint32_t* __restrict__ wh, uint32_t qmask) {
     const int t = threadIdx.x;
     for (long b = blockIdx.x; b < nblocks; b += gridDim.x) {
         const uint8_t* blk = W + b * kBlockBytes;
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kExportThreads) void q4k_export_kernel(
             const long lo0 = b * kQK + 64 * c + p;  // first even-sub-block weight
             const long hi0 = lo0 + 32;              // first odd-sub-block weight
             if constexpr (kind == ExportKind::kFields) {
-                const uint32_t ql = low_quants(v), qh = high_quants(v);
+                const uint32_t ql = low_quants_rt(v, qmask), qh = high_quants_rt(v, qmask);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     q[lo0 + i] = static_cast<uint8_t>(ql >> (8 * i));
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kExportThreads) void q4k_export_kernel(
             } else if constexpr (kind == ExportKind::kF32) {
                 const QuarterScales s = quarter_scales(hdr, static_cast<uint32_t>(c));
                 float lo[4], hi[4];
-                dequant_dword_f32(v, s, lo, hi);
+                dequant_dword_f32(v, s, lo, hi, qmask);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     wf[lo0 + i] = lo[i];
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kExportThreads) void q4k_export_kernel(
             } else {
                 const QuarterScales s = quarter_scales(hdr, static_cast<uint32_t>(c));
                 uint32_t lo2[2], hi2[2];
-                dequant_dword_bf16(v, s, lo2, hi2);
+                dequant_dword_bf16(v, s, lo2, hi2, qmask);
                 wh[lo0 / 2] = lo2[0];
                 wh[lo0 / 2 + 1] = lo2[1];
                 wh[hi0 / 2] = hi2[0];
@@ -75,21 +75,21 @@ static unsigned export_grid(long nblocks) {
 hipError_t launch_unpack_fields(const uint8_t* W, long nblocks, uint8_t* q, uint8_t* sc,
                                 uint8_t* m, hipStream_t stream) {
     hipLaunchKernelGGL(q4k_export_kernel<ExportKind::kFields>, dim3(export_grid(nblocks)),
-                       dim3(kExportThreads), 0, stream, W, nblocks, q, sc, m, nullptr, nullptr);
+                       dim3(kExportThreads), 0, stream, W, nblocks, q, sc, m, nullptr, nullptr, kNibbleMask);
     return hipGetLastError();
 }
 
 hipError_t launch_dequant_f32(const uint8_t* W, long nblocks, float* w, hipStream_t stream) {
     hipLaunchKernelGGL(q4k_export_kernel<ExportKind::kF32>, dim3(export_grid(nblocks)),
                        dim3(kExportThreads), 0, stream, W, nblocks, nullptr, nullptr, nullptr, w,
-                       nullptr);
+                       nullptr, kNibbleMask);
     return hipGetLastError();
 }
 
 hipError_t launch_dequant_bf16(const uint8_t* W, long nblocks, uint16_t* w, hipStream_t stream) {
     hipLaunchKernelGGL(q4k_export_kernel<ExportKind::kBf16>, dim3(export_grid(nblocks)),
                        dim3(kExportThreads), 0, stream, W, nblocks, nullptr, nullptr, nullptr,
-                       nullptr, reinterpret_cast<uint32_t*>(w));
+                       nullptr, reinterpret_cast<uint32_t*>(w), kNibbleMask);
     return hipGetLastError();
 }
 

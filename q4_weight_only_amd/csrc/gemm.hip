@@ -13,9 +13,8 @@
 // LDS is double-buffered and the loop is software-pipelined: while stage s
 // is on the matrix cores, stage s+1 is dequantised into the other buffer and
 // the global loads of stages s+2 and s+3 are in flight; one barrier per stage.
-// LDS rows are 128 bytes (8 chunks of 16 bytes); chunk i of row r is stored
-// at i ^ (r & 7) so the 32 rows an MFMA operand read touches hit distinct
-// bank groups.
+// LDS rows are 128 bytes (8 chunks of 16 bytes), XOR-swizzled by row (see
+// lds_chunk) so the operand reads hit distinct banks.
 //
 // Operand layouts (v_mfma_f32_32x32x16_bf16): lane l supplies row l % 32 of
 // A and column l % 32 of B, k = 8 (l / 32) .. +7 of the 16-wide k step; the
@@ -30,8 +29,13 @@ constexpr int kBK = 64;               // K per stage: one quarter block
 constexpr int kRowChunks = kBK / 8;   // 16-byte chunks per LDS row
 constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
 
+// Chunk c of tile row r sits at chunk c ^ f(r), f(r) = (r >> 1) ^ 4 (r & 1).
+// An MFMA operand read has 16 lanes on 16 consecutive rows and one chunk;
+// f gives them 16 different 16-byte slots in every 256-byte window (and 8
+// different slots in every 128-byte window for each run of 8 lanes), so
+// reads and the row-wise tile writes are free of bank conflicts.
 __device__ __forceinline__ int lds_chunk(int row, int chunk) {
-    return row * kRowChunks + (chunk ^ (row & 7));
+    return row * kRowChunks + (chunk ^ (((row >> 1) ^ ((row & 1) << 2)) & 7));
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -51,7 +55,7 @@ struct GemmCfg {
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ X, float* __restrict__ Y,
-    int M, int N, int K, int ntiles, int per_xcd) {
+    int M, int N, int K, int ntiles, int per_xcd, uint32_t qmask) {
     using C = GemmCfg<BM, BN, WM, WN>;
     __shared__ uint4 lds[2][C::kLdsChunks];
 
@@ -130,8 +134,8 @@ __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < C::kQBytes / 8; ++j) {
             uint32_t lo_a[2], hi_a[2], lo_b[2], hi_b[2];
-            dequant_dword_bf16(r.q[2 * j], sc, lo_a, hi_a);
-            dequant_dword_bf16(r.q[2 * j + 1], sc, lo_b, hi_b);
+            dequant_dword_bf16(r.q[2 * j], sc, lo_a, hi_a, qmask);
+            dequant_dword_bf16(r.q[2 * j + 1], sc, lo_b, hi_b, qmask);
             const int ch = (qoff >> 3) + j;
             wbuf[lds_chunk(wr, ch)] = make_uint4(lo_a[0], lo_a[1], lo_b[0], lo_b[1]);
             wbuf[lds_chunk(wr, 4 + ch)] = make_uint4(hi_a[0], hi_a[1], hi_b[0], hi_b[1]);
@@ -224,7 +228,7 @@ static hipError_t launch_cfg(const uint8_t* W, const uint16_t* X, float* Y, int 
     const long per_xcd = (ntiles + kXcds - 1) / kXcds;
     hipLaunchKernelGGL((q4k_gemm_mfma_kernel<BM, BN, WM, WN>), dim3(per_xcd * kXcds),
                        dim3(kGemmThreads), 0, stream, W, X, Y, M, N, K,
-                       static_cast<int>(ntiles), static_cast<int>(per_xcd));
+                       static_cast<int>(ntiles), static_cast<int>(per_xcd), kNibbleMask);
     return hipGetLastError();
 }
 
@@ -233,14 +237,12 @@ long gemm_tile_count(int M, int N, int tile) {
     return static_cast<long>((N + bn - 1) / bn) * ((M + tile - 1) / tile);
 }
 
-// tile: 64, 128 or 256 rows of M per workgroup.
+// tile: 64 or 128 rows of M per workgroup (the 256-row tile is the
+// wave-specialised kernel of gemm_ws.hip).
 hipError_t launch_gemm_mfma(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
                             int tile, hipStream_t stream) {
-    switch (tile) {
-        case 64: return launch_cfg<64, 256, 1, 4>(W, X, Y, M, N, K, stream);
-        case 128: return launch_cfg<128, 128, 2, 2>(W, X, Y, M, N, K, stream);
-        default: return launch_cfg<256, 128, 2, 2>(W, X, Y, M, N, K, stream);
-    }
+    if (tile == 64) return launch_cfg<64, 256, 1, 4>(W, X, Y, M, N, K, stream);
+    return launch_cfg<128, 128, 2, 2>(W, X, Y, M, N, K, stream);
 }
 
 }  // namespace jq4k

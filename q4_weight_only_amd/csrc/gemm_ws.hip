@@ -1,0 +1,199 @@
+// gemm_ws.hip -- wave-specialised Q4_K matmul on the gfx950 matrix cores.
+//
+// Y (M x N) = X (M x K) . W^T with W in Q4_K (genie-ai-runtime README, "At a
+// glance": "tensor-core MMQ Q4_K prefill"), for large M.  A workgroup of
+// eight waves computes a 256 x 128 tile of Y.  The dequantisation of W is
+// vector-ALU work of about three instructions per weight, done once per tile;
+// instead of interleaving it with the matrix instructions in one stream, the
+// workgroup splits the roles by wave:
+//   * waves 0..3 (consumers) only read operand fragments from LDS and issue
+//     v_mfma_f32_32x32x16_bf16 into fp32 accumulators (each owns 128 x 64);
+//   * waves 4..7 (producers) fetch the next stages of X (bf16) and W (header
+//     + quant bytes), dequantise W to bf16 (fma(d*sc, q, -dmin*m) rounded
+//     once, then rounded to bf16) and write both slabs to LDS.
+// The hardware places one consumer and one producer wave on each SIMD, so the
+// vector ALU and the matrix core run side by side.  The K loop advances one
+// quarter block (64 weights) per stage; LDS holds two stages and one barrier
+// per stage hands a filled buffer from producers to consumers.  Producers keep
+// two register sets, so global data has two stages of time to arrive.
+#include "q4k_device.h"
+
+namespace jq4k {
+
+namespace {
+
+constexpr int kWsThreads = 512;
+constexpr int kWsBM = 256, kWsBN = 128, kWsBK = 64;
+constexpr int kWsRowChunks = kWsBK / 8;
+constexpr int kWsXcds = 8;
+constexpr int kWsLdsChunks = (kWsBM + kWsBN) * kWsRowChunks;   // per buffer
+constexpr int kWsXChunks = kWsBM * kWsRowChunks / 256;          // per producer thread
+constexpr int kWsTM = 4, kWsTN = 2;                             // 32x32 tiles per consumer
+
+// Same swizzle as the single-role kernel: chunk c of row r at c ^ f(r).
+__device__ __forceinline__ int ws_chunk(int row, int chunk) {
+    return row * kWsRowChunks + (chunk ^ (((row >> 1) ^ ((row & 1) << 2)) & 7));
+}
+
+struct WsRegs {
+    uint4 x[kWsXChunks];
+    uint4 hdr;
+    uint4 q;  // 16 quant bytes: half of the row's quarter
+};
+
+}  // namespace
+
+__global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(
+    const uint8_t* __restrict__ W, const uint16_t* __restrict__ X, float* __restrict__ Y,
+    int M, int N, int K, int ntiles, int per_xcd, uint32_t qmask) {
+    __shared__ uint4 lds[2][kWsLdsChunks];
+
+    const int t = threadIdx.x;
+    const int wave = t >> 6, lane = t & 63;
+
+    const int ntile_n = (N + kWsBN - 1) / kWsBN;
+    const int lin = (blockIdx.x % kWsXcds) * per_xcd + blockIdx.x / kWsXcds;
+    if (lin >= ntiles) return;
+    const int n0 = (lin % ntile_n) * kWsBN, m0 = (lin / ntile_n) * kWsBM;
+    const int nb = K / kQK;
+    const int nstage = K / kWsBK;  // a multiple of 4
+    auto last = [&](int s) { return min(s, nstage - 1); };
+
+    // The two roles run separate loops (their registers never need to be
+    // live together); both loops pass the same 1 + nstage barriers.
+    if (wave >= 4) {
+        // ---------------- producers: fetch, dequantise, fill LDS
+        const int pt = t - 256;                        // 0..255
+        const int wr = pt >> 1, qoff = (pt & 1) * 16;  // W row of the tile, quant byte offset
+        // Rows past N (or M) are clamped to the last row: they only feed
+        // outputs that are never stored.
+        const uint8_t* wrow = W + static_cast<long>(min(n0 + wr, N - 1)) * nb * kBlockBytes;
+        const uint16_t* xrow[kWsXChunks];
+        int xlds[kWsXChunks];
+#pragma unroll
+        for (int j = 0; j < kWsXChunks; ++j) {
+            const int g = pt + j * 256;
+            xrow[j] = X + static_cast<long>(min(m0 + (g >> 3), M - 1)) * K + (g & 7) * 8;
+            xlds[j] = ws_chunk(g >> 3, g & 7);
+        }
+        const int wlds_lo0 = kWsBM * kWsRowChunks + ws_chunk(wr, (qoff >> 3));
+        const int wlds_lo1 = kWsBM * kWsRowChunks + ws_chunk(wr, (qoff >> 3) + 1);
+        const int wlds_hi0 = kWsBM * kWsRowChunks + ws_chunk(wr, 4 + (qoff >> 3));
+        const int wlds_hi1 = kWsBM * kWsRowChunks + ws_chunk(wr, 5 + (qoff >> 3));
+        WsRegs rs[2];
+        auto load_stage = [&](int s, WsRegs& r) {
+#pragma unroll
+            for (int j = 0; j < kWsXChunks; ++j)
+                r.x[j] = *reinterpret_cast<const uint4*>(xrow[j] + s * kWsBK);
+            const uint8_t* blk = wrow + (s >> 2) * kBlockBytes;
+            r.hdr = *reinterpret_cast<const uint4*>(blk);
+            r.q = *reinterpret_cast<const uint4*>(blk + 16 + 32 * (s & 3) + qoff);
+        };
+        auto store_stage = [&](int s, const WsRegs& r, uint4* buf) {
+#pragma unroll
+            for (int j = 0; j < kWsXChunks; ++j) buf[xlds[j]] = r.x[j];
+            const QuarterScales sc = quarter_scales(r.hdr, static_cast<uint32_t>(s & 3));
+            uint32_t lo_a[2], hi_a[2], lo_b[2], hi_b[2];
+            dequant_dword_bf16(r.q.x, sc, lo_a, hi_a, qmask);
+            dequant_dword_bf16(r.q.y, sc, lo_b, hi_b, qmask);
+            buf[wlds_lo0] = make_uint4(lo_a[0], lo_a[1], lo_b[0], lo_b[1]);
+            buf[wlds_hi0] = make_uint4(hi_a[0], hi_a[1], hi_b[0], hi_b[1]);
+            dequant_dword_bf16(r.q.z, sc, lo_a, hi_a, qmask);
+            dequant_dword_bf16(r.q.w, sc, lo_b, hi_b, qmask);
+            buf[wlds_lo1] = make_uint4(lo_a[0], lo_a[1], lo_b[0], lo_b[1]);
+            buf[wlds_hi1] = make_uint4(hi_a[0], hi_a[1], hi_b[0], hi_b[1]);
+        };
+        load_stage(0, rs[0]);
+        load_stage(last(1), rs[1]);
+        store_stage(0, rs[0], lds[0]);
+        load_stage(last(2), rs[0]);
+        __syncthreads();
+        for (int s = 0; s < nstage; s += 2) {
+            store_stage(last(s + 1), rs[1], lds[1]);
+            load_stage(last(s + 3), rs[1]);
+            __syncthreads();
+            store_stage(last(s + 2), rs[0], lds[0]);
+            load_stage(last(s + 4), rs[0]);
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---------------- consumers: LDS fragments -> MFMA -> fp32 Y
+    const int wm = wave >> 1, wn = wave & 1;
+    const int arow = wm * 128 + (lane & 31);
+    const int bcol = wn * 64 + (lane & 31);
+    const int khalf = lane >> 5;
+    float16_t acc[kWsTM][kWsTN];
+#pragma unroll
+    for (int i = 0; i < kWsTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kWsTN; ++j) acc[i][j] = float16_t{};
+    auto read_frags = [&](const uint4* buf, int ks, bf16x8_t* a, bf16x8_t* b) {
+        const uint4* wb = buf + kWsBM * kWsRowChunks;
+        const int ch = 2 * ks + khalf;
+#pragma unroll
+        for (int i = 0; i < kWsTM; ++i)
+            a[i] = __builtin_bit_cast(bf16x8_t, buf[ws_chunk(arow + 32 * i, ch)]);
+#pragma unroll
+        for (int j = 0; j < kWsTN; ++j)
+            b[j] = __builtin_bit_cast(bf16x8_t, wb[ws_chunk(bcol + 32 * j, ch)]);
+    };
+    auto mma = [&](const bf16x8_t* a, const bf16x8_t* b) {
+#pragma unroll
+        for (int i = 0; i < kWsTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kWsTN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0,
+                                                                     0);
+    };
+    // four k-steps of 16; the fragments of step ks + 1 are read while step ks
+    // multiplies (two named fragment sets, kept in registers)
+    auto mfma_stage = [&](const uint4* buf) {
+        bf16x8_t a0[kWsTM], b0[kWsTN], a1[kWsTM], b1[kWsTN];
+        read_frags(buf, 0, a0, b0);
+        read_frags(buf, 1, a1, b1);
+        mma(a0, b0);
+        read_frags(buf, 2, a0, b0);
+        mma(a1, b1);
+        read_frags(buf, 3, a1, b1);
+        mma(a0, b0);
+        mma(a1, b1);
+    };
+    __syncthreads();
+    for (int s = 0; s < nstage; s += 2) {
+        mfma_stage(lds[0]);
+        __syncthreads();
+        mfma_stage(lds[1]);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < kWsTM; ++i) {
+#pragma unroll
+        for (int j = 0; j < kWsTN; ++j) {
+            const int n = n0 + wn * 64 + 32 * j + (lane & 31);
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                if (m < M) Y[static_cast<long>(m) * N + n] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+long gemm_ws_tile_count(int M, int N) {
+    return static_cast<long>((N + kWsBN - 1) / kWsBN) * ((M + kWsBM - 1) / kWsBM);
+}
+
+hipError_t launch_gemm_ws(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
+                          hipStream_t stream) {
+    const long ntiles = gemm_ws_tile_count(M, N);
+    const long per_xcd = (ntiles + kWsXcds - 1) / kWsXcds;
+    hipLaunchKernelGGL(q4k_gemm_ws_kernel, dim3(per_xcd * kWsXcds), dim3(kWsThreads), 0, stream,
+                       W, X, Y, M, N, K, static_cast<int>(ntiles), static_cast<int>(per_xcd),
+                       kNibbleMask);
+    return hipGetLastError();
+}
+
+}  // namespace jq4k

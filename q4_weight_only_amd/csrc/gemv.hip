@@ -27,9 +27,8 @@
 // its nb block values in order (deterministic, no atomics).
 //
 // LDS layout of x.  x is stored as 16-byte chunks, chunk g = 32 kb + 8 c + i
-// (i = 0..3 the even sub-block, 4..7 the odd one), with i XOR-ed by
-// (c + 4 (kb & 1)) so that the eight lanes of two neighbouring blocks read
-// eight different bank groups.
+// (i = 0..3 the even sub-block, 4..7 the odd one), with i XOR-swizzled by
+// block and quarter (x_chunk_phys) so the reads are free of bank conflicts.
 #include "q4k_device.h"
 
 namespace jq4k {
@@ -39,8 +38,13 @@ constexpr int kGemvBatchMax = 16;  // problems per batched launch
 
 size_t gemv_lds_bytes(int nb, int R);
 
+// A 16-lane group of a round reads one chunk index i for 4 consecutive
+// blocks x 4 quarters; XOR-ing i by g(kb, c) gives those 16 lanes 16
+// different 16-byte slots in each 256-byte window (and each 8-lane half 8
+// different slots in a 128-byte window): no bank conflicts.
 __device__ __forceinline__ int x_chunk_phys(int kb, int c, int i) {
-    return (kb << 5) | (c << 3) | (i ^ ((c + ((kb & 1) << 2)) & 7));
+    const int g = ((c >> 1) | ((kb & 3) << 1)) ^ ((c & 1) << 2);
+    return (kb << 5) | (c << 3) | (i ^ (g & 7));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }

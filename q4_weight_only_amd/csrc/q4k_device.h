@@ -19,6 +19,7 @@ namespace jq4k {
 
 constexpr int kQK = 256;          // weights per block
 constexpr int kBlockBytes = 144;  // bytes per block
+constexpr uint32_t kNibbleMask = 0x0F0F0F0Fu;  // value of the run-time `mask` arguments
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -64,7 +65,18 @@ __device__ __forceinline__ void scale_min_pair(uint32_t c, uint32_t s0, uint32_t
 __device__ __forceinline__ uint32_t low_quants(uint32_t v) { return v & 0x0F0F0F0Fu; }
 __device__ __forceinline__ uint32_t high_quants(uint32_t v) { return (v >> 4) & 0x0F0F0F0Fu; }
 
-// Byte k of a 32-bit word as fp32 (selected to one v_cvt_f32_ubyte{k}).
+// The same with the nibble mask supplied at run time (a kernel argument equal
+// to 0x0F0F0F0F).  With a compile-time mask the compiler turns "mask, then
+// convert byte k" into a bit-field extract plus a byte-0 convert, one extra
+// instruction per weight; an opaque mask keeps one v_cvt_f32_ubyte{k} per
+// weight.
+__device__ __forceinline__ uint32_t low_quants_rt(uint32_t v, uint32_t mask) { return v & mask; }
+__device__ __forceinline__ uint32_t high_quants_rt(uint32_t v, uint32_t mask) {
+    return (v >> 4) & mask;
+}
+
+// Byte k of a 32-bit word as fp32 (one v_cvt_f32_ubyte{k} when the compiler
+// cannot see which bits of the word are zero; see low_quants_rt).
 template <int k>
 __device__ __forceinline__ float ubyte_to_float(uint32_t v) {
     return static_cast<float>((v >> (8 * k)) & 0xFFu);
@@ -94,9 +106,10 @@ __device__ __forceinline__ QuarterScales quarter_scales(uint4 hdr, uint32_t c) {
 
 // fp32 weights of one qs dword: lo[0..3] are weights 64c + p + 0..3 and
 // hi[0..3] are weights 64c + 32 + p + 0..3, p = byte offset within the quarter.
+// `mask` is 0x0F0F0F0F, passed in at run time (see low_quants_rt).
 __device__ __forceinline__ void dequant_dword_f32(uint32_t v, const QuarterScales& s,
-                                                  float lo[4], float hi[4]) {
-    const uint32_t ql = low_quants(v), qh = high_quants(v);
+                                                  float lo[4], float hi[4], uint32_t mask) {
+    const uint32_t ql = low_quants_rt(v, mask), qh = high_quants_rt(v, mask);
     lo[0] = __builtin_fmaf(s.ds0, ubyte_to_float<0>(ql), -s.dm0);
     lo[1] = __builtin_fmaf(s.ds0, ubyte_to_float<1>(ql), -s.dm0);
     lo[2] = __builtin_fmaf(s.ds0, ubyte_to_float<2>(ql), -s.dm0);
@@ -116,9 +129,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // bf16 weights of one qs dword, as two packed pairs per half:
 // lo2[0] = (w0, w1), lo2[1] = (w2, w3) of the even sub-block; hi2 likewise.
 __device__ __forceinline__ void dequant_dword_bf16(uint32_t v, const QuarterScales& s,
-                                                   uint32_t lo2[2], uint32_t hi2[2]) {
+                                                   uint32_t lo2[2], uint32_t hi2[2],
+                                                   uint32_t mask) {
     float lo[4], hi[4];
-    dequant_dword_f32(v, s, lo, hi);
+    dequant_dword_f32(v, s, lo, hi, mask);
     lo2[0] = pack_bf16x2(lo[0], lo[1]);
     lo2[1] = pack_bf16x2(lo[2], lo[3]);
     hi2[0] = pack_bf16x2(hi[0], hi[1]);
