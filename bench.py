@@ -83,6 +83,7 @@ def timed(torch, fn, steps, warmup, use_graph):
 
 
 DEPENDENCY_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]   # q|k|v, o, gate|up, down
+PREFILL_KERNEL = "jq4k::q4k_gemm_mfma_kernel<128, 128, 2, 2>"   # jq4k_gemm's tile at M = 2048
 
 
 def decode_leg(torch, jq4k, args):
@@ -250,6 +251,25 @@ def profile_run(torch, jq4k):
     print("profile run done", flush=True)
 
 
+def measured_traffic(kernel):
+    """Mean HBM bytes (fetch + write) per dispatch of `kernel` from
+    profiles/traffic.json, or None when the file is missing or was measured on
+    other kernel sources."""
+    from profile_summary import kernel_source_hash
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    hits = [e for e in doc["kernels"].values() if e["kernel"] == kernel]
+    n = sum(e["dispatches"] for e in hits)
+    if not n:
+        return None
+    return round(sum((e["fetch_bytes"] + e["write_bytes"]) * e["dispatches"] for e in hits) / n)
+
+
 def cpu_baseline(layer, budget_s=12.0):
     import oracle
     reps, t0 = 0, time.perf_counter()
@@ -328,7 +348,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("jq4k::q4k_gemv_batched_kernel"),
             "kernel": "q4k_gemv_batched_kernel",
             "avg_launch_us": round(secs / args.steps * 1e6, 3),
             "bytes_per_launch": layer_bytes,
@@ -342,8 +363,9 @@ def main():
             "ms_per_step": round(psecs / args.prefill_steps * 1e3, 4),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "q4k_gemm_mfma_kernel"},
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic(PREFILL_KERNEL),
+                         "kernel": PREFILL_KERNEL},
             "per_projection": p_per,
         },
     }
