@@ -31,9 +31,10 @@ constexpr int kMaxDevices = 64;
 constexpr int kQuickReturn = 1;
 constexpr int kGemvMaxRows = 1024;
 constexpr int kGemvSmallRowsPerCu = 64;  // below this many rows per CU: small-matrix rule
-constexpr int kGemvBlocksPerCu = 4;
+// blocks of W per workgroup for large and for batched GEMVs (measured best
+// on the 151936 x 2560 LM head and on the seven-projection decode batch)
+constexpr int kGemvLargeBlocksPerWg = 320;
 constexpr size_t kGemvLdsLimit = 64 * 1024;
-constexpr int kBatchBlocksPerWg = 160;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -63,10 +64,10 @@ int check_matmul(const void* W, const void* X, const void* Y, int M, int N, int 
 }
 
 // Rows per workgroup of the GEMV.  Small matrices take few rows per
-// workgroup so that every compute unit has loads in flight; large ones take
-// as many rows as one resident wave of workgroups (kGemvBlocksPerCu per compute
-// unit) needs, so that no tail of half-filled workgroup waves remains and the
-// per-workgroup staging of x is paid once.  Bounded by the LDS budget.
+// workgroup so that every compute unit has loads in flight (about two
+// workgroups per compute unit); large ones take about kGemvLargeBlocksPerWg
+// blocks of W per workgroup (measured best on the 151936 x 2560 LM head).
+// Bounded by the LDS budget.
 int gemv_rows_per_block(int N, int K) {
     const int nb = K / jq4k::kQK;
     const long cus = cu_count();
@@ -74,7 +75,7 @@ int gemv_rows_per_block(int N, int K) {
     if (N <= kGemvSmallRowsPerCu * cus)
         R = (N + 2 * cus - 1) / (2 * cus);
     else
-        R = (N + kGemvBlocksPerCu * cus - 1) / (kGemvBlocksPerCu * cus);
+        R = (kGemvLargeBlocksPerWg + nb - 1) / nb;
     if (R < 1) R = 1;
     if (R > kGemvMaxRows) R = kGemvMaxRows;
     while (R > 1 && jq4k::gemv_lds_bytes(nb, static_cast<int>(R)) > kGemvLdsLimit) --R;
@@ -90,11 +91,11 @@ int run_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K, in
 }
 
 // Rows per workgroup inside a batched launch: the whole batch fills the GPU,
-// so each workgroup takes about kBatchBlocksPerWg blocks of W (2.5 rounds of
-// quarter tasks) whatever the row length.
+// so each workgroup takes about kGemvLargeBlocksPerWg blocks of W whatever
+// the row length.
 int gemv_batch_rows(int N, int K) {
     const int nb = K / jq4k::kQK;
-    int R = (kBatchBlocksPerWg + nb - 1) / nb;
+    int R = (kGemvLargeBlocksPerWg + nb - 1) / nb;
     if (R > N) R = N;
     if (R < 1) R = 1;
     while (R > 1 && jq4k::gemv_lds_bytes(nb, R) > kGemvLdsLimit) --R;

@@ -82,9 +82,9 @@ struct QuarterLoad {
 
 __device__ __forceinline__ QuarterLoad load_quarter(const uint8_t* blk, int c) {
     QuarterLoad r;
-    r.hdr = load_stream16(blk);
-    r.qa = load_stream16(blk + 16 + 32 * c);
-    r.qb = load_stream16(blk + 32 + 32 * c);
+    r.hdr = load16(blk);
+    r.qa = load16(blk + 16 + 32 * c);
+    r.qb = load16(blk + 32 + 32 * c);
     return r;
 }
 
