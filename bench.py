@@ -83,7 +83,7 @@ def timed(torch, fn, steps, warmup, use_graph):
 
 
 DEPENDENCY_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]   # q|k|v, o, gate|up, down
-PREFILL_KERNEL = "jq4k::q4k_gemm_mfma_kernel<128, 128, 2, 2>"   # jq4k_gemm's tile at M = 2048
+PREFILL_KERNEL = "jq4k::q4k_gemm_mfma_kernel<128, 128, 2, 2>"   # jq4k_gemm_batched at M = 2048
 
 
 def decode_leg(torch, jq4k, args):
@@ -178,6 +178,11 @@ def lm_head_leg(torch, jq4k, args):
 
 
 def prefill_leg(torch, jq4k, args):
+    """The seven projections of one layer at M = 2048 tokens on the MFMA path,
+    timed as batched_1 (one jq4k_gemm_batched launch; the headline prefill
+    figure), dependency_4 (q|k|v, o, gate|up, down) and separate_7 (seven
+    jq4k_gemm launches)."""
+    import ctypes
     M = 2048
     projs = [qi.prefill_projection(3, 0, p, M) for p in range(7)]
     flops = sum(2.0 * M * N * K for _, N, K, _, _ in projs)
@@ -189,31 +194,61 @@ def prefill_leg(torch, jq4k, args):
     Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda:0") for _, N, _, _, _ in projs]
     L = jq4k.raw()
 
-    def step(i):
+    def descs(c, idx):
+        arr = (jq4k.GemmDesc * len(idx))()
+        for j, p in enumerate(idx):
+            _, N, K, _, _ = projs[p]
+            arr[j] = jq4k.GemmDesc(Ws[c][p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(),
+                                   M, N, K)
+        return arr
+    all7 = [descs(c, range(7)) for c in range(copies)]
+    grouped = [[descs(c, gi) for gi in DEPENDENCY_GROUPS] for c in range(copies)]
+
+    def check(rc):
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+
+    def step_batched(i):
+        check(L.jq4k_gemm_batched(ctypes.addressof(all7[i % copies]), 7,
+                                  torch.cuda.current_stream().cuda_stream))
+
+    def step_grouped(i):
+        s = torch.cuda.current_stream().cuda_stream
+        for arr, gi in zip(grouped[i % copies], DEPENDENCY_GROUPS):
+            check(L.jq4k_gemm_batched(ctypes.addressof(arr), len(gi), s))
+
+    def step_separate(i):
         Wc = Ws[i % copies]
         s = torch.cuda.current_stream().cuda_stream
         for p, (_, N, K, _, _) in enumerate(projs):
-            rc = L.jq4k_gemm(Wc[p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(), M, N, K, s)
-            if rc:
-                raise RuntimeError(jq4k.strerror(rc))
+            check(L.jq4k_gemm(Wc[p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(), M, N, K, s))
 
-    secs = timed(torch, step, args.prefill_steps, 2, not args.eager)
+    graph = not args.eager
+    secs = timed(torch, step_batched, args.prefill_steps, 2, graph)
+    modes = {}
+    for name, fn, launches in (("batched_1", None, 1), ("dependency_4", step_grouped, 4),
+                               ("separate_7", step_separate, 7)):
+        t = secs if fn is None else timed(torch, fn, args.prefill_steps, 2, graph)
+        modes[name] = {"launches_per_step": launches,
+                       "us_per_step": round(t / args.prefill_steps * 1e6, 1),
+                       "TFLOP_s": round(flops * args.prefill_steps / t / 1e12, 1)}
     per_proj = {}
     for p, (name, N, K, _, _) in enumerate(projs):
         def one(i, p=p, N=N, K=K):
             s = torch.cuda.current_stream().cuda_stream
-            L.jq4k_gemm(Ws[i % copies][p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(),
-                        M, N, K, s)
-        t = timed(torch, one, args.prefill_steps, 1, not args.eager)
+            check(L.jq4k_gemm(Ws[i % copies][p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(),
+                              M, N, K, s))
+        t = timed(torch, one, args.prefill_steps, 1, graph)
         per_proj[name] = {"N": N, "K": K, "us": round(t / args.prefill_steps * 1e6, 2),
                           "TFLOP_s": round(2.0 * M * N * K * args.prefill_steps / t / 1e12, 1)}
-    return flops, secs, per_proj
+    return flops, secs, modes, per_proj
 
 
 def profile_run(torch, jq4k):
     """Launches for rocprofv3 runs: a 512 MiB device copy (the reference for
     scaling FETCH_SIZE / WRITE_SIZE), then 20 batched decode-layer GEMVs, 20
-    LM-head GEMVs and 3 passes of the M=2048 layer, eagerly, synchronised."""
+    LM-head GEMVs and 3 batched launches of the M=2048 layer, eagerly,
+    synchronised."""
     import ctypes
     a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
@@ -240,14 +275,18 @@ def profile_run(torch, jq4k):
         assert L.jq4k_gemv(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), 1, 151936, 2560, s) == 0
     torch.cuda.synchronize()
     M = 2048
+    keep = []
+    garr = (jq4k.GemmDesc * 7)()
     for p in range(7):
         _, N, K, W, X = qi.prefill_projection(3, 0, p, M)
         Wd = torch.from_numpy(W).to("cuda:0")
         Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
         Yd = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
-        for _ in range(3):
-            assert L.jq4k_gemm(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K, s) == 0
-        torch.cuda.synchronize()
+        keep.append((Wd, Xd, Yd))
+        garr[p] = jq4k.GemmDesc(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K)
+    for _ in range(3):
+        assert L.jq4k_gemm_batched(ctypes.addressof(garr), 7, s) == 0
+    torch.cuda.synchronize()
     print("profile run done", flush=True)
 
 
@@ -320,7 +359,7 @@ def main():
     layer, layer_bytes, copies, secs, modes, per_proj = decode_leg(torch, jq4k, args)
     gbs = layer_bytes * args.steps / secs / 1e9
     lm = lm_head_leg(torch, jq4k, args)
-    flops, psecs, p_per = prefill_leg(torch, jq4k, args)
+    flops, psecs, p_modes, p_per = prefill_leg(torch, jq4k, args)
     tflops = flops * args.prefill_steps / psecs / 1e12
 
     out = {
@@ -358,14 +397,18 @@ def main():
         "per_projection": per_proj,
         "lm_head_m1": lm,
         "prefill": {
-            "workload": "Qwen3-4B layer, 7 Q4_K projections at M=2048, seeds [3,0,p]",
+            "workload": "Qwen3-4B layer, 7 Q4_K projections at M=2048, seeds [3,0,p]; one "
+                        "jq4k_gemm_batched launch per step (the seven are independent here)",
             "value": round(tflops, 1), "unit": "TFLOP/s", "steps": args.prefill_steps,
             "ms_per_step": round(psecs / args.prefill_steps * 1e3, 4),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(PREFILL_KERNEL),
-                         "kernel": PREFILL_KERNEL},
+                         "kernel": PREFILL_KERNEL,
+                         "avg_launch_us": round(psecs / args.prefill_steps * 1e6, 2),
+                         "flops_per_launch": flops},
+            "modes": p_modes,
             "per_projection": p_per,
         },
     }

@@ -132,6 +132,32 @@ int jq4k_gemv_batched(const jq4k_gemv_desc *problems, int count, hipStream_t str
 int jq4k_gemm(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
               int M, int N, int K, hipStream_t stream);
 
+/* One problem of a batched matmul: Y (M x N) = X (M x K) . W^T. */
+typedef struct {
+    const block_q4_K *W;  /* N*(K/256) blocks, 16-byte aligned */
+    const jq4k_bf16 *X;   /* M x K bf16, 16-byte aligned       */
+    float *Y;             /* M x N floats, 4-byte aligned      */
+    int M;
+    int N;
+    int K;                /* positive multiple of 256          */
+} jq4k_gemm_desc;
+
+#define JQ4K_GEMM_BATCH_MAX 16
+
+/* Up to JQ4K_GEMM_BATCH_MAX independent matmuls in one launch on the MFMA
+ * path (the genie-ai-runtime README, "At a glance": tensor-core MMQ Q4_K
+ * prefill; one launch for projections that do not depend on each other, such
+ * as q, k and v, or gate and up, so that their tiles fill the GPU together).
+ * The tile (64 or 128 rows of M) is the one jq4k_gemm picks for the largest
+ * M of the batch; every problem meets the same bound as jq4k_gemm.  Problems
+ * with M == 0 or N == 0 are skipped.  `problems` is a host array read before
+ * the call returns (passed to the kernel by value; nothing is allocated).
+ * Outputs must not overlap any input.  Errors: JQ4K_EINVAL for count < 0,
+ * count > JQ4K_GEMM_BATCH_MAX, a null `problems` with count > 0, or any
+ * problem that jq4k_gemm rejects (JQ4K_EALIGN likewise); nothing is launched
+ * then. */
+int jq4k_gemm_batched(const jq4k_gemm_desc *problems, int count, hipStream_t stream);
+
 /* Kernel paths for jq4k_gemm_path (tests and benchmarks reach every path). */
 #define JQ4K_PATH_AUTO 0 /* what jq4k_gemm picks                        */
 #define JQ4K_PATH_GEMV 1 /* the M = 1 kernel (M must be 1)               */

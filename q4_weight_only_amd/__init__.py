@@ -34,6 +34,15 @@ class GemvDesc(ctypes.Structure):
 GEMV_BATCH_MAX = 16
 
 
+class GemmDesc(ctypes.Structure):
+    """jq4k_gemm_desc: one problem of jq4k_gemm_batched."""
+    _fields_ = [("W", ctypes.c_void_p), ("X", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("M", ctypes.c_int), ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
+GEMM_BATCH_MAX = 16
+
+
 class Jq4kError(RuntimeError):
     def __init__(self, code, where):
         self.code = code
@@ -60,6 +69,8 @@ def _load():
         L.jq4k_gemv_rows.restype = i
         L.jq4k_gemv_batched.argtypes = [vp, i, vp]
         L.jq4k_gemv_batched.restype = i
+        L.jq4k_gemm_batched.argtypes = [vp, i, vp]
+        L.jq4k_gemm_batched.restype = i
         L.jq4k_gemm_path.argtypes = [vp, vp, vp, i, i, i, i, vp]
         L.jq4k_gemm_path.restype = i
         L.jq4k_unpack_fields.argtypes = [vp, l, vp, vp, vp, vp]
@@ -151,6 +162,22 @@ def gemv_batched(problems, stream=None):
     arr = gemv_descs(problems)
     _check(_load().jq4k_gemv_batched(ctypes.addressof(arr), len(problems), _stream(stream)),
            "jq4k_gemv_batched")
+
+
+def gemm_descs(problems):
+    """ctypes array of GemmDesc from (W, X, Y) torch tensor triples."""
+    arr = (GemmDesc * max(len(problems), 1))()
+    for i, (W, X, Y) in enumerate(problems):
+        M, N, K = _shapes(W, X, Y)
+        arr[i] = GemmDesc(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K)
+    return arr
+
+
+def gemm_batched(problems, stream=None):
+    """One MFMA launch for several independent matmuls: [(W, X, Y), ...]."""
+    arr = gemm_descs(problems)
+    _check(_load().jq4k_gemm_batched(ctypes.addressof(arr), len(problems), _stream(stream)),
+           "jq4k_gemm_batched")
 
 
 def gemm(W, X, Y, stream=None, path=PATH_AUTO):

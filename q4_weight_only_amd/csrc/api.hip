@@ -6,6 +6,7 @@
 
 #include "jq4k.h"
 #include "q4k_device.h"
+#include "tile_sched.h"
 
 namespace jq4k {
 hipError_t launch_gemv(const uint8_t* W, const uint16_t* X, float* Y, int N, int K, int R,
@@ -14,16 +15,20 @@ size_t gemv_lds_bytes(int nb, int R);
 hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X,
                                float* const* Y, const int* N, const int* K, const int* R,
                                int count, hipStream_t stream);
-hipError_t launch_gemm_mfma(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
-                            int tile, hipStream_t stream);
-long gemm_tile_count(int M, int N, int tile);
+hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
+                            const int* M, const int* N, const int* K, int count, int tile,
+                            hipStream_t stream);
+long gemm_launch_size(const int* M, const int* N, int count, int tile);
 hipError_t launch_gemm_ws(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
                           hipStream_t stream);
+long gemm_ws_launch_size(int M, int N);
 hipError_t launch_unpack_fields(const uint8_t* W, long nblocks, uint8_t* q, uint8_t* sc,
                                 uint8_t* m, hipStream_t stream);
 hipError_t launch_dequant_f32(const uint8_t* W, long nblocks, float* w, hipStream_t stream);
 hipError_t launch_dequant_bf16(const uint8_t* W, long nblocks, uint16_t* w, hipStream_t stream);
 }  // namespace jq4k
+
+static_assert(JQ4K_GEMM_BATCH_MAX <= jq4k::kSchedMax, "one launch per grouped matmul");
 
 namespace {
 
@@ -112,10 +117,13 @@ int mfma_tile_for(int M, int N) {
 
 int run_mfma(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K, int tile,
              hipStream_t stream) {
-    if (jq4k::gemm_tile_count(M, N, tile) > 0x7FFFFFFFL - 8) return JQ4K_EINVAL;
+    const long wgs = tile == 256 ? jq4k::gemm_ws_launch_size(M, N)
+                                 : jq4k::gemm_launch_size(&M, &N, 1, tile);
+    if (wgs > 0x7FFFFFFFL) return JQ4K_EINVAL;
     const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
-    const hipError_t e = tile == 256 ? jq4k::launch_gemm_ws(w, X, Y, M, N, K, stream)
-                                     : jq4k::launch_gemm_mfma(w, X, Y, M, N, K, tile, stream);
+    const hipError_t e = tile == 256
+                             ? jq4k::launch_gemm_ws(w, X, Y, M, N, K, stream)
+                             : jq4k::launch_gemm_mfma(&w, &X, &Y, &M, &N, &K, 1, tile, stream);
     return static_cast<int>(e);
 }
 
@@ -179,6 +187,35 @@ int jq4k_gemv_batched(const jq4k_gemv_desc* problems, int count, hipStream_t str
     if (live == 0) return JQ4K_OK;
     if (wgs > 0x7FFFFFFFL) return JQ4K_EINVAL;
     return static_cast<int>(jq4k::launch_gemv_batched(W, X, Y, N, K, R, live, stream));
+}
+
+int jq4k_gemm_batched(const jq4k_gemm_desc* problems, int count, hipStream_t stream) {
+    if (count < 0 || count > JQ4K_GEMM_BATCH_MAX) return JQ4K_EINVAL;
+    if (count == 0) return JQ4K_OK;
+    if (problems == nullptr) return JQ4K_EINVAL;
+    const uint8_t* W[JQ4K_GEMM_BATCH_MAX];
+    const uint16_t* X[JQ4K_GEMM_BATCH_MAX];
+    float* Y[JQ4K_GEMM_BATCH_MAX];
+    int M[JQ4K_GEMM_BATCH_MAX], N[JQ4K_GEMM_BATCH_MAX], K[JQ4K_GEMM_BATCH_MAX];
+    int live = 0, max_m = 0;
+    for (int i = 0; i < count; ++i) {
+        const jq4k_gemm_desc& d = problems[i];
+        const int rc = check_matmul(d.W, d.X, d.Y, d.M, d.N, d.K);
+        if (rc == kQuickReturn) continue;
+        if (rc != 0) return rc;
+        W[live] = reinterpret_cast<const uint8_t*>(d.W);
+        X[live] = d.X;
+        Y[live] = d.Y;
+        M[live] = d.M;
+        N[live] = d.N;
+        K[live] = d.K;
+        max_m = d.M > max_m ? d.M : max_m;
+        ++live;
+    }
+    if (live == 0) return JQ4K_OK;
+    const int tile = mfma_tile_for(max_m, 0);
+    if (jq4k::gemm_launch_size(M, N, live, tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
+    return static_cast<int>(jq4k::launch_gemm_mfma(W, X, Y, M, N, K, live, tile, stream));
 }
 
 int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,

@@ -21,13 +21,13 @@
 // 16 accumulators of lane l hold column l % 32, rows 8 (r / 4) + 4 (l / 32)
 // + r % 4 for r = 0..15.
 #include "q4k_device.h"
+#include "tile_sched.h"
 
 namespace jq4k {
 
 constexpr int kGemmThreads = 256;
 constexpr int kBK = 64;               // K per stage: one quarter block
 constexpr int kRowChunks = kBK / 8;   // 16-byte chunks per LDS row
-constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
 
 // Chunk c of tile row r sits at chunk c ^ f(r), f(r) = (r >> 1) ^ 4 (r & 1).
 // An MFMA operand read has 16 lanes on 16 consecutive rows and one chunk;
@@ -52,24 +52,17 @@ struct GemmCfg {
     static constexpr int kLdsChunks = (BM + BN) * kRowChunks;         // per buffer
 };
 
+// One BM x BN tile of Y = X . W^T, rows m0.. and columns n0.. (the whole
+// K loop and the epilogue), computed by the 256 threads of a workgroup.
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(
-    const uint8_t* __restrict__ W, const uint16_t* __restrict__ X, float* __restrict__ Y,
-    int M, int N, int K, int ntiles, int per_xcd, uint32_t qmask) {
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
+                                          const uint16_t* __restrict__ X, float* __restrict__ Y,
+                                          int M, int N, int K, int n0, int m0, uint32_t qmask,
+                                          uint4 (*lds)[GemmCfg<BM, BN, WM, WN>::kLdsChunks]) {
     using C = GemmCfg<BM, BN, WM, WN>;
-    __shared__ uint4 lds[2][C::kLdsChunks];
-
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    // XCD-aware tile order: workgroup i runs on XCD i % 8; XCD x takes the
-    // contiguous tile range [x * per_xcd, (x + 1) * per_xcd) of the n-fastest
-    // tile order, so the workgroups resident on one XCD share rows of X (and
-    // its L2) while they sweep the columns of W.
-    const int ntile_n = (N + BN - 1) / BN;
-    const int lin = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (lin >= ntiles) return;
-    const int n0 = (lin % ntile_n) * BN, m0 = (lin / ntile_n) * BM;
     const int nb = K / kQK;
     const int nstage = K / kBK;
 
@@ -221,28 +214,78 @@ __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(
     }
 }
 
+// One launch computes the tiles of up to kSchedMax independent problems
+// (a single matmul is a batch of one); the descriptors and the tile schedule
+// travel in the kernel arguments.
+struct GemmProblem {
+    const uint8_t* W;
+    const uint16_t* X;
+    float* Y;
+    int M, N, K;
+};
+
+struct GemmBatch {
+    GemmProblem p[kSchedMax];
+    TileSched s;
+};
+
 template <int BM, int BN, int WM, int WN>
-static hipError_t launch_cfg(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
+__global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(const GemmBatch batch,
+                                                                     uint32_t qmask) {
+    using C = GemmCfg<BM, BN, WM, WN>;
+    __shared__ uint4 lds[2][C::kLdsChunks];
+    int q, tm, tn;
+    if (!tile_sched_next(batch.s, blockIdx.x, &q, &tm, &tn)) return;
+    const GemmProblem& pr = batch.p[q];
+    gemm_tile<BM, BN, WM, WN>(pr.W, pr.X, pr.Y, pr.M, pr.N, pr.K, tn * BN, tm * BM, qmask, lds);
+}
+
+// Band height of the grouped tile order: 256 rows of X (measured best of
+// 128..2048 on the seven projections of a layer at M = 512 and M = 2048).
+constexpr int group_rows(int BM) { return BM >= 256 ? 1 : 256 / BM; }
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_cfg(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
+                             const int* M, const int* N, const int* K, int count,
                              hipStream_t stream) {
-    const long ntiles = static_cast<long>((N + BN - 1) / BN) * ((M + BM - 1) / BM);
-    const long per_xcd = (ntiles + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((q4k_gemm_mfma_kernel<BM, BN, WM, WN>), dim3(per_xcd * kXcds),
-                       dim3(kGemmThreads), 0, stream, W, X, Y, M, N, K,
-                       static_cast<int>(ntiles), static_cast<int>(per_xcd), kNibbleMask);
+    // queue order: longest K first (stable), so the longest tiles start first
+    int order[kSchedMax];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    for (int i = 1; i < count; ++i)
+        for (int j = i; j > 0 && K[order[j]] > K[order[j - 1]]; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    GemmBatch b = {};
+    int Ms[kSchedMax], Ns[kSchedMax];
+    for (int i = 0; i < count; ++i) {
+        const int o = order[i];
+        b.p[i] = {W[o], X[o], Y[o], M[o], N[o], K[o]};
+        Ms[i] = M[o];
+        Ns[i] = N[o];
+    }
+    const long grid = tile_sched_init(b.s, Ms, Ns, count, BM, BN, group_rows(BM));
+    hipLaunchKernelGGL((q4k_gemm_mfma_kernel<BM, BN, WM, WN>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kGemmThreads), 0, stream, b, kNibbleMask);
     return hipGetLastError();
 }
 
-long gemm_tile_count(int M, int N, int tile) {
+// Workgroups a launch of these problems takes (tiles plus at most seven idle
+// workgroups per problem).
+long gemm_launch_size(const int* M, const int* N, int count, int tile) {
     const int bn = tile == 64 ? 256 : 128;
-    return static_cast<long>((N + bn - 1) / bn) * ((M + tile - 1) / tile);
+    TileSched s;
+    return tile_sched_init(s, M, N, count, tile, bn, 1);
 }
 
-// tile: 64 or 128 rows of M per workgroup (the 256-row tile is the
-// wave-specialised kernel of gemm_ws.hip).
-hipError_t launch_gemm_mfma(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
-                            int tile, hipStream_t stream) {
-    if (tile == 64) return launch_cfg<64, 256, 1, 4>(W, X, Y, M, N, K, stream);
-    return launch_cfg<128, 128, 2, 2>(W, X, Y, M, N, K, stream);
+// tile: 64 or 128 rows of M per workgroup, for the whole batch (the 256-row
+// tile is the wave-specialised kernel of gemm_ws.hip).
+hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
+                            const int* M, const int* N, const int* K, int count, int tile,
+                            hipStream_t stream) {
+    if (tile == 64) return launch_cfg<64, 256, 1, 4>(W, X, Y, M, N, K, count, stream);
+    return launch_cfg<128, 128, 2, 2>(W, X, Y, M, N, K, count, stream);
 }
 
 }  // namespace jq4k

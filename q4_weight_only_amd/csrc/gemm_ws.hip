@@ -17,6 +17,7 @@
 // per stage hands a filled buffer from producers to consumers.  Producers keep
 // two register sets, so global data has two stages of time to arrive.
 #include "q4k_device.h"
+#include "tile_sched.h"
 
 namespace jq4k {
 
@@ -25,7 +26,6 @@ namespace {
 constexpr int kWsThreads = 512;
 constexpr int kWsBM = 256, kWsBN = 128, kWsBK = 64;
 constexpr int kWsRowChunks = kWsBK / 8;
-constexpr int kWsXcds = 8;
 constexpr int kWsLdsChunks = (kWsBM + kWsBN) * kWsRowChunks;   // per buffer
 constexpr int kWsXChunks = kWsBM * kWsRowChunks / 256;          // per producer thread
 constexpr int kWsTM = 4, kWsTN = 2;                             // 32x32 tiles per consumer
@@ -45,16 +45,15 @@ struct WsRegs {
 
 __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ X, float* __restrict__ Y,
-    int M, int N, int K, int ntiles, int per_xcd, uint32_t qmask) {
+    int M, int N, int K, const TileSched sched, uint32_t qmask) {
     __shared__ uint4 lds[2][kWsLdsChunks];
 
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
 
-    const int ntile_n = (N + kWsBN - 1) / kWsBN;
-    const int lin = (blockIdx.x % kWsXcds) * per_xcd + blockIdx.x / kWsXcds;
-    if (lin >= ntiles) return;
-    const int n0 = (lin % ntile_n) * kWsBN, m0 = (lin / ntile_n) * kWsBM;
+    int q, tm, tn;
+    if (!tile_sched_next(sched, blockIdx.x, &q, &tm, &tn)) return;
+    const int n0 = tn * kWsBN, m0 = tm * kWsBM;
     const int nb = K / kQK;
     const int nstage = K / kWsBK;  // a multiple of 4
     auto last = [&](int s) { return min(s, nstage - 1); };
@@ -182,17 +181,17 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(
     }
 }
 
-long gemm_ws_tile_count(int M, int N) {
-    return static_cast<long>((N + kWsBN - 1) / kWsBN) * ((M + kWsBM - 1) / kWsBM);
+long gemm_ws_launch_size(int M, int N) {
+    TileSched s;
+    return tile_sched_init(s, &M, &N, 1, kWsBM, kWsBN, 1);
 }
 
 hipError_t launch_gemm_ws(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
                           hipStream_t stream) {
-    const long ntiles = gemm_ws_tile_count(M, N);
-    const long per_xcd = (ntiles + kWsXcds - 1) / kWsXcds;
-    hipLaunchKernelGGL(q4k_gemm_ws_kernel, dim3(per_xcd * kWsXcds), dim3(kWsThreads), 0, stream,
-                       W, X, Y, M, N, K, static_cast<int>(ntiles), static_cast<int>(per_xcd),
-                       kNibbleMask);
+    TileSched s;
+    const long grid = tile_sched_init(s, &M, &N, 1, kWsBM, kWsBN, 2);
+    hipLaunchKernelGGL(q4k_gemm_ws_kernel, dim3(static_cast<unsigned>(grid)), dim3(kWsThreads),
+                       0, stream, W, X, Y, M, N, K, s, kNibbleMask);
     return hipGetLastError();
 }
 

@@ -154,3 +154,26 @@ def test_gemv_batched_argument_checks(L):
         assert f(ctypes.addressof(arr), 2, None) == code, bad
     empty = _descs((0, 0, 0, 0, 256), (0, 0, 0, 0, 512))
     assert f(ctypes.addressof(empty), 2, None) == jq4k.OK
+
+
+def test_gemm_batched_argument_checks(L):
+    f = L.jq4k_gemm_batched
+
+    def descs(*rows):
+        arr = (jq4k.GemmDesc * max(len(rows), 1))()
+        for i, r in enumerate(rows):
+            arr[i] = jq4k.GemmDesc(*r)
+        return arr
+    good = (ALIGNED, ALIGNED2, ALIGNED3, 4, 8, 256)
+    assert f(None, 0, None) == jq4k.OK
+    assert f(None, 1, None) == jq4k.EINVAL
+    assert f(ctypes.addressof(descs(good)), -1, None) == jq4k.EINVAL
+    many = descs(*([good] * 17))
+    assert f(ctypes.addressof(many), 17, None) == jq4k.EINVAL
+    for bad, code in (((ALIGNED, ALIGNED2, ALIGNED3, 4, 8, 300), jq4k.EINVAL),
+                      ((ALIGNED, ALIGNED2, ALIGNED3, -1, 8, 256), jq4k.EINVAL),
+                      ((ALIGNED, 0, ALIGNED3, 4, 8, 256), jq4k.EINVAL),
+                      ((ALIGNED, ALIGNED2 + 4, ALIGNED3, 4, 8, 256), jq4k.EALIGN)):
+        assert f(ctypes.addressof(descs(good, bad)), 2, None) == code, bad
+    empty = descs((0, 0, 0, 0, 8, 256), (0, 0, 0, 5, 0, 512))
+    assert f(ctypes.addressof(empty), 2, None) == jq4k.OK

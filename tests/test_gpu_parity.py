@@ -230,6 +230,32 @@ def test_gemm_auto_and_determinism(gpu, M):
     parity(y1, Y, A, f"auto M={M}")
 
 
+def test_gemm_batched_mixed_problems(gpu):
+    """One MFMA launch for independent problems of different shapes: each
+    output meets the bound and equals the single-problem result on the same
+    tile bit for bit."""
+    g = np.random.default_rng(110)
+    shapes = [(300, 130, 512), (77, 384, 768), (129, 65, 256), (0, 64, 256), (256, 1000, 2560)]
+    probs = []
+    for M, N, K in shapes:
+        probs.append((M, N, K, qi.weight_bytes(g, N, K), qi.activations(g, M, K)))
+    Wd = [dev(W) for *_, W, _ in probs]
+    Xd = [dev(X).view(torch.bfloat16) for *_, X in probs]
+    Yb = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+          for M, N, *_ in probs]
+    announce(f"gemm batched {len(probs)} problems")
+    gpu.gemm_batched(list(zip(Wd, Xd, Yb)))
+    for (M, N, K, W, X), wd, xd, yb in zip(probs, Wd, Xd, Yb):
+        if M == 0:
+            continue
+        ys = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        gpu.gemm(wd, xd, ys, path=gpu.PATH_MFMA_T128)
+        got = host(yb)
+        assert np.array_equal(got.view(np.uint32), host(ys).view(np.uint32)), (M, N, K)
+        Y, A = oracle.gemm(W, X, N, K)
+        parity(got, Y, A, f"gemm batched M={M} N={N} K={K}")
+
+
 def test_prefill_m33_one_layer(gpu):
     for p in range(7):
         name, N, K, W, X = qi.prefill_projection(2, 0, p, 33)
