@@ -36,9 +36,11 @@ constexpr int kMaxDevices = 64;
 constexpr int kQuickReturn = 1;
 constexpr int kGemvMaxRows = 1024;
 constexpr int kGemvSmallRowsPerCu = 64;  // below this many rows per CU: small-matrix rule
-// blocks of W per workgroup for large and for batched GEMVs (measured best
-// on the 151936 x 2560 LM head and on the seven-projection decode batch)
+// blocks of W per workgroup for large single GEMVs (measured best on the
+// 151936 x 2560 LM head) and inside batched launches (measured best on the
+// seven projections of a decode layer: 990 workgroups, all resident at once)
 constexpr int kGemvLargeBlocksPerWg = 320;
+constexpr int kGemvBatchBlocksPerWg = 400;
 constexpr size_t kGemvLdsLimit = 64 * 1024;
 
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -96,11 +98,11 @@ int run_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K, in
 }
 
 // Rows per workgroup inside a batched launch: the whole batch fills the GPU,
-// so each workgroup takes about kGemvLargeBlocksPerWg blocks of W whatever
+// so each workgroup takes about kGemvBatchBlocksPerWg blocks of W whatever
 // the row length.
 int gemv_batch_rows(int N, int K) {
     const int nb = K / jq4k::kQK;
-    int R = (kGemvLargeBlocksPerWg + nb - 1) / nb;
+    int R = (kGemvBatchBlocksPerWg + nb - 1) / nb;
     if (R > N) R = N;
     if (R < 1) R = 1;
     while (R > 1 && jq4k::gemv_lds_bytes(nb, R) > kGemvLdsLimit) --R;

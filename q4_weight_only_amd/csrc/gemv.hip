@@ -27,8 +27,9 @@
 // its nb block values in order (deterministic, no atomics).
 //
 // LDS layout of x.  x is stored as 16-byte chunks, chunk g = 32 kb + 8 c + i
-// (i = 0..3 the even sub-block, 4..7 the odd one), with i XOR-swizzled by
-// block and quarter (x_chunk_phys) so the reads are free of bank conflicts.
+// (i = 0..3 the even sub-block, 4..7 the odd one), in groups of 8 per
+// (block, quarter) at a stride of 9 chunks (x_group_base), which keeps the
+// reads free of bank conflicts and costs no address arithmetic per chunk.
 #include "q4k_device.h"
 
 namespace jq4k {
@@ -38,14 +39,16 @@ constexpr int kGemvBatchMax = 16;  // problems per batched launch
 
 size_t gemv_lds_bytes(int nb, int R);
 
-// A 16-lane group of a round reads one chunk index i for 4 consecutive
-// blocks x 4 quarters; XOR-ing i by g(kb, c) gives those 16 lanes 16
-// different 16-byte slots in each 256-byte window (and each 8-lane half 8
-// different slots in a 128-byte window): no bank conflicts.
-__device__ __forceinline__ int x_chunk_phys(int kb, int c, int i) {
-    const int g = ((c >> 1) | ((kb & 3) << 1)) ^ ((c & 1) << 2);
-    return (kb << 5) | (c << 3) | (i ^ (g & 7));
-}
+// x in LDS: the 8 chunks of (block kb, quarter c) -- chunk g = 32 kb + 8 c
+// + i of x, i = 0..3 the even sub-block, 4..7 the odd one -- sit at 9 (4 kb
+// + c) + i.  The stride of 9 chunks spreads the groups over the banks: the
+// 64 lanes of a round read one chunk index i of 64 consecutive groups, and
+// 9 m mod 16 takes every 16-byte slot exactly four times, the conflict-free
+// case of ds_read_b128.  A thread's 8 reads are one base address plus
+// immediate offsets.
+constexpr int kXGroupStride = 9;
+__device__ __forceinline__ int x_group_base(int kb, int c) { return (4 * kb + c) * kXGroupStride; }
+__device__ __forceinline__ int x_chunk_phys(int g) { return (g >> 3) * kXGroupStride + (g & 7); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
@@ -100,10 +103,11 @@ __device__ __forceinline__ float quarter_dot(const QuarterLoad& ld, int c, const
     float acc1 = -128.f * xsum.y;  // -128 X_(2c+1)
     const uint32_t qw[8] = {ld.qa.x, ld.qa.y, ld.qa.z, ld.qa.w,
                             ld.qb.x, ld.qb.y, ld.qb.z, ld.qb.w};
+    const uint4* xg = xs + x_group_base(kb, c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint4 xl = xs[x_chunk_phys(kb, c, i)];
-        const uint4 xh = xs[x_chunk_phys(kb, c, 4 + i)];
+        const uint4 xl = xg[i];
+        const uint4 xh = xg[4 + i];
         const uint32_t v0 = qw[2 * i], v1 = qw[2 * i + 1];
         acc0 = quant_dot8(low_quants(v0), xl.x, xl.y, acc0);
         acc0 = quant_dot8(low_quants(v1), xl.z, xl.w, acc0);
@@ -117,7 +121,7 @@ __device__ __forceinline__ float quarter_dot(const QuarterLoad& ld, int c, const
     return d * qx - dmin * mx;
 }
 
-// LDS: x chunks (nb*32 x 16 B), per-sub-block sums X_s (nb*8 floats, as a
+// LDS: x chunks (nb*36 x 16 B), per-sub-block sums X_s (nb*8 floats, as a
 // float2 (even, odd) per (kb, quarter)), per-block partials (R*nb floats).
 constexpr int kGemvDepth = 4;  // quarter tasks in flight per thread
 constexpr int kGemvMaxK = 16384;
@@ -128,7 +132,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
                                           const uint4* __restrict__ X, float* __restrict__ Y,
                                           int N, int nb, int R, long tile, uint4* smem) {
     uint4* xs = smem;
-    float2* xsum = reinterpret_cast<float2*>(xs + nb * 32);
+    float2* xsum = reinterpret_cast<float2*>(xs + nb * 4 * kXGroupStride);
     float* part = reinterpret_cast<float*>(xsum + nb * 4);
 
     const int t = threadIdx.x;
@@ -161,9 +165,8 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     for (int j = 0; j < kGemvMaxXChunksPerThread; ++j) {
         const int g = t + j * kGemvThreads;
         if (g < nxc) {
-            const int kb = g >> 5, cc = (g >> 3) & 3, i = g & 7;
             const uint4 v = xv[j];
-            xs[x_chunk_phys(kb, cc, i)] = v;
+            xs[x_chunk_phys(g)] = v;
             float sum = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
                         ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
             sum = quad_sum(sum);
@@ -251,7 +254,7 @@ hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X
 }
 
 size_t gemv_lds_bytes(int nb, int R) {
-    return static_cast<size_t>(nb) * 32 * 16 + static_cast<size_t>(nb) * 4 * 8 +
+    return static_cast<size_t>(nb) * 4 * kXGroupStride * 16 + static_cast<size_t>(nb) * 4 * 8 +
            static_cast<size_t>(R) * nb * 4;
 }
 
