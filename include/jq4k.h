@@ -84,6 +84,10 @@ typedef uint16_t jq4k_bf16; /* bfloat16 bit pattern */
 /* Largest K the M = 1 kernel accepts (it keeps x in LDS). */
 #define JQ4K_GEMV_MAX_K 16384
 
+/* Largest K the matrix-core kernels accept (a tile of X rows is addressed
+ * with 32-bit byte offsets). */
+#define JQ4K_MFMA_MAX_K 4194304
+
 /* Decode GEMV, M must be 1: Y[0..N) = sum_k w[n][k] * X[k].
  * The genie-ai-runtime README, "At a glance": INT4 dequant-fused GEMV.
  * W: N*(K/256) blocks, 16-byte aligned.  X: K bf16, 16-byte aligned.
@@ -127,8 +131,9 @@ int jq4k_gemv_batched(const jq4k_gemv_desc *problems, int count, hipStream_t str
 /* Matmul for any M >= 0: Y (M x N) = X (M x K) . W^T.
  * The genie-ai-runtime README, "At a glance": tensor-core MMQ Q4_K prefill.
  * M == 1 runs the decode GEMV when K <= JQ4K_GEMV_MAX_K; larger M runs the
- * dequantise-to-LDS bf16 MFMA kernels.  M == 0 or N == 0 returns 0 without
- * launching.  Same pointer, alignment and K rules as jq4k_gemv. */
+ * dequantise-to-LDS bf16 MFMA kernels (K <= JQ4K_MFMA_MAX_K, else
+ * JQ4K_EINVAL).  M == 0 or N == 0 returns 0 without launching.  Same
+ * pointer and alignment rules as jq4k_gemv. */
 int jq4k_gemm(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
               int M, int N, int K, hipStream_t stream);
 
@@ -149,7 +154,7 @@ typedef struct {
  * prefill; one launch for projections that do not depend on each other, such
  * as q, k and v, or gate and up, so that their tiles fill the GPU together).
  * The tile (64 or 128 rows of M) is the one jq4k_gemm picks for the largest
- * M of the batch; every problem meets the same bound as jq4k_gemm.  Problems
+ * M of the batch; every problem meets the same bounds as jq4k_gemm.  Problems
  * with M == 0 or N == 0 are skipped.  `problems` is a host array read before
  * the call returns (passed to the kernel by value; nothing is allocated).
  * Outputs must not overlap any input.  Errors: JQ4K_EINVAL for count < 0,

@@ -21,6 +21,7 @@ HEADER = os.path.join(HERE, "..", "include", "jq4k.h")
 OK, EINVAL, EALIGN = 0, -1, -2
 PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_T64, PATH_MFMA_T128, PATH_MFMA_T256 = range(6)
 GEMV_MAX_K = 16384
+MFMA_MAX_K = 4194304
 BLOCK_BYTES = 144
 QK = 256
 

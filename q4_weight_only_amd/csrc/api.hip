@@ -119,6 +119,7 @@ int mfma_tile_for(int M, int N) {
 
 int run_mfma(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K, int tile,
              hipStream_t stream) {
+    if (K > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
     const long wgs = tile == 256 ? jq4k::gemm_ws_launch_size(M, N)
                                  : jq4k::gemm_launch_size(&M, &N, 1, tile);
     if (wgs > 0x7FFFFFFFL) return JQ4K_EINVAL;
@@ -215,6 +216,8 @@ int jq4k_gemm_batched(const jq4k_gemm_desc* problems, int count, hipStream_t str
         ++live;
     }
     if (live == 0) return JQ4K_OK;
+    for (int i = 0; i < live; ++i)
+        if (K[i] > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
     const int tile = mfma_tile_for(max_m, 0);
     if (jq4k::gemm_launch_size(M, N, live, tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
     return static_cast<int>(jq4k::launch_gemm_mfma(W, X, Y, M, N, K, live, tile, stream));

@@ -28,6 +28,9 @@ namespace jq4k {
 constexpr int kGemmThreads = 256;
 constexpr int kBK = 64;               // K per stage: one quarter block
 constexpr int kRowChunks = kBK / 8;   // 16-byte chunks per LDS row
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
+// no swizzle): byte-addressed loads with a range check against num_records.
+constexpr int kBufferConfig = 0x00020000;
 
 // Chunk c of tile row r sits at chunk c ^ f(r), f(r) = (r >> 1) ^ 4 (r & 1).
 // An MFMA operand read has 16 lanes on 16 consecutive rows and one chunk;
@@ -73,8 +76,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
     // are never stored
     const uint8_t* wrow = W + static_cast<long>(min(n0 + wr, N - 1)) * nb * kBlockBytes;
 
-    // ---- X slab assignment: chunk g = t + 256 j -> row g / 8, chunk g % 8
-    const uint16_t* xbase = X;
+    // ---- X slab assignment: chunk g = t + 256 j -> row g / 8, chunk g % 8.
+    // X is read through a buffer resource over rows m0 .. m0 + BM - 1 (only
+    // those below M): the hardware returns zeros past the end, and buffer
+    // loads are kept in registers until their LDS store instead of being
+    // re-issued there by the compiler.
+    const long xrows = min(static_cast<long>(BM), static_cast<long>(M - m0));
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(X + static_cast<long>(m0) * K), 0,
+        static_cast<int>(xrows * K * 2), kBufferConfig);
 
     // Global data of one stage, held in registers until it is stored to LDS.
     struct StageRegs {
@@ -90,11 +100,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
         for (int j = 0; j < C::kXChunks; ++j) {
             const int g = t + j * kGemmThreads;
             const int row = g >> 3, ch = g & 7;
-            // rows past M are clamped to row M-1: they only feed output rows
-            // that are never stored
-            const int m = min(m0 + row, M - 1);
-            r.x[j] = *reinterpret_cast<const uint4*>(xbase + static_cast<long>(m) * K +
-                                                     s * kBK + ch * 8);
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+                xres, (row * K + s * kBK + ch * 8) * 2, 0, 0);
+            r.x[j] = make_uint4(v.x, v.y, v.z, v.w);
         }
         const uint8_t* blk = wrow + kb * kBlockBytes;
         r.hdr = *reinterpret_cast<const uint4*>(blk);

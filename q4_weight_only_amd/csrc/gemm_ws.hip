@@ -29,6 +29,7 @@ constexpr int kWsRowChunks = kWsBK / 8;
 constexpr int kWsLdsChunks = (kWsBM + kWsBN) * kWsRowChunks;   // per buffer
 constexpr int kWsXChunks = kWsBM * kWsRowChunks / 256;          // per producer thread
 constexpr int kWsTM = 4, kWsTN = 2;                             // 32x32 tiles per consumer
+constexpr int kWsBufferConfig = 0x00020000;   // raw buffer resource word 3 (gfx9 family)
 
 // Same swizzle as the single-role kernel: chunk c of row r at c ^ f(r).
 __device__ __forceinline__ int ws_chunk(int row, int chunk) {
@@ -67,12 +68,18 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(
         // Rows past N (or M) are clamped to the last row: they only feed
         // outputs that are never stored.
         const uint8_t* wrow = W + static_cast<long>(min(n0 + wr, N - 1)) * nb * kBlockBytes;
-        const uint16_t* xrow[kWsXChunks];
+        // X through a buffer resource over rows m0 .. m0 + BM - 1 below M
+        // (zeros past the end; the loads stay in registers until stored)
+        const long xrows = min(static_cast<long>(kWsBM), static_cast<long>(M - m0));
+        const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(X + static_cast<long>(m0) * K), 0,
+            static_cast<int>(xrows * K * 2), kWsBufferConfig);
+        int xoff[kWsXChunks];
         int xlds[kWsXChunks];
 #pragma unroll
         for (int j = 0; j < kWsXChunks; ++j) {
             const int g = pt + j * 256;
-            xrow[j] = X + static_cast<long>(min(m0 + (g >> 3), M - 1)) * K + (g & 7) * 8;
+            xoff[j] = ((g >> 3) * K + (g & 7) * 8) * 2;
             xlds[j] = ws_chunk(g >> 3, g & 7);
         }
         const int wlds_lo0 = kWsBM * kWsRowChunks + ws_chunk(wr, (qoff >> 3));
@@ -82,8 +89,11 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(
         WsRegs rs[2];
         auto load_stage = [&](int s, WsRegs& r) {
 #pragma unroll
-            for (int j = 0; j < kWsXChunks; ++j)
-                r.x[j] = *reinterpret_cast<const uint4*>(xrow[j] + s * kWsBK);
+            for (int j = 0; j < kWsXChunks; ++j) {
+                const u32x4_t v =
+                    __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[j] + s * kWsBK * 2, 0, 0);
+                r.x[j] = make_uint4(v.x, v.y, v.z, v.w);
+            }
             const uint8_t* blk = wrow + (s >> 2) * kBlockBytes;
             r.hdr = *reinterpret_cast<const uint4*>(blk);
             r.q = *reinterpret_cast<const uint4*>(blk + 16 + 32 * (s & 3) + qoff);

@@ -156,6 +156,13 @@ def test_gemv_batched_argument_checks(L):
     assert f(ctypes.addressof(empty), 2, None) == jq4k.OK
 
 
+def test_mfma_k_limit(L):
+    for path in (jq4k.PATH_AUTO, jq4k.PATH_MFMA, jq4k.PATH_MFMA_T64, jq4k.PATH_MFMA_T128,
+                 jq4k.PATH_MFMA_T256):
+        assert L.jq4k_gemm_path(ALIGNED, ALIGNED2, ALIGNED3, 4, 8, jq4k.MFMA_MAX_K + 256, path,
+                                None) == jq4k.EINVAL
+
+
 def test_gemm_batched_argument_checks(L):
     f = L.jq4k_gemm_batched
 
@@ -173,7 +180,8 @@ def test_gemm_batched_argument_checks(L):
     for bad, code in (((ALIGNED, ALIGNED2, ALIGNED3, 4, 8, 300), jq4k.EINVAL),
                       ((ALIGNED, ALIGNED2, ALIGNED3, -1, 8, 256), jq4k.EINVAL),
                       ((ALIGNED, 0, ALIGNED3, 4, 8, 256), jq4k.EINVAL),
-                      ((ALIGNED, ALIGNED2 + 4, ALIGNED3, 4, 8, 256), jq4k.EALIGN)):
+                      ((ALIGNED, ALIGNED2 + 4, ALIGNED3, 4, 8, 256), jq4k.EALIGN),
+                      ((ALIGNED, ALIGNED2, ALIGNED3, 4, 8, jq4k.MFMA_MAX_K + 256), jq4k.EINVAL)):
         assert f(ctypes.addressof(descs(good, bad)), 2, None) == code, bad
     empty = descs((0, 0, 0, 0, 8, 256), (0, 0, 0, 5, 0, 512))
     assert f(ctypes.addressof(empty), 2, None) == jq4k.OK
