@@ -83,7 +83,7 @@ def timed(torch, fn, steps, warmup, use_graph):
 
 
 DEPENDENCY_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]   # q|k|v, o, gate|up, down
-PREFILL_KERNEL = "jq4k::q4k_gemm_mfma_kernel<128, 128, 2, 2>"   # jq4k_gemm_batched at M = 2048
+PREFILL_KERNEL = "jq4k::q4k_gemm_ws_kernel"   # jq4k_gemm_batched at M = 2048 (256-row tile)
 
 
 def decode_leg(torch, jq4k, args):

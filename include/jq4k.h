@@ -153,8 +153,9 @@ typedef struct {
  * path (the genie-ai-runtime README, "At a glance": tensor-core MMQ Q4_K
  * prefill; one launch for projections that do not depend on each other, such
  * as q, k and v, or gate and up, so that their tiles fill the GPU together).
- * The tile (64 or 128 rows of M) is the one jq4k_gemm picks for the largest
- * M of the batch; every problem meets the same bounds as jq4k_gemm.  Problems
+ * The tile (64, 128 or 256 rows of M) follows the largest M of the batch:
+ * 64 up to M = 64, 256 from M = 512, else 128; every problem meets the same
+ * bounds as jq4k_gemm.  Problems
  * with M == 0 or N == 0 are skipped.  `problems` is a host array read before
  * the call returns (passed to the kernel by value; nothing is allocated).
  * Outputs must not overlap any input.  Errors: JQ4K_EINVAL for count < 0,

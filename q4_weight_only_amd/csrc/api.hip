@@ -19,9 +19,7 @@ hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, f
                             const int* M, const int* N, const int* K, int count, int tile,
                             hipStream_t stream);
 long gemm_launch_size(const int* M, const int* N, int count, int tile);
-hipError_t launch_gemm_ws(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
-                          hipStream_t stream);
-long gemm_ws_launch_size(int M, int N);
+
 hipError_t launch_unpack_fields(const uint8_t* W, long nblocks, uint8_t* q, uint8_t* sc,
                                 uint8_t* m, hipStream_t stream);
 hipError_t launch_dequant_f32(const uint8_t* W, long nblocks, float* w, hipStream_t stream);
@@ -109,25 +107,22 @@ int gemv_batch_rows(int N, int K) {
     return R;
 }
 
-// MFMA tile for a shape: 64 rows of M up to M = 64, else 128 rows (the
-// 128 x 128 tile runs two workgroups per compute unit and measured fastest
-// on every Qwen3-4B projection shape at M = 2048).
-int mfma_tile_for(int M, int N) {
-    (void)N;
-    return M <= 64 ? 64 : 128;
+// MFMA tile (rows of M per workgroup) for the largest M of a launch: 64 up
+// to M = 64; then 128; 256 (the wave-specialised kernel) from M = 2048 for a
+// single matmul and from M = 512 for a grouped launch, whose several
+// problems fill the GPU with fewer, larger tiles.  Measured on the Qwen3-4B
+// projections at M = 128 .. 4096.
+int mfma_tile_for(int M, bool grouped) {
+    if (M <= 64) return 64;
+    return M >= (grouped ? 512 : 2048) ? 256 : 128;
 }
 
 int run_mfma(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K, int tile,
              hipStream_t stream) {
     if (K > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
-    const long wgs = tile == 256 ? jq4k::gemm_ws_launch_size(M, N)
-                                 : jq4k::gemm_launch_size(&M, &N, 1, tile);
-    if (wgs > 0x7FFFFFFFL) return JQ4K_EINVAL;
+    if (jq4k::gemm_launch_size(&M, &N, 1, tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
     const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
-    const hipError_t e = tile == 256
-                             ? jq4k::launch_gemm_ws(w, X, Y, M, N, K, stream)
-                             : jq4k::launch_gemm_mfma(&w, &X, &Y, &M, &N, &K, 1, tile, stream);
-    return static_cast<int>(e);
+    return static_cast<int>(jq4k::launch_gemm_mfma(&w, &X, &Y, &M, &N, &K, 1, tile, stream));
 }
 
 int check_export(const void* W, long nblocks, const void* out, uintptr_t out_align) {
@@ -218,7 +213,7 @@ int jq4k_gemm_batched(const jq4k_gemm_desc* problems, int count, hipStream_t str
     if (live == 0) return JQ4K_OK;
     for (int i = 0; i < live; ++i)
         if (K[i] > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
-    const int tile = mfma_tile_for(max_m, 0);
+    const int tile = mfma_tile_for(max_m, true);
     if (jq4k::gemm_launch_size(M, N, live, tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
     return static_cast<int>(jq4k::launch_gemm_mfma(W, X, Y, M, N, K, live, tile, stream));
 }
@@ -231,13 +226,13 @@ int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int
     if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
     switch (path) {
         case JQ4K_PATH_GEMV: return run_gemv(W, X, Y, N, K, 0, stream);
-        case JQ4K_PATH_MFMA: return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, N), stream);
+        case JQ4K_PATH_MFMA: return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, false), stream);
         case JQ4K_PATH_MFMA_T64: return run_mfma(W, X, Y, M, N, K, 64, stream);
         case JQ4K_PATH_MFMA_T128: return run_mfma(W, X, Y, M, N, K, 128, stream);
         case JQ4K_PATH_MFMA_T256: return run_mfma(W, X, Y, M, N, K, 256, stream);
         default:
             if (M == 1 && K <= JQ4K_GEMV_MAX_K) return run_gemv(W, X, Y, N, K, 0, stream);
-            return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, N), stream);
+            return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, false), stream);
     }
 }
 

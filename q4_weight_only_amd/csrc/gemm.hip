@@ -222,21 +222,6 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
     }
 }
 
-// One launch computes the tiles of up to kSchedMax independent problems
-// (a single matmul is a batch of one); the descriptors and the tile schedule
-// travel in the kernel arguments.
-struct GemmProblem {
-    const uint8_t* W;
-    const uint16_t* X;
-    float* Y;
-    int M, N, K;
-};
-
-struct GemmBatch {
-    GemmProblem p[kSchedMax];
-    TileSched s;
-};
-
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(const GemmBatch batch,
                                                                      uint32_t qmask) {
@@ -248,36 +233,20 @@ __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(const GemmB
     gemm_tile<BM, BN, WM, WN>(pr.W, pr.X, pr.Y, pr.M, pr.N, pr.K, tn * BN, tm * BM, qmask, lds);
 }
 
-// Band height of the grouped tile order: 256 rows of X (measured best of
-// 128..2048 on the seven projections of a layer at M = 512 and M = 2048).
-constexpr int group_rows(int BM) { return BM >= 256 ? 1 : 256 / BM; }
-
 template <int BM, int BN, int WM, int WN>
 static hipError_t launch_cfg(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
                              const int* M, const int* N, const int* K, int count,
                              hipStream_t stream) {
-    // queue order: longest K first (stable), so the longest tiles start first
-    int order[kSchedMax];
-    for (int i = 0; i < count; ++i) order[i] = i;
-    for (int i = 1; i < count; ++i)
-        for (int j = i; j > 0 && K[order[j]] > K[order[j - 1]]; --j) {
-            const int t = order[j];
-            order[j] = order[j - 1];
-            order[j - 1] = t;
-        }
-    GemmBatch b = {};
-    int Ms[kSchedMax], Ns[kSchedMax];
-    for (int i = 0; i < count; ++i) {
-        const int o = order[i];
-        b.p[i] = {W[o], X[o], Y[o], M[o], N[o], K[o]};
-        Ms[i] = M[o];
-        Ns[i] = N[o];
-    }
-    const long grid = tile_sched_init(b.s, Ms, Ns, count, BM, BN, group_rows(BM));
+    GemmBatch b;
+    const long grid = gemm_batch_init(b, W, X, Y, M, N, K, count, BM, BN);
     hipLaunchKernelGGL((q4k_gemm_mfma_kernel<BM, BN, WM, WN>), dim3(static_cast<unsigned>(grid)),
                        dim3(kGemmThreads), 0, stream, b, kNibbleMask);
     return hipGetLastError();
 }
+
+hipError_t launch_gemm_ws(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
+                          const int* M, const int* N, const int* K, int count,
+                          hipStream_t stream);
 
 // Workgroups a launch of these problems takes (tiles plus at most seven idle
 // workgroups per problem).
@@ -287,12 +256,13 @@ long gemm_launch_size(const int* M, const int* N, int count, int tile) {
     return tile_sched_init(s, M, N, count, tile, bn, 1);
 }
 
-// tile: 64 or 128 rows of M per workgroup, for the whole batch (the 256-row
-// tile is the wave-specialised kernel of gemm_ws.hip).
+// tile: 64, 128 or 256 rows of M per workgroup, for the whole batch (the
+// 256-row tile is the wave-specialised kernel of gemm_ws.hip).
 hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
                             const int* M, const int* N, const int* K, int count, int tile,
                             hipStream_t stream) {
     if (tile == 64) return launch_cfg<64, 256, 1, 4>(W, X, Y, M, N, K, count, stream);
+    if (tile == 256) return launch_gemm_ws(W, X, Y, M, N, K, count, stream);
     return launch_cfg<128, 128, 2, 2>(W, X, Y, M, N, K, count, stream);
 }
 

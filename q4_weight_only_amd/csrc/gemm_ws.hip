@@ -44,16 +44,20 @@ struct WsRegs {
 
 }  // namespace
 
-__global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(
-    const uint8_t* __restrict__ W, const uint16_t* __restrict__ X, float* __restrict__ Y,
-    int M, int N, int K, const TileSched sched, uint32_t qmask) {
+__global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch batch,
+                                                                 uint32_t qmask) {
     __shared__ uint4 lds[2][kWsLdsChunks];
 
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
 
     int q, tm, tn;
-    if (!tile_sched_next(sched, blockIdx.x, &q, &tm, &tn)) return;
+    if (!tile_sched_next(batch.s, blockIdx.x, &q, &tm, &tn)) return;
+    const GemmProblem& pr = batch.p[q];
+    const uint8_t* __restrict__ W = pr.W;
+    const uint16_t* __restrict__ X = pr.X;
+    float* __restrict__ Y = pr.Y;
+    const int M = pr.M, N = pr.N, K = pr.K;
     const int n0 = tn * kWsBN, m0 = tm * kWsBM;
     const int nb = K / kQK;
     const int nstage = K / kWsBK;  // a multiple of 4
@@ -191,17 +195,13 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(
     }
 }
 
-long gemm_ws_launch_size(int M, int N) {
-    TileSched s;
-    return tile_sched_init(s, &M, &N, 1, kWsBM, kWsBN, 1);
-}
-
-hipError_t launch_gemm_ws(const uint8_t* W, const uint16_t* X, float* Y, int M, int N, int K,
+hipError_t launch_gemm_ws(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
+                          const int* M, const int* N, const int* K, int count,
                           hipStream_t stream) {
-    TileSched s;
-    const long grid = tile_sched_init(s, &M, &N, 1, kWsBM, kWsBN, 2);
+    GemmBatch b;
+    const long grid = gemm_batch_init(b, W, X, Y, M, N, K, count, kWsBM, kWsBN);
     hipLaunchKernelGGL(q4k_gemm_ws_kernel, dim3(static_cast<unsigned>(grid)), dim3(kWsThreads),
-                       0, stream, W, X, Y, M, N, K, s, kNibbleMask);
+                       0, stream, b, kNibbleMask);
     return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-// tile_sched.h -- which output tile each workgroup of a matmul launch computes.
+// tile_sched.h -- which output tile each workgroup of a matmul launch
+// computes, and the list of problems a launch carries.
 //
 // A launch covers one or more independent problems, each a TM x TN grid of
 // output tiles.  An MI355X has eight accelerator complex dies (XCDs), each
@@ -17,6 +18,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace jq4k {
 
@@ -70,6 +72,50 @@ __host__ __device__ __forceinline__ bool tile_sched_next(const TileSched& s, uns
     *tile_m = first + r % rows;
     *tile_n = r / rows;
     return true;
+}
+
+// One launch computes the tiles of up to kSchedMax independent problems (a
+// single matmul is a batch of one); the descriptors and the tile schedule
+// travel in the kernel arguments.
+struct GemmProblem {
+    const uint8_t* W;
+    const uint16_t* X;
+    float* Y;
+    int M, N, K;
+};
+
+struct GemmBatch {
+    GemmProblem p[kSchedMax];
+    TileSched s;
+};
+
+// Band height of the grouped tile order, in tile rows: 256 rows of X for
+// the 64- and 128-row tiles, 512 for the 256-row tile (measured best on the
+// seven projections of a layer at M = 512 .. 4096).
+constexpr int group_rows(int BM) { return BM >= 256 ? 2 : 256 / BM; }
+
+// Host side: the batch for BM x BN tiles, problems queued longest K first
+// (stable).  Returns the number of workgroups to launch.
+inline long gemm_batch_init(GemmBatch& b, const uint8_t* const* W, const uint16_t* const* X,
+                            float* const* Y, const int* M, const int* N, const int* K, int count,
+                            int BM, int BN) {
+    int order[kSchedMax];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    for (int i = 1; i < count; ++i)
+        for (int j = i; j > 0 && K[order[j]] > K[order[j - 1]]; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    b = GemmBatch{};
+    int Ms[kSchedMax], Ns[kSchedMax];
+    for (int i = 0; i < count; ++i) {
+        const int o = order[i];
+        b.p[i] = {W[o], X[o], Y[o], M[o], N[o], K[o]};
+        Ms[i] = M[o];
+        Ns[i] = N[o];
+    }
+    return tile_sched_init(b.s, Ms, Ns, count, BM, BN, group_rows(BM));
 }
 
 }  // namespace jq4k

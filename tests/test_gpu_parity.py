@@ -230,12 +230,19 @@ def test_gemm_auto_and_determinism(gpu, M):
     parity(y1, Y, A, f"auto M={M}")
 
 
-def test_gemm_batched_mixed_problems(gpu):
+@pytest.mark.parametrize("seed,shapes,path", [
+    # largest M below 512: the 128-row tile
+    (110, [(300, 130, 512), (77, 384, 768), (129, 65, 256), (0, 64, 256), (256, 1000, 2560)],
+     "PATH_MFMA_T128"),
+    # largest M from 512: the 256-row wave-specialised kernel, ragged in M and N
+    (111, [(600, 200, 512), (512, 130, 768), (1, 64, 256), (37, 300, 256), (259, 0, 512)],
+     "PATH_MFMA_T256"),
+])
+def test_gemm_batched_mixed_problems(gpu, seed, shapes, path):
     """One MFMA launch for independent problems of different shapes: each
     output meets the bound and equals the single-problem result on the same
     tile bit for bit."""
-    g = np.random.default_rng(110)
-    shapes = [(300, 130, 512), (77, 384, 768), (129, 65, 256), (0, 64, 256), (256, 1000, 2560)]
+    g = np.random.default_rng(seed)
     probs = []
     for M, N, K in shapes:
         probs.append((M, N, K, qi.weight_bytes(g, N, K), qi.activations(g, M, K)))
@@ -246,10 +253,10 @@ def test_gemm_batched_mixed_problems(gpu):
     announce(f"gemm batched {len(probs)} problems")
     gpu.gemm_batched(list(zip(Wd, Xd, Yb)))
     for (M, N, K, W, X), wd, xd, yb in zip(probs, Wd, Xd, Yb):
-        if M == 0:
+        if M == 0 or N == 0:
             continue
         ys = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
-        gpu.gemm(wd, xd, ys, path=gpu.PATH_MFMA_T128)
+        gpu.gemm(wd, xd, ys, path=getattr(gpu, path))
         got = host(yb)
         assert np.array_equal(got.view(np.uint32), host(ys).view(np.uint32)), (M, N, K)
         Y, A = oracle.gemm(W, X, N, K)
