@@ -160,25 +160,29 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0,
                                                                      0);
     };
-    // four k-steps of 16; the fragments of step ks + 1 are read while step ks
-    // multiplies (two named fragment sets, kept in registers)
-    auto mfma_stage = [&](const uint4* buf) {
-        bf16x8_t a0[kWsTM], b0[kWsTN], a1[kWsTM], b1[kWsTN];
-        read_frags(buf, 0, a0, b0);
-        read_frags(buf, 1, a1, b1);
+    // Four k-steps of 16 per stage; the fragments of step ks + 1 are read
+    // while step ks multiplies (two named fragment sets).  The last step of
+    // a stage is issued after the barrier, behind the reads of the next
+    // stage's first fragments, so the matrix cores stay busy while the LDS
+    // latency of the new stage passes.
+    bf16x8_t a0[kWsTM], b0[kWsTN], a1[kWsTM], b1[kWsTN];
+    auto half = [&](const uint4* cur, const uint4* nxt) {
         mma(a0, b0);
-        read_frags(buf, 2, a0, b0);
+        read_frags(cur, 2, a0, b0);
         mma(a1, b1);
-        read_frags(buf, 3, a1, b1);
+        read_frags(cur, 3, a1, b1);
         mma(a0, b0);
+        __syncthreads();
+        read_frags(nxt, 0, a0, b0);
         mma(a1, b1);
+        read_frags(nxt, 1, a1, b1);
     };
     __syncthreads();
+    read_frags(lds[0], 0, a0, b0);
+    read_frags(lds[0], 1, a1, b1);
     for (int s = 0; s < nstage; s += 2) {
-        mfma_stage(lds[0]);
-        __syncthreads();
-        mfma_stage(lds[1]);
-        __syncthreads();
+        half(lds[0], lds[1]);
+        half(lds[1], lds[0]);
     }
 #pragma unroll
     for (int i = 0; i < kWsTM; ++i) {
