@@ -123,7 +123,7 @@ __device__ __forceinline__ float quarter_dot(const QuarterLoad& ld, int c, const
 
 // LDS: x chunks (nb*36 x 16 B), per-sub-block sums X_s (nb*8 floats, as a
 // float2 (even, odd) per (kb, quarter)), per-block partials (R*nb floats).
-constexpr int kGemvDepth = 4;  // quarter tasks in flight per thread
+constexpr int kGemvDepth = 2;  // quarter tasks in flight per thread (2 measured best: 74 VGPRs, 6 waves per SIMD)
 constexpr int kGemvMaxK = 16384;
 constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
 
