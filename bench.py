@@ -244,6 +244,70 @@ def prefill_leg(torch, jq4k, args):
     return flops, secs, modes, per_proj
 
 
+def prefill_m33_leg(torch, jq4k, args):
+    """M = 33 through all 36 layers' seven projections (252 matmuls, 2.04 GB of
+    Q4_K weights, child seeds [2, layer, p]): one jq4k_gemm_batched launch per
+    layer, 36 per pass.  HBM-bound: the attainable roofline counts W, X and Y
+    bytes at 8 TB/s."""
+    import ctypes
+    M, L = 33, jq4k.raw()
+    keep, arrs = [], []
+    wbytes = xybytes = flops = 0
+    for layer in range(36):
+        arr = (jq4k.GemmDesc * 7)()
+        for p in range(7):
+            _, N, K, W, X = qi.prefill_projection(2, layer, p, M)
+            Wd = torch.from_numpy(W).to("cuda:0")
+            Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+            Yd = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+            keep.append((Wd, Xd, Yd))
+            arr[p] = jq4k.GemmDesc(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K)
+            wbytes += W.nbytes
+            xybytes += X.nbytes + M * N * 4
+            flops += 2.0 * M * N * K
+        arrs.append(arr)
+
+    def one_pass(i):
+        s = torch.cuda.current_stream().cuda_stream
+        for arr in arrs:
+            rc = L.jq4k_gemm_batched(ctypes.addressof(arr), 7, s)
+            if rc:
+                raise RuntimeError(jq4k.strerror(rc))
+    steps = max(3, args.prefill_steps // 2)
+    t = timed(torch, one_pass, steps, 1, not args.eager) / steps
+    allb = wbytes + xybytes
+    return {"workload": "Qwen3-4B cold prefill, M=33 through 36 layers x 7 Q4_K projections "
+                        "(252 matmuls), seeds [2,l,p]; one jq4k_gemm_batched launch per layer",
+            "launches_per_pass": 36, "us_per_pass": round(t * 1e6, 1),
+            "weight_GB_s": round(wbytes / t / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(allb / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(allb / t / 1e9 / HBM_PEAK_GBS, 4),
+                         "bytes_per_pass": allb},
+            "TFLOP_s": round(flops / t / 1e12, 2)}
+
+
+def lm_head_m512_leg(torch, jq4k, args):
+    """The 151936 x 2560 Q4_K LM head at M = 512 (a prefill chunk): one
+    jq4k_gemm launch, MFMA-bound."""
+    W, X = qi.lm_head(4, 512)
+    N, K, M = 151936, 2560, 512
+    Wd = torch.from_numpy(W).to("cuda:0")
+    Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+    Yd = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    L = jq4k.raw()
+
+    def one(i):
+        rc = L.jq4k_gemm(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K,
+                         torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+    steps = max(3, args.prefill_steps)
+    t = timed(torch, one, steps, 2, not args.eager) / steps
+    tf = 2.0 * M * N * K / t / 1e12
+    return {"N": N, "K": K, "M": M, "us": round(t * 1e6, 1), "TFLOP_s": round(tf, 1),
+            "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def profile_run(torch, jq4k):
     """Launches for rocprofv3 runs: a 512 MiB device copy (the reference for
     scaling FETCH_SIZE / WRITE_SIZE), then 20 batched decode-layer GEMVs, 20
@@ -360,6 +424,8 @@ def main():
     gbs = layer_bytes * args.steps / secs / 1e9
     lm = lm_head_leg(torch, jq4k, args)
     flops, psecs, p_modes, p_per = prefill_leg(torch, jq4k, args)
+    m33 = prefill_m33_leg(torch, jq4k, args)
+    lm512 = lm_head_m512_leg(torch, jq4k, args)
     tflops = flops * args.prefill_steps / psecs / 1e12
 
     out = {
@@ -411,6 +477,8 @@ def main():
             "modes": p_modes,
             "per_projection": p_per,
         },
+        "prefill_m33_36_layers": m33,
+        "lm_head_m512": lm512,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layer)

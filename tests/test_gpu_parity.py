@@ -272,14 +272,60 @@ def test_prefill_m33_one_layer(gpu):
         parity(y, Y, A, f"M=33 {name}")
 
 
+def _grouped_layer(gpu, projs, M):
+    """The seven projections of a layer in one grouped launch (as the
+    benchmark times them); returns the host outputs."""
+    Wd = [dev(W) for _, _, _, W, _ in projs]
+    Xd = [dev(X).view(torch.bfloat16) for _, _, _, _, X in projs]
+    Yd = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+          for _, N, _, _, _ in projs]
+    gpu.gemm_batched(list(zip(Wd, Xd, Yd)))
+    return [host(y) for y in Yd]
+
+
 def test_prefill_m2048_sampled(gpu):
+    """M = 2048, one layer, one grouped launch (the 256-row tile): sampled
+    rows and tokens of every projection against the oracle."""
     g = np.random.default_rng(108)
-    for p in range(7):
-        name, N, K, W, X = qi.prefill_projection(3, 0, p, 2048)
-        announce(f"prefill M=2048 {name} {N}x{K}")
-        y = run_gemm(W, X, N, K)
+    projs = [qi.prefill_projection(3, 0, p, 2048) for p in range(7)]
+    announce("prefill M=2048 layer 0, one grouped launch")
+    ys = _grouped_layer(gpu, projs, 2048)
+    for (name, N, K, W, X), y in zip(projs, ys):
         rows = np.sort(g.choice(N, 48, replace=False))
         ms = np.sort(g.choice(2048, 24, replace=False))
         Y, A = oracle.gemm(W[rows], X[ms], len(rows), K)
         parity(y[np.ix_(ms, rows)], Y, A, f"M=2048 {name} sampled")
         assert np.all(np.isfinite(y))
+
+
+def test_prefill_m33_all_layers_sampled(gpu):
+    """M = 33 through all 36 layers (252 matmuls), each layer one grouped
+    launch: 12 sampled rows of every output, all 33 tokens, against the
+    oracle."""
+    g = np.random.default_rng(113)
+    for layer in range(36):
+        projs = [qi.prefill_projection(2, layer, p, 33) for p in range(7)]
+        announce(f"prefill M=33 layer {layer}, one grouped launch")
+        ys = _grouped_layer(gpu, projs, 33)
+        for (name, N, K, W, X), y in zip(projs, ys):
+            rows = np.sort(g.choice(N, 12, replace=False))
+            Y, A = oracle.gemm(W[rows], X, len(rows), K)
+            parity(y[:, rows], Y, A, f"M=33 layer {layer} {name} sampled")
+            assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("M", [1, 512])
+def test_lm_head_sampled(gpu, M):
+    """The 151936 x 2560 LM head at M = 1 (the GEMV) and M = 512 (X1 is row 0
+    of X512): sampled rows against the oracle, every output finite."""
+    g = np.random.default_rng(114 + M)
+    W, X = qi.lm_head(4, 512)
+    X = X[:M]
+    N, K = 151936, 2560
+    announce(f"LM head M={M}")
+    y = run_gemm(W, X, N, K)
+    rows = np.sort(g.choice(N, 64, replace=False))
+    ms = np.sort(g.choice(M, min(M, 32), replace=False))
+    Y, A = oracle.gemm(W[rows], X[ms], len(rows), K)
+    parity(y[np.ix_(ms, rows)], Y, A, f"LM head M={M} sampled")
+    assert np.all(np.isfinite(y))
