@@ -53,6 +53,9 @@ struct GemmCfg {
     static_assert(kThreadsPerRow == 1 || kThreadsPerRow == 2 || kThreadsPerRow == 4, "BN");
     static constexpr int kQBytes = 32 / kThreadsPerRow;               // quant bytes / thread
     static constexpr int kLdsChunks = (BM + BN) * kRowChunks;         // per buffer
+    // register sets of global data in flight: deeper for the 64-row tile,
+    // whose loop is load-latency-bound at small M
+    static constexpr int kSets = BM == 64 ? 4 : 2;
 };
 
 // One BM x BN tile of Y = X . W^T, rows m0.. and columns n0.. (the whole
@@ -92,7 +95,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
         uint4 hdr;
         uint32_t q[C::kQBytes / 4];
     };
-    StageRegs rs[2];
+    StageRegs rs[C::kSets];
 
     auto load_stage = [&](int s, StageRegs& r) {
         const int kb = s >> 2, c = s & 3;
@@ -155,12 +158,12 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
 
     // Software pipeline, one barrier per stage.  While the matrix cores work
     // on stage s from LDS buffer s & 1, the same instruction stream
-    // dequantises stage s + 1 (from register set (s + 1) & 1) into the other
-    // buffer and requests stage s + 3 into the register set it just freed, so
-    // global data has two stages of work to arrive.  Stage indices past the
-    // end are clamped (harmless repeats), keeping the body one basic block.
-    // Within a stage the operand fragments of k-step ks + 1 are read from LDS
-    // while the MFMAs of k-step ks run.
+    // dequantises stage s + 1 (from register set (s + 1) % S) into the other
+    // buffer and requests stage s + 1 + S into the register set it just
+    // freed, so global data has S stages of work to arrive (S = kSets).
+    // Stage indices past the end are clamped (harmless repeats), keeping the
+    // body one basic block.  Within a stage the operand fragments of k-step
+    // ks + 1 are read from LDS while the MFMAs of k-step ks run.
     auto read_frags = [&](const uint4* buf, int ks, bf16x8_t* a, bf16x8_t* b) {
         const uint4* xb = buf;
         const uint4* wb = buf + BM * kRowChunks;
@@ -188,22 +191,20 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
     };
     auto last = [&](int s) { return min(s, nstage - 1); };
 
-    load_stage(0, rs[0]);
-    load_stage(last(1), rs[1]);
+#pragma unroll
+    for (int j = 0; j < C::kSets; ++j) load_stage(last(j), rs[j]);
     store_stage(0, rs[0], lds[0]);
-    load_stage(last(2), rs[0]);
+    load_stage(last(C::kSets), rs[0]);
     __syncthreads();
-    for (int s = 0; s < nstage; s += 2) {
-        // even stage s: fragments from lds[0], next stage from rs[1]
-        mfma_stage(lds[0]);
-        store_stage(last(s + 1), rs[1], lds[1]);
-        load_stage(last(s + 3), rs[1]);
-        __syncthreads();
-        // odd stage (nstage = K / 64 is a multiple of 4, so s + 1 < nstage) s + 1: fragments from lds[1], next stage from rs[0]
-        mfma_stage(lds[1]);
-        store_stage(last(s + 2), rs[0], lds[0]);
-        load_stage(last(s + 4), rs[0]);
-        __syncthreads();
+    // nstage = K / 64 is a multiple of 4, hence of kSets
+    for (int s = 0; s < nstage; s += C::kSets) {
+#pragma unroll
+        for (int u = 0; u < C::kSets; ++u) {
+            mfma_stage(lds[u & 1]);
+            store_stage(last(s + u + 1), rs[(u + 1) % C::kSets], lds[(u + 1) & 1]);
+            load_stage(last(s + u + 1 + C::kSets), rs[(u + 1) % C::kSets]);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: fp32 Y, row-major
