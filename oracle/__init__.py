@@ -151,3 +151,40 @@ def within_tolerance(y, Y_ref, A) -> np.ndarray:
     """Boolean mask of the elements that satisfy the bound (NaN never does)."""
     y = np.asarray(y, np.float64)
     return np.abs(y - Y_ref) <= tolerance(A)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU of a gate/up pair (the genie-ai-runtime README, "At a glance": fused
+# RMSNorm + RoPE + SwiGLU kernels; the pages do not define the function, and
+# the reading taken is Qwen3's MLP activation, h = silu(g) * u with
+# silu(z) = z * sigmoid(z), on the outputs g = X.Wg^T and u = X.Wu^T).
+
+SILU_LIPSCHITZ = 1.0999  # max |silu'(z)| = 1.0998... (near z = 2.40)
+
+
+def silu(z):
+    """silu(z) = z / (1 + exp(-z)) in fp64 (exp(-z) may overflow to inf for
+    very negative z, giving the correct limit -0)."""
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def gemm_swiglu(Wg, Wu, X_bf16, N: int, K: int):
+    """H = silu(X.Wg^T) * (X.Wu^T) in fp64, from two oracle contractions.
+    Returns (H, G, U, Ag, Au): the fp64 gate and up outputs and their
+    sum |w*x| are what the bound of swiglu_tolerance needs."""
+    G, Ag = gemm(Wg, X_bf16, N, K)
+    U, Au = gemm(Wu, X_bf16, N, K)
+    return silu(G) * U, G, U, Ag, Au
+
+
+def swiglu_tolerance(G, U, Ag, Au):
+    """Per-element bound on |h_gpu - h_ref| for h = silu(g) * u, derived from
+    the matmul bound tau = 2e-3 * A + 1e-5 on g and on u:
+      |silu(g)u - silu(g*)u*| <= L tau_g (|u*| + tau_u) + |silu(g*)| tau_u,
+    L = max |silu'|, plus 1e-6 |h*| for the fp32 evaluation of silu and the
+    product on the GPU (a few rounding steps of 2^-24)."""
+    tg, tu = tolerance(Ag), tolerance(Au)
+    sg = np.abs(silu(G))
+    return SILU_LIPSCHITZ * tg * (np.abs(U) + tu) + sg * tu + 1e-6 * sg * np.abs(U)

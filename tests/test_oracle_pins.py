@@ -373,3 +373,67 @@ def test_planted_transposed_x_breaks_tolerance(single_gemv_ref):
     W, X, Y, A = single_gemv_ref
     Yb, _ = oracle.gemm(W, X[:, ::-1].copy(), 2560, 2560)
     assert 1.0 - oracle.within_tolerance(Yb, Y, A).mean() > 0.25
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU epilogue (h = silu(g) * u)
+
+def test_silu_closed_forms_and_library():
+    import torch
+    z = np.concatenate([np.linspace(-60, 60, 2001), [0.0, 1e-300, -1e-300, 700.0, -700.0]])
+    s = oracle.silu(z)
+    assert s[np.where(z == 0.0)[0][0]] == 0.0
+    # silu(z) - silu(-z) = z, since sigmoid(z) + sigmoid(-z) = 1
+    assert np.allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=1e-14, atol=1e-300)
+    # silu(z) -> z for large z, -> 0 for very negative z
+    assert oracle.silu(np.array([700.0]))[0] == 700.0
+    assert 0.0 > oracle.silu(np.array([-700.0]))[0] > -1e-300     # -700 e^-700
+    assert oracle.silu(np.array([-800.0]))[0] == 0.0               # e^800 overflows
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    assert np.allclose(s, ref, rtol=1e-13, atol=1e-300)
+
+
+def test_silu_lipschitz_constant():
+    z = np.linspace(-20, 20, 400001)
+    sig = 1.0 / (1.0 + np.exp(-z))
+    d = sig * (1.0 + z * (1.0 - sig))          # silu'(z)
+    assert np.max(np.abs(d)) <= oracle.SILU_LIPSCHITZ
+    assert np.max(np.abs(d)) > oracle.SILU_LIPSCHITZ - 1e-3
+
+
+def _swiglu_case(seed, N=48, K=512, M=3):
+    g = np.random.default_rng(seed)
+    Wg = qi.weight_bytes(g, N, K)
+    Wu = qi.weight_bytes(g, N, K)
+    X = qi.activations(g, M, K)
+    return Wg, Wu, X, N, K
+
+
+def test_swiglu_is_silu_of_gate_times_up():
+    Wg, Wu, X, N, K = _swiglu_case(200)
+    H, G, U, Ag, Au = oracle.gemm_swiglu(Wg, Wu, X, N, K)
+    Gs, _ = oracle.gemm(Wg, X, N, K)
+    Us, _ = oracle.gemm(Wu, X, N, K)
+    assert np.array_equal(G, Gs) and np.array_equal(U, Us)
+    sig = 1.0 / (1.0 + np.exp(-Gs))
+    assert np.allclose(H, Gs * sig * Us, rtol=1e-13, atol=0)
+
+
+def test_swiglu_bound_holds_for_perturbed_inputs_and_rejects_mistakes():
+    """The bound admits any g, u within the matmul bound (worst-case signs),
+    and planted mistakes in the epilogue fail it on most outputs."""
+    Wg, Wu, X, N, K = _swiglu_case(201)
+    H, G, U, Ag, Au = oracle.gemm_swiglu(Wg, Wu, X, N, K)
+    tol = oracle.swiglu_tolerance(G, U, Ag, Au)
+    tg, tu = oracle.tolerance(Ag), oracle.tolerance(Au)
+    for sg in (-1, 1):
+        for su in (-1, 1):
+            h = oracle.silu(G + sg * tg) * (U + su * tu)
+            assert np.all(np.abs(h - H) <= tol)
+    sig = 1.0 / (1.0 + np.exp(-G))
+    for wrong in (sig * U,                       # sigmoid instead of silu
+                  oracle.silu(U) * G,            # gate and up swapped
+                  G * U,                         # no activation
+                  oracle.silu(np.roll(G, 1, axis=1)) * U):   # gate of the neighbouring row
+        bad = np.abs(wrong - H) > tol
+        assert bad.mean() > 0.25, bad.mean()
