@@ -83,7 +83,7 @@ def timed(torch, fn, steps, warmup, use_graph):
 
 
 DEPENDENCY_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]   # q|k|v, o, gate|up, down
-PREFILL_KERNEL = "jq4k::q4k_gemm_ws_kernel"   # jq4k_gemm_batched at M = 2048 (256-row tile)
+PREFILL_KERNEL = "jq4k::q4k_gemm_ws_kernel<false>"   # jq4k_gemm_batched at M = 2048 (256-row tile)
 
 
 def decode_leg(torch, jq4k, args):
@@ -308,6 +308,73 @@ def lm_head_m512_leg(torch, jq4k, args):
             "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def swiglu_leg(torch, jq4k, args):
+    """gate|up of a layer with the SwiGLU epilogue fused (jq4k_gemm_swiglu):
+    M = 1 (the decode gate/up, rotated over copies like the decode leg) and
+    M = 2048; beside each, the same two matmuls as one grouped launch without
+    the epilogue."""
+    import ctypes
+    L = jq4k.raw()
+    out = {}
+    for M, seed in ((1, 1), (2048, 3)):
+        if M == 1:
+            layer = qi.decode_layer(1, 0, 1)
+            (_, N, K, Wg, X), (_, _, _, Wu, _) = layer[4], layer[5]
+        else:
+            _, N, K, Wg, X = qi.prefill_projection(seed, 0, 4, M)
+            _, _, _, Wu, _ = qi.prefill_projection(seed, 0, 5, M)
+        wbytes = Wg.nbytes + Wu.nbytes
+        copies = max(2, math.ceil(ROTATION_BYTES / wbytes)) if M == 1 else 1
+        Wgs = [torch.from_numpy(Wg).to("cuda:0")]
+        Wus = [torch.from_numpy(Wu).to("cuda:0")]
+        for _ in range(copies - 1):
+            Wgs.append(Wgs[0].clone())
+            Wus.append(Wus[0].clone())
+        Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+        H = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        Yg = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        Yu = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+
+        def fused(i):
+            rc = L.jq4k_gemm_swiglu(Wgs[i % copies].data_ptr(), Wus[i % copies].data_ptr(),
+                                    Xd.data_ptr(), H.data_ptr(), M, N, K,
+                                    torch.cuda.current_stream().cuda_stream)
+            if rc:
+                raise RuntimeError(jq4k.strerror(rc))
+        descs = []
+        for c in range(copies):
+            if M == 1:
+                arr = (jq4k.GemvDesc * 2)()
+                arr[0] = jq4k.GemvDesc(Wgs[c].data_ptr(), Xd.data_ptr(), Yg.data_ptr(), N, K)
+                arr[1] = jq4k.GemvDesc(Wus[c].data_ptr(), Xd.data_ptr(), Yu.data_ptr(), N, K)
+            else:
+                arr = (jq4k.GemmDesc * 2)()
+                arr[0] = jq4k.GemmDesc(Wgs[c].data_ptr(), Xd.data_ptr(), Yg.data_ptr(), M, N, K)
+                arr[1] = jq4k.GemmDesc(Wus[c].data_ptr(), Xd.data_ptr(), Yu.data_ptr(), M, N, K)
+            descs.append(arr)
+        grouped_fn = L.jq4k_gemv_batched if M == 1 else L.jq4k_gemm_batched
+
+        def grouped(i):
+            rc = grouped_fn(ctypes.addressof(descs[i % copies]), 2,
+                            torch.cuda.current_stream().cuda_stream)
+            if rc:
+                raise RuntimeError(jq4k.strerror(rc))
+        steps = args.steps if M == 1 else args.prefill_steps
+        tf = timed(torch, fused, steps, 3, not args.eager) / steps
+        tg = timed(torch, grouped, steps, 3, not args.eager) / steps
+        key = "m1" if M == 1 else f"m{M}"
+        if M == 1:
+            out[key] = {"N": N, "K": K, "weight_bytes": wbytes, "fused_us": round(tf * 1e6, 2),
+                        "fused_GB_s": round(wbytes / tf / 1e9, 1),
+                        "grouped_no_epilogue_us": round(tg * 1e6, 2)}
+        else:
+            fl = 2.0 * 2 * M * N * K
+            out[key] = {"N": N, "K": K, "M": M, "fused_us": round(tf * 1e6, 1),
+                        "fused_TFLOP_s": round(fl / tf / 1e12, 1),
+                        "grouped_no_epilogue_us": round(tg * 1e6, 1)}
+    return out
+
+
 def profile_run(torch, jq4k):
     """Launches for rocprofv3 runs: a 512 MiB device copy (the reference for
     scaling FETCH_SIZE / WRITE_SIZE), then 20 batched decode-layer GEMVs, 20
@@ -426,6 +493,7 @@ def main():
     flops, psecs, p_modes, p_per = prefill_leg(torch, jq4k, args)
     m33 = prefill_m33_leg(torch, jq4k, args)
     lm512 = lm_head_m512_leg(torch, jq4k, args)
+    swiglu = swiglu_leg(torch, jq4k, args)
     tflops = flops * args.prefill_steps / psecs / 1e12
 
     out = {
@@ -479,6 +547,7 @@ def main():
         },
         "prefill_m33_36_layers": m33,
         "lm_head_m512": lm512,
+        "swiglu_gate_up": swiglu,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layer)

@@ -164,6 +164,21 @@ typedef struct {
  * then. */
 int jq4k_gemm_batched(const jq4k_gemm_desc *problems, int count, hipStream_t stream);
 
+/* SwiGLU of a gate/up projection pair, one launch for any M >= 0:
+ * H (M x N) = silu(X . Wg^T) * (X . Wu^T), elementwise, silu(z) = z / (1 +
+ * exp(-z)) (the genie-ai-runtime README, "At a glance": fused RMSNorm + RoPE
+ * + SwiGLU; the activation of Qwen3's MLP).  Wg and Wu are N rows of K/256
+ * blocks each; the gate and up products are never written.  M == 1 with
+ * K <= JQ4K_GEMV_MAX_K runs the decode GEMV over both matrices; larger M the
+ * MFMA kernels (K <= JQ4K_MFMA_MAX_K), each tile holding the gate and up
+ * columns of the same outputs.  Accuracy: each of g and u within the
+ * matmul's bound, then silu and the product in fp32.  M == 0 or N == 0
+ * returns 0 without launching.  Errors: JQ4K_EINVAL / JQ4K_EALIGN under the
+ * rules of jq4k_gemm, applied to both matrices; H must not overlap an
+ * input. */
+int jq4k_gemm_swiglu(const block_q4_K *Wg, const block_q4_K *Wu, const jq4k_bf16 *X, float *H,
+                     int M, int N, int K, hipStream_t stream);
+
 /* Kernel paths for jq4k_gemm_path (tests and benchmarks reach every path). */
 #define JQ4K_PATH_AUTO 0 /* what jq4k_gemm picks                        */
 #define JQ4K_PATH_GEMV 1 /* the M = 1 kernel (M must be 1)               */

@@ -73,6 +73,8 @@ def _load():
         L.jq4k_gemm_batched.argtypes = [vp, i, vp]
         L.jq4k_gemm_batched.restype = i
         L.jq4k_gemm_path.argtypes = [vp, vp, vp, i, i, i, i, vp]
+        L.jq4k_gemm_swiglu.argtypes = [vp, vp, vp, vp, i, i, i, vp]
+        L.jq4k_gemm_swiglu.restype = i
         L.jq4k_gemm_path.restype = i
         L.jq4k_unpack_fields.argtypes = [vp, l, vp, vp, vp, vp]
         L.jq4k_unpack_fields.restype = i
@@ -192,6 +194,16 @@ def gemm(W, X, Y, stream=None, path=PATH_AUTO):
                               _stream(stream))
     _check(rc, "jq4k_gemm")
     return Y
+
+
+def gemm_swiglu(Wg, Wu, X, H, stream=None):
+    """H = silu(X . Wg^T) * (X . Wu^T) (jq4k_gemm_swiglu); Wg and Wu alike."""
+    M, N, K = _shapes(Wg, X, H)
+    if Wu.shape != Wg.shape:
+        raise ValueError("gate and up matrices differ in shape")
+    _check(_load().jq4k_gemm_swiglu(Wg.data_ptr(), Wu.data_ptr(), X.data_ptr(), H.data_ptr(),
+                                    M, N, K, _stream(stream)), "jq4k_gemm_swiglu")
+    return H
 
 
 def _nblocks(W):

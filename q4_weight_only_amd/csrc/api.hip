@@ -19,6 +19,11 @@ hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, f
                             const int* M, const int* N, const int* K, int count, int tile,
                             hipStream_t stream);
 long gemm_launch_size(const int* M, const int* N, int count, int tile);
+hipError_t launch_gemm_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
+                              int M, int N, int K, hipStream_t stream);
+long gemm_swiglu_launch_size(int M, int N);
+hipError_t launch_gemv_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
+                              int N, int K, int R, hipStream_t stream);
 
 hipError_t launch_unpack_fields(const uint8_t* W, long nblocks, uint8_t* q, uint8_t* sc,
                                 uint8_t* m, hipStream_t stream);
@@ -216,6 +221,27 @@ int jq4k_gemm_batched(const jq4k_gemm_desc* problems, int count, hipStream_t str
     const int tile = mfma_tile_for(max_m, true);
     if (jq4k::gemm_launch_size(M, N, live, tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
     return static_cast<int>(jq4k::launch_gemm_mfma(W, X, Y, M, N, K, live, tile, stream));
+}
+
+int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16* X, float* H,
+                     int M, int N, int K, hipStream_t stream) {
+    const int rc = check_matmul(Wg, X, H, M, N, K);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    if (Wu == nullptr) return JQ4K_EINVAL;
+    if (misaligned(Wu, 16)) return JQ4K_EALIGN;
+    const uint8_t* wg = reinterpret_cast<const uint8_t*>(Wg);
+    const uint8_t* wu = reinterpret_cast<const uint8_t*>(Wu);
+    if (M == 1 && K <= JQ4K_GEMV_MAX_K) {
+        // R rows of each matrix per workgroup: half the single GEMV's, so a
+        // workgroup streams about as many blocks; both sets of partials fit
+        const int nb = K / jq4k::kQK;
+        int R = (gemv_rows_per_block(N, K) + 1) / 2;
+        while (R > 1 && jq4k::gemv_lds_bytes(nb, 2 * R) > kGemvLdsLimit) --R;
+        return static_cast<int>(jq4k::launch_gemv_swiglu(wg, wu, X, H, N, K, R, stream));
+    }
+    if (K > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
+    if (jq4k::gemm_swiglu_launch_size(M, N) > 0x7FFFFFFFL) return JQ4K_EINVAL;
+    return static_cast<int>(jq4k::launch_gemm_swiglu(wg, wu, X, H, M, N, K, stream));
 }
 
 int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,

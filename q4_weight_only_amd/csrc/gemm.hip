@@ -60,12 +60,21 @@ struct GemmCfg {
 
 // One BM x BN tile of Y = X . W^T, rows m0.. and columns n0.. (the whole
 // K loop and the epilogue), computed by the 256 threads of a workgroup.
-template <int BM, int BN, int WM, int WN>
+//
+// kPair (SwiGLU of a gate/up pair, H = silu(X.Wg^T) * (X.Wu^T)): the tile's
+// BN rows of W are BN/2 rows of W (gate) and the same BN/2 rows of W2 (up),
+// interleaved in runs of 32 so that k-tile 2j of every wave holds gate
+// columns and k-tile 2j+1 the matching up columns: tile row wr is row
+// n0 + 32 (wr / 64) + wr % 32 of W if (wr / 32) is even, of W2 if odd, and
+// the tile writes BN/2 columns of H from column n0 (each wave 64 wide).
+template <int BM, int BN, int WM, int WN, bool kPair>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
+                                          const uint8_t* __restrict__ W2,
                                           const uint16_t* __restrict__ X, float* __restrict__ Y,
                                           int M, int N, int K, int n0, int m0, uint32_t qmask,
                                           uint4 (*lds)[GemmCfg<BM, BN, WM, WN>::kLdsChunks]) {
     using C = GemmCfg<BM, BN, WM, WN>;
+    static_assert(!kPair || C::kWaveN == 64, "pairs need 64-wide wave tiles");
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -77,7 +86,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
     const int qoff = (t % C::kThreadsPerRow) * C::kQBytes;
     // rows past N are clamped to row N-1: they only feed output columns that
     // are never stored
-    const uint8_t* wrow = W + static_cast<long>(min(n0 + wr, N - 1)) * nb * kBlockBytes;
+    const int wn_row = kPair ? n0 + 32 * (wr >> 6) + (wr & 31) : n0 + wr;
+    const uint8_t* wsrc = kPair && ((wr >> 5) & 1) ? W2 : W;
+    const uint8_t* wrow = wsrc + static_cast<long>(min(wn_row, N - 1)) * nb * kBlockBytes;
 
     // ---- X slab assignment: chunk g = t + 256 j -> row g / 8, chunk g % 8.
     // X is read through a buffer resource over rows m0 .. m0 + BM - 1 (only
@@ -208,6 +219,24 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
     }
 
     // ---- epilogue: fp32 Y, row-major
+    if constexpr (kPair) {
+        // k-tiles (2j, 2j + 1) are the gate and up columns of the same rows
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i) {
+#pragma unroll
+            for (int j = 0; j < C::kTN; j += 2) {   // kTN == 2: one pair
+                const int n = n0 + wn * 32 + (lane & 31);
+                if (n >= N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m =
+                        m0 + wm * C::kWaveM + 32 * i + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                    if (m < M) Y[static_cast<long>(m) * N + n] = silu(acc[i][j][r]) * acc[i][j + 1][r];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < C::kTM; ++i) {
 #pragma unroll
@@ -223,15 +252,17 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ W,
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool kPair>
 __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(const GemmBatch batch,
                                                                      uint32_t qmask) {
     using C = GemmCfg<BM, BN, WM, WN>;
     __shared__ uint4 lds[2][C::kLdsChunks];
+    constexpr int kOutN = kPair ? BN / 2 : BN;   // output columns per tile
     int q, tm, tn;
     if (!tile_sched_next(batch.s, blockIdx.x, &q, &tm, &tn)) return;
     const GemmProblem& pr = batch.p[q];
-    gemm_tile<BM, BN, WM, WN>(pr.W, pr.X, pr.Y, pr.M, pr.N, pr.K, tn * BN, tm * BM, qmask, lds);
+    gemm_tile<BM, BN, WM, WN, kPair>(pr.W, pr.W2, pr.X, pr.Y, pr.M, pr.N, pr.K, tn * kOutN,
+                                     tm * BM, qmask, lds);
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -240,14 +271,45 @@ static hipError_t launch_cfg(const uint8_t* const* W, const uint16_t* const* X, 
                              hipStream_t stream) {
     GemmBatch b;
     const long grid = gemm_batch_init(b, W, X, Y, M, N, K, count, BM, BN);
-    hipLaunchKernelGGL((q4k_gemm_mfma_kernel<BM, BN, WM, WN>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kGemmThreads), 0, stream, b, kNibbleMask);
+    hipLaunchKernelGGL((q4k_gemm_mfma_kernel<BM, BN, WM, WN, false>),
+                       dim3(static_cast<unsigned>(grid)), dim3(kGemmThreads), 0, stream, b,
+                       kNibbleMask);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_pair_cfg(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X,
+                                  float* H, int M, int N, int K, hipStream_t stream) {
+    GemmBatch b;
+    const long grid = gemm_batch_init(b, &Wg, &X, &H, &M, &N, &K, 1, BM, BN / 2);
+    b.p[0].W2 = Wu;
+    hipLaunchKernelGGL((q4k_gemm_mfma_kernel<BM, BN, WM, WN, true>),
+                       dim3(static_cast<unsigned>(grid)), dim3(kGemmThreads), 0, stream, b,
+                       kNibbleMask);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_ws(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
                           const int* M, const int* N, const int* K, int count,
                           hipStream_t stream);
+
+hipError_t launch_gemm_ws_pair(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
+                               int M, int N, int K, hipStream_t stream);
+
+// SwiGLU of a gate/up pair, H = silu(X.Wg^T) * (X.Wu^T): 64 x 128 tiles (64
+// outputs) at M <= 64, 128 x 128 below M = 2048, else the 256-row kernel.
+hipError_t launch_gemm_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
+                              int M, int N, int K, hipStream_t stream) {
+    if (M <= 64) return launch_pair_cfg<64, 128, 2, 2>(Wg, Wu, X, H, M, N, K, stream);
+    if (M < 2048) return launch_pair_cfg<128, 128, 2, 2>(Wg, Wu, X, H, M, N, K, stream);
+    return launch_gemm_ws_pair(Wg, Wu, X, H, M, N, K, stream);
+}
+
+// Workgroups a SwiGLU launch takes (the largest of its tile choices).
+long gemm_swiglu_launch_size(int M, int N) {
+    TileSched s;
+    return tile_sched_init(s, &M, &N, 1, 64, 64, 1);
+}
 
 // Workgroups a launch of these problems takes (tiles plus at most seven idle
 // workgroups per problem).

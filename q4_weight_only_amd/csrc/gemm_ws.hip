@@ -44,6 +44,12 @@ struct WsRegs {
 
 }  // namespace
 
+// kPair: SwiGLU of a gate/up pair, with the tile layout of gemm_tile's
+// kPair (gemm.hip): tile row wr is row n0 + 32 (wr / 64) + wr % 32 of the
+// gate (W) or the up matrix (W2) as (wr / 32) is even or odd; each consumer
+// wave's two 32-column k-tiles are then the gate and up columns of the same
+// 32 outputs, and the tile writes 64 columns of H = silu(gate) * up.
+template <bool kPair>
 __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch batch,
                                                                  uint32_t qmask) {
     __shared__ uint4 lds[2][kWsLdsChunks];
@@ -58,7 +64,7 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
     const uint16_t* __restrict__ X = pr.X;
     float* __restrict__ Y = pr.Y;
     const int M = pr.M, N = pr.N, K = pr.K;
-    const int n0 = tn * kWsBN, m0 = tm * kWsBM;
+    const int n0 = tn * (kPair ? kWsBN / 2 : kWsBN), m0 = tm * kWsBM;
     const int nb = K / kQK;
     const int nstage = K / kWsBK;  // a multiple of 4
     auto last = [&](int s) { return min(s, nstage - 1); };
@@ -71,7 +77,9 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
         const int wr = pt >> 1, qoff = (pt & 1) * 16;  // W row of the tile, quant byte offset
         // Rows past N (or M) are clamped to the last row: they only feed
         // outputs that are never stored.
-        const uint8_t* wrow = W + static_cast<long>(min(n0 + wr, N - 1)) * nb * kBlockBytes;
+        const int wn_row = kPair ? n0 + 32 * (wr >> 6) + (wr & 31) : n0 + wr;
+        const uint8_t* wsrc = kPair && ((wr >> 5) & 1) ? pr.W2 : W;
+        const uint8_t* wrow = wsrc + static_cast<long>(min(wn_row, N - 1)) * nb * kBlockBytes;
         // X through a buffer resource over rows m0 .. m0 + BM - 1 below M
         // (zeros past the end; the loads stay in registers until stored)
         const long xrows = min(static_cast<long>(kWsBM), static_cast<long>(M - m0));
@@ -184,6 +192,20 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
         half(lds[0], lds[1]);
         half(lds[1], lds[0]);
     }
+    if constexpr (kPair) {
+        static_assert(kWsTN == 2, "one gate/up pair of k-tiles per consumer wave");
+        const int n = n0 + wn * 32 + (lane & 31);
+        if (n >= N) return;
+#pragma unroll
+        for (int i = 0; i < kWsTM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                if (m < M) Y[static_cast<long>(m) * N + n] = silu(acc[i][0][r]) * acc[i][1][r];
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kWsTM; ++i) {
 #pragma unroll
@@ -204,8 +226,18 @@ hipError_t launch_gemm_ws(const uint8_t* const* W, const uint16_t* const* X, flo
                           hipStream_t stream) {
     GemmBatch b;
     const long grid = gemm_batch_init(b, W, X, Y, M, N, K, count, kWsBM, kWsBN);
-    hipLaunchKernelGGL(q4k_gemm_ws_kernel, dim3(static_cast<unsigned>(grid)), dim3(kWsThreads),
-                       0, stream, b, kNibbleMask);
+    hipLaunchKernelGGL(q4k_gemm_ws_kernel<false>, dim3(static_cast<unsigned>(grid)),
+                       dim3(kWsThreads), 0, stream, b, kNibbleMask);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_ws_pair(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
+                               int M, int N, int K, hipStream_t stream) {
+    GemmBatch b;
+    const long grid = gemm_batch_init(b, &Wg, &X, &H, &M, &N, &K, 1, kWsBM, kWsBN / 2);
+    b.p[0].W2 = Wu;
+    hipLaunchKernelGGL(q4k_gemm_ws_kernel<true>, dim3(static_cast<unsigned>(grid)),
+                       dim3(kWsThreads), 0, stream, b, kNibbleMask);
     return hipGetLastError();
 }
 

@@ -122,13 +122,19 @@ __device__ __forceinline__ float quarter_dot(const QuarterLoad& ld, int c, const
 }
 
 // LDS: x chunks (nb*36 x 16 B), per-sub-block sums X_s (nb*8 floats, as a
-// float2 (even, odd) per (kb, quarter)), per-block partials (R*nb floats).
+// float2 (even, odd) per (kb, quarter)), per-block partials (R*nb floats per
+// matrix).
 constexpr int kGemvDepth = 2;  // quarter tasks in flight per thread (2 measured best: 74 VGPRs, 6 waves per SIMD)
 constexpr int kGemvMaxK = 16384;
 constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
 
 // One workgroup's share of a GEMV: rows [tile * R, tile * R + R) of W.
+// kPair: the same rows of a second matrix W2 follow in the task list (the
+// gate and up projections of an MLP), and the row's output is
+// silu(gate) * up (SwiGLU) instead of the dot product.
+template <bool kPair>
 __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
+                                          const uint8_t* __restrict__ W2,
                                           const uint4* __restrict__ X, float* __restrict__ Y,
                                           int N, int nb, int R, long tile, uint4* smem) {
     uint4* xs = smem;
@@ -139,8 +145,15 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     const int c = t & 3;
     const long row0 = tile * R;
     const int rows = static_cast<int>(min(static_cast<long>(R), N - row0));
-    const int ntask = rows * nb * 4;
+    const int nblk = rows * nb;                       // blocks per matrix
+    const int ntask = (kPair ? 2 : 1) * nblk * 4;
     const uint8_t* Wt = W + row0 * nb * kBlockBytes;
+    const uint8_t* Wt2 = kPair ? W2 + row0 * nb * kBlockBytes : nullptr;
+    // block b of the task list: W's span, then (kPair) W2's
+    auto blk_ptr = [&](int b) {
+        if (kPair && b >= nblk) return Wt2 + static_cast<long>(b - nblk) * kBlockBytes;
+        return Wt + static_cast<long>(b) * kBlockBytes;
+    };
     const int b0 = t >> 2;  // this thread's first block; +64 per round
 
     // Memory requests in the order they are needed (vmcnt retires in order):
@@ -156,7 +169,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     for (int u = 0; u < kGemvDepth; ++u) {
         ld[u] = {};
         if (t + u * kGemvThreads < ntask)
-            ld[u] = load_quarter(Wt + static_cast<long>(b0 + 64 * u) * kBlockBytes, c);
+            ld[u] = load_quarter(blk_ptr(b0 + 64 * u), c);
     }
 
     // Stage x; each quad of lanes holds one half sub-block (4 chunks of 8),
@@ -188,8 +201,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
                 p = quad_sum(p);
                 if (c == 0) part[b] = p;
                 if (tau + kGemvDepth * kGemvThreads < ntask)
-                    ld[u] = load_quarter(Wt + static_cast<long>(b + 64 * kGemvDepth) * kBlockBytes,
-                                         c);
+                    ld[u] = load_quarter(blk_ptr(b + 64 * kGemvDepth), c);
             }
             kb += kb_step;
             if (kb >= nb) kb -= nb;
@@ -199,6 +211,11 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     for (int r = t; r < rows; r += kGemvThreads) {
         float s = 0.f;
         for (int j = 0; j < nb; ++j) s += part[r * nb + j];
+        if constexpr (kPair) {
+            float u = 0.f;
+            for (int j = 0; j < nb; ++j) u += part[nblk + r * nb + j];
+            s = silu(s) * u;
+        }
         Y[row0 + r] = s;
     }
 }
@@ -207,7 +224,15 @@ __global__ __launch_bounds__(kGemvThreads) void q4k_gemv_kernel(
     const uint8_t* __restrict__ W, const uint4* __restrict__ X, float* __restrict__ Y,
     int N, int nb, int R) {
     extern __shared__ uint4 smem[];
-    gemv_tile(W, X, Y, N, nb, R, blockIdx.x, smem);
+    gemv_tile<false>(W, nullptr, X, Y, N, nb, R, blockIdx.x, smem);
+}
+
+// SwiGLU of a gate/up pair at M = 1: H[n] = silu(Wg[n] . x) * (Wu[n] . x).
+__global__ __launch_bounds__(kGemvThreads) void q4k_gemv_swiglu_kernel(
+    const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu, const uint4* __restrict__ X,
+    float* __restrict__ H, int N, int nb, int R) {
+    extern __shared__ uint4 smem[];
+    gemv_tile<true>(Wg, Wu, X, H, N, nb, R, blockIdx.x, smem);
 }
 
 // Several independent GEMVs in one launch: workgroups [first[p], first[p+1])
@@ -231,7 +256,7 @@ __global__ __launch_bounds__(kGemvThreads) void q4k_gemv_batched_kernel(const Ge
     int p = 0;
     while (p + 1 < batch.count && wg >= batch.first[p + 1]) ++p;
     const GemvProblem& pr = batch.p[p];
-    gemv_tile(pr.W, pr.X, pr.Y, pr.N, pr.nb, pr.R, wg - batch.first[p], smem);
+    gemv_tile<false>(pr.W, nullptr, pr.X, pr.Y, pr.N, pr.nb, pr.R, wg - batch.first[p], smem);
 }
 
 hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X,
@@ -256,6 +281,18 @@ hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X
 size_t gemv_lds_bytes(int nb, int R) {
     return static_cast<size_t>(nb) * 4 * kXGroupStride * 16 + static_cast<size_t>(nb) * 4 * 8 +
            static_cast<size_t>(R) * nb * 4;
+}
+
+// R rows of each matrix per workgroup; the partials of both sit in LDS
+// (gemv_lds_bytes(nb, 2 R)).
+hipError_t launch_gemv_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
+                              int N, int K, int R, hipStream_t stream) {
+    const int nb = K / kQK;
+    const unsigned grid = static_cast<unsigned>((static_cast<long>(N) + R - 1) / R);
+    hipLaunchKernelGGL(q4k_gemv_swiglu_kernel, dim3(grid), dim3(kGemvThreads),
+                       gemv_lds_bytes(nb, 2 * R), stream, Wg, Wu,
+                       reinterpret_cast<const uint4*>(X), H, N, nb, R);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv(const uint8_t* W, const uint16_t* X, float* Y, int N, int K, int R,

@@ -140,4 +140,14 @@ __device__ __forceinline__ void dequant_dword_bf16(uint32_t v, const QuarterScal
     hi2[1] = pack_bf16x2(hi[2], hi[3]);
 }
 
+// silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), fp32 (the SwiGLU epilogues),
+// on the hardware's base-2 exponential and reciprocal (v_exp_f32, v_rcp_f32;
+// about 1 ulp each): exp(-z) = 2^(-z log2 e).  For very negative z the
+// exponential overflows to inf and the reciprocal to 0, giving the limit -0;
+// for large z it gives z.
+__device__ __forceinline__ float silu(float z) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
 }  // namespace jq4k

@@ -82,6 +82,7 @@ struct GemmProblem {
     const uint16_t* X;
     float* Y;
     int M, N, K;
+    const uint8_t* W2;   // up matrix of a SwiGLU pair (W is the gate), else null
 };
 
 struct GemmBatch {
@@ -111,7 +112,7 @@ inline long gemm_batch_init(GemmBatch& b, const uint8_t* const* W, const uint16_
     int Ms[kSchedMax], Ns[kSchedMax];
     for (int i = 0; i < count; ++i) {
         const int o = order[i];
-        b.p[i] = {W[o], X[o], Y[o], M[o], N[o], K[o]};
+        b.p[i] = {W[o], X[o], Y[o], M[o], N[o], K[o], nullptr};
         Ms[i] = M[o];
         Ns[i] = N[o];
     }

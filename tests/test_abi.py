@@ -11,6 +11,7 @@ import q4_weight_only_amd as jq4k
 ALIGNED = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced
 ALIGNED2 = 0x20000
 ALIGNED3 = 0x30000
+ALIGNED4 = 0x40000
 
 
 @pytest.fixture(scope="module")
@@ -185,3 +186,16 @@ def test_gemm_batched_argument_checks(L):
         assert f(ctypes.addressof(descs(good, bad)), 2, None) == code, bad
     empty = descs((0, 0, 0, 0, 8, 256), (0, 0, 0, 5, 0, 512))
     assert f(ctypes.addressof(empty), 2, None) == jq4k.OK
+
+
+def test_gemm_swiglu_argument_checks(L):
+    f = L.jq4k_gemm_swiglu
+    A, B, C, D = ALIGNED, ALIGNED2, ALIGNED3, ALIGNED4
+    assert f(A, B, C, D, 4, 8, 300, None) == jq4k.EINVAL          # K not a multiple of 256
+    assert f(A, B, C, D, -1, 8, 256, None) == jq4k.EINVAL
+    assert f(A, 0, C, D, 4, 8, 256, None) == jq4k.EINVAL           # no up matrix
+    assert f(A, B + 4, C, D, 4, 8, 256, None) == jq4k.EALIGN       # up misaligned
+    assert f(A + 4, B, C, D, 4, 8, 256, None) == jq4k.EALIGN
+    assert f(A, B, C, D, 4, 8, jq4k.MFMA_MAX_K + 256, None) == jq4k.EINVAL
+    assert f(0, 0, 0, 0, 0, 8, 256, None) == jq4k.OK               # M == 0
+    assert f(0, 0, 0, 0, 3, 0, 256, None) == jq4k.OK               # N == 0

@@ -329,3 +329,57 @@ def test_lm_head_sampled(gpu, M):
     Y, A = oracle.gemm(W[rows], X[ms], len(rows), K)
     parity(y[np.ix_(ms, rows)], Y, A, f"LM head M={M} sampled")
     assert np.all(np.isfinite(y))
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU of a gate/up pair (jq4k_gemm_swiglu)
+
+def _swiglu_check(gpu, Wg, Wu, X, N, K, what, rows=None, ms=None):
+    M = X.shape[0]
+    H = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    announce(f"swiglu {what} M={M} N={N} K={K}")
+    gpu.gemm_swiglu(dev(Wg), dev(Wu), dev(X).view(torch.bfloat16), H)
+    h = host(H)
+    assert np.all(np.isfinite(h)), what
+    rows = np.arange(N) if rows is None else rows
+    ms = np.arange(M) if ms is None else ms
+    Href, G, U, Ag, Au = oracle.gemm_swiglu(Wg[rows], Wu[rows], X[ms], len(rows), K)
+    tol = oracle.swiglu_tolerance(G, U, Ag, Au)
+    err = np.abs(h[np.ix_(ms, rows)].astype(np.float64) - Href)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} out of the SwiGLU bound"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1000, 512), (1, 300, 16384), (1, 77, 2560),
+                                   (2, 200, 512), (33, 130, 768), (64, 64, 256),
+                                   (65, 300, 512), (300, 129, 1024)])
+def test_swiglu_ragged(gpu, M, N, K):
+    g = np.random.default_rng(300 + M + N)
+    Wg, Wu = qi.weight_bytes(g, N, K), qi.weight_bytes(g, N, K)
+    _swiglu_check(gpu, Wg, Wu, qi.activations(g, M, K), N, K, "ragged")
+
+
+def test_swiglu_decode_gate_up(gpu):
+    """The decode layer's gate and up projections (9728 x 2560) at M = 1."""
+    layer = qi.decode_layer(1, 0, 1)
+    (_, N, K, Wg, X), (_, _, _, Wu, _) = layer[4], layer[5]
+    _swiglu_check(gpu, Wg, Wu, X, N, K, "decode gate|up")
+
+
+@pytest.mark.parametrize("M", [33, 2048])
+def test_swiglu_prefill_gate_up_sampled(gpu, M):
+    """gate|up of a layer at M = 33 (the 64-row tiles) and M = 2048 (the
+    256-row kernel), sampled rows and tokens."""
+    seed = 2 if M == 33 else 3
+    _, N, K, Wg, X = qi.prefill_projection(seed, 0, 4, M)
+    _, _, _, Wu, _ = qi.prefill_projection(seed, 0, 5, M)
+    g = np.random.default_rng(310 + M)
+    rows = np.sort(g.choice(N, 64, replace=False))
+    ms = np.sort(g.choice(M, min(M, 24), replace=False))
+    _swiglu_check(gpu, Wg, Wu, X, N, K, "prefill gate|up", rows, ms)
+
+
+def test_swiglu_quick_returns(gpu):
+    """M == 0 or N == 0: nothing is launched, whatever the pointers."""
+    assert gpu.raw().jq4k_gemm_swiglu(0, 0, 0, 0, 0, 5, 256, None) == 0
+    assert gpu.raw().jq4k_gemm_swiglu(0, 0, 0, 0, 7, 0, 256, None) == 0
