@@ -188,3 +188,42 @@ def swiglu_tolerance(G, U, Ag, Au):
     tg, tu = tolerance(Ag), tolerance(Au)
     sg = np.abs(silu(G))
     return SILU_LIPSCHITZ * tg * (np.abs(U) + tu) + sg * tu + 1e-6 * sg * np.abs(U)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm of the activations ahead of a projection (the genie-ai-runtime
+# README, "At a glance": fused RMSNorm + RoPE + SwiGLU kernels; the pages do
+# not define it, and the reading taken is Qwen3's: x_hat = x / sqrt(mean(x^2)
+# + eps) * gamma over the K inputs, stored as bf16 before the matmul, as an
+# engine that keeps activations in bf16 would).
+
+def bf16_to_f64(b):
+    """bf16 bit patterns -> fp64 (exact): the 16 bits are the top half of a
+    binary32."""
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def rmsnorm_f64(X_bf16, gamma_bf16, eps: float):
+    """x / sqrt(mean(x^2) + eps) * gamma per row, fp64 (rows of X)."""
+    X = bf16_to_f64(X_bf16)
+    g = bf16_to_f64(gamma_bf16)
+    if X.ndim == 1:
+        X = X.reshape(1, -1)
+    r = 1.0 / np.sqrt(np.mean(X * X, axis=1, keepdims=True) + eps)
+    return X * r * g
+
+
+def rmsnorm_bf16(X_bf16, gamma_bf16, eps: float):
+    """The normalised activations as bf16 bits: the fp64 value rounded to
+    fp32, then to bf16 (round to nearest even)."""
+    Xh = rmsnorm_f64(X_bf16, gamma_bf16, eps).astype(np.float32)
+    return float_to_bf16_rne(Xh).reshape(Xh.shape)
+
+
+def gemm_rmsnorm(W, X_bf16, gamma_bf16, eps: float, N: int, K: int):
+    """Y = rmsnorm(X).W^T: the oracle contraction of the bf16 normalised
+    activations; returns (Y, A, X_hat_bf16)."""
+    Xh = rmsnorm_bf16(X_bf16, gamma_bf16, eps)
+    Y, A = gemm(W, Xh, N, K)
+    return Y, A, Xh

@@ -437,3 +437,41 @@ def test_swiglu_bound_holds_for_perturbed_inputs_and_rejects_mistakes():
                   oracle.silu(np.roll(G, 1, axis=1)) * U):   # gate of the neighbouring row
         bad = np.abs(wrong - H) > tol
         assert bad.mean() > 0.25, bad.mean()
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm ahead of a projection
+
+def test_rmsnorm_library_and_invariants():
+    import torch
+    g = np.random.default_rng(400)
+    K = 2560
+    X = qi.activations(g, 3, K)
+    gamma = qi.f32_to_bf16_bits((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    eps = 1e-6
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(oracle.bf16_to_f64(X)), (K,),
+                                       weight=torch.from_numpy(oracle.bf16_to_f64(gamma)),
+                                       eps=eps).numpy()
+    assert np.allclose(oracle.rmsnorm_f64(X, gamma, eps), ref, rtol=1e-14, atol=0)
+    # scale invariance (eps = 0): a power-of-two scaling of x cancels exactly
+    X2 = qi.f32_to_bf16_bits((qi.bf16_bits_to_f32(X) * 4.0).astype(np.float32))
+    assert np.array_equal(oracle.rmsnorm_f64(X2, gamma, 0.0), oracle.rmsnorm_f64(X, gamma, 0.0))
+    # constant row c: x_hat = gamma * c / sqrt(c^2 + eps)
+    c = np.full((1, K), qi.f32_to_bf16_bits(np.float32(-0.75)), dtype=np.uint16)
+    want = oracle.bf16_to_f64(gamma) * (-0.75 / np.sqrt(0.5625 + eps))
+    assert np.allclose(oracle.rmsnorm_f64(c, gamma, eps)[0], want, rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_bf16_rounding_and_contraction():
+    g = np.random.default_rng(401)
+    N, K = 24, 512
+    W = qi.weight_bytes(g, N, K)
+    X = qi.activations(g, 2, K)
+    gamma = qi.f32_to_bf16_bits((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    Y, A, Xh = oracle.gemm_rmsnorm(W, X, gamma, 1e-6, N, K)
+    f = oracle.rmsnorm_f64(X, gamma, 1e-6)
+    # x_hat is the nearest bf16 to the fp32 rounding of the exact value
+    back = oracle.bf16_to_f64(Xh)
+    assert np.all(np.abs(back - f) <= np.abs(f) * 2.0 ** -8 + 1e-300)
+    Y2, A2 = oracle.gemm(W, Xh, N, K)
+    assert np.array_equal(Y, Y2) and np.array_equal(A, A2)
