@@ -375,6 +375,39 @@ def swiglu_leg(torch, jq4k, args):
     return out
 
 
+def rmsnorm_leg(torch, jq4k, args):
+    """The decode gate projection (9728 x 2560) with its RMSNorm fused into the
+    x staging (jq4k_gemv_rmsnorm), beside the plain GEMV of the same matrix;
+    weights rotate over copies like the decode leg."""
+    layer = qi.decode_layer(1, 0, 1)
+    _, N, K, W, X = layer[4]
+    g = qi.rng(7)
+    gamma = qi.f32_to_bf16_bits((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    copies = max(2, math.ceil(ROTATION_BYTES / W.nbytes))
+    Ws = [torch.from_numpy(W).to("cuda:0")]
+    Ws += [Ws[0].clone() for _ in range(copies - 1)]
+    Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+    Gd = torch.from_numpy(gamma.view(np.int16)).to("cuda:0")
+    Y = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    L = jq4k.raw()
+
+    def fused(i):
+        rc = L.jq4k_gemv_rmsnorm(Ws[i % copies].data_ptr(), Xd.data_ptr(), Gd.data_ptr(), 1e-6,
+                                 Y.data_ptr(), N, K, torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+
+    def plain(i):
+        rc = L.jq4k_gemv(Ws[i % copies].data_ptr(), Xd.data_ptr(), Y.data_ptr(), 1, N, K,
+                         torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+    tf = timed(torch, fused, args.steps, 4, not args.eager) / args.steps
+    tp = timed(torch, plain, args.steps, 4, not args.eager) / args.steps
+    return {"N": N, "K": K, "fused_us": round(tf * 1e6, 2),
+            "fused_GB_s": round(W.nbytes / tf / 1e9, 1), "plain_gemv_us": round(tp * 1e6, 2)}
+
+
 def profile_run(torch, jq4k):
     """Launches for rocprofv3 runs: a 512 MiB device copy (the reference for
     scaling FETCH_SIZE / WRITE_SIZE), then 20 batched decode-layer GEMVs, 20
@@ -494,6 +527,7 @@ def main():
     m33 = prefill_m33_leg(torch, jq4k, args)
     lm512 = lm_head_m512_leg(torch, jq4k, args)
     swiglu = swiglu_leg(torch, jq4k, args)
+    rmsnorm = rmsnorm_leg(torch, jq4k, args)
     tflops = flops * args.prefill_steps / psecs / 1e12
 
     out = {
@@ -548,6 +582,7 @@ def main():
         "prefill_m33_36_layers": m33,
         "lm_head_m512": lm512,
         "swiglu_gate_up": swiglu,
+        "rmsnorm_gate_m1": rmsnorm,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layer)

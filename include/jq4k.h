@@ -164,6 +164,19 @@ typedef struct {
  * then. */
 int jq4k_gemm_batched(const jq4k_gemm_desc *problems, int count, hipStream_t stream);
 
+/* Decode GEMV with the RMSNorm of x fused into its staging (the
+ * genie-ai-runtime README, "At a glance": fused RMSNorm + RoPE + SwiGLU;
+ * Qwen3's RMSNorm ahead of a projection):
+ *   x_hat[k] = bf16(x[k] / sqrt(mean_k(x^2) + eps) * gamma[k]),  Y = W . x_hat.
+ * x_hat is rounded to bf16 (nearest even) as an activation stored between
+ * the two steps would be; the sum of squares is reduced in fp32 in a fixed
+ * order.  X and gamma: K bf16 each, 16-byte aligned.  Errors: JQ4K_EINVAL
+ * for eps < 0, eps infinite or NaN, a null gamma, or what jq4k_gemv rejects
+ * with M = 1; JQ4K_EALIGN for a misaligned gamma or as jq4k_gemv.  N == 0
+ * returns 0 without launching. */
+int jq4k_gemv_rmsnorm(const block_q4_K *W, const jq4k_bf16 *X, const jq4k_bf16 *gamma,
+                      float eps, float *Y, int N, int K, hipStream_t stream);
+
 /* SwiGLU of a gate/up projection pair, one launch for any M >= 0:
  * H (M x N) = silu(X . Wg^T) * (X . Wu^T), elementwise, silu(z) = z / (1 +
  * exp(-z)) (the genie-ai-runtime README, "At a glance": fused RMSNorm + RoPE

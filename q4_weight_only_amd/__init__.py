@@ -75,6 +75,8 @@ def _load():
         L.jq4k_gemm_path.argtypes = [vp, vp, vp, i, i, i, i, vp]
         L.jq4k_gemm_swiglu.argtypes = [vp, vp, vp, vp, i, i, i, vp]
         L.jq4k_gemm_swiglu.restype = i
+        L.jq4k_gemv_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_float, vp, i, i, vp]
+        L.jq4k_gemv_rmsnorm.restype = i
         L.jq4k_gemm_path.restype = i
         L.jq4k_unpack_fields.argtypes = [vp, l, vp, vp, vp, vp]
         L.jq4k_unpack_fields.restype = i
@@ -193,6 +195,16 @@ def gemm(W, X, Y, stream=None, path=PATH_AUTO):
         rc = L.jq4k_gemm_path(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K, int(path),
                               _stream(stream))
     _check(rc, "jq4k_gemm")
+    return Y
+
+
+def gemv_rmsnorm(W, X, gamma, eps, Y, stream=None):
+    """Y = W . bf16(rmsnorm(x) * gamma) at M = 1 (jq4k_gemv_rmsnorm)."""
+    M, N, K = _shapes(W, X, Y)
+    if M != 1 or gamma.numel() != K:
+        raise ValueError("gemv_rmsnorm takes one token and K gamma values")
+    _check(_load().jq4k_gemv_rmsnorm(W.data_ptr(), X.data_ptr(), gamma.data_ptr(), float(eps),
+                                     Y.data_ptr(), N, K, _stream(stream)), "jq4k_gemv_rmsnorm")
     return Y
 
 

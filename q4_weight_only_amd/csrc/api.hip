@@ -22,6 +22,8 @@ long gemm_launch_size(const int* M, const int* N, int count, int tile);
 hipError_t launch_gemm_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
                               int M, int N, int K, hipStream_t stream);
 long gemm_swiglu_launch_size(int M, int N);
+hipError_t launch_gemv_rmsnorm(const uint8_t* W, const uint16_t* X, const uint16_t* gamma,
+                               float eps, float* Y, int N, int K, int R, hipStream_t stream);
 hipError_t launch_gemv_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
                               int N, int K, int R, hipStream_t stream);
 
@@ -221,6 +223,18 @@ int jq4k_gemm_batched(const jq4k_gemm_desc* problems, int count, hipStream_t str
     const int tile = mfma_tile_for(max_m, true);
     if (jq4k::gemm_launch_size(M, N, live, tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
     return static_cast<int>(jq4k::launch_gemm_mfma(W, X, Y, M, N, K, live, tile, stream));
+}
+
+int jq4k_gemv_rmsnorm(const block_q4_K* W, const jq4k_bf16* X, const jq4k_bf16* gamma,
+                      float eps, float* Y, int N, int K, hipStream_t stream) {
+    if (K > JQ4K_GEMV_MAX_K || !(eps >= 0.0f) || eps == __builtin_inff()) return JQ4K_EINVAL;
+    const int rc = check_matmul(W, X, Y, 1, N, K);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    if (gamma == nullptr) return JQ4K_EINVAL;
+    if (misaligned(gamma, 16)) return JQ4K_EALIGN;
+    const int R = gemv_rows_per_block(N, K);
+    return static_cast<int>(jq4k::launch_gemv_rmsnorm(reinterpret_cast<const uint8_t*>(W), X,
+                                                      gamma, eps, Y, N, K, R, stream));
 }
 
 int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16* X, float* H,

@@ -132,11 +132,16 @@ constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
 // kPair: the same rows of a second matrix W2 follow in the task list (the
 // gate and up projections of an MLP), and the row's output is
 // silu(gate) * up (SwiGLU) instead of the dot product.
-template <bool kPair>
+// kNorm: x is RMS-normalised while it is staged, x_hat = bf16(x / sqrt(
+// mean(x^2) + eps) * gamma) (RMSNorm ahead of the projection); the sum of
+// squares is reduced in a fixed order (lane butterfly, then the four waves).
+template <bool kPair, bool kNorm = false>
 __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
                                           const uint8_t* __restrict__ W2,
                                           const uint4* __restrict__ X, float* __restrict__ Y,
-                                          int N, int nb, int R, long tile, uint4* smem) {
+                                          int N, int nb, int R, long tile, uint4* smem,
+                                          const uint4* __restrict__ gamma = nullptr,
+                                          float eps = 0.f) {
     uint4* xs = smem;
     float2* xsum = reinterpret_cast<float2*>(xs + nb * 4 * kXGroupStride);
     float* part = reinterpret_cast<float*>(xsum + nb * 4);
@@ -161,15 +166,51 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     // x waits only for x and each round waits only for its own weights.
     const int nxc = nb * 32;  // 16-byte chunks of x, at most 2048 (K <= 16384)
     uint4 xv[kGemvMaxXChunksPerThread];
+    uint4 gv[kNorm ? kGemvMaxXChunksPerThread : 1];
 #pragma unroll
     for (int j = 0; j < kGemvMaxXChunksPerThread; ++j)
-        if (t + j * kGemvThreads < nxc) xv[j] = X[t + j * kGemvThreads];
+        if (t + j * kGemvThreads < nxc) {
+            xv[j] = X[t + j * kGemvThreads];
+            if constexpr (kNorm) gv[j] = gamma[t + j * kGemvThreads];
+        }
     QuarterLoad ld[kGemvDepth];
 #pragma unroll
     for (int u = 0; u < kGemvDepth; ++u) {
         ld[u] = {};
         if (t + u * kGemvThreads < ntask)
             ld[u] = load_quarter(blk_ptr(b0 + 64 * u), c);
+    }
+
+    if constexpr (kNorm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < kGemvMaxXChunksPerThread; ++j)
+            if (t + j * kGemvThreads < nxc) {
+                const uint4 v = xv[j];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ss += bf16_lo(w[e]) * bf16_lo(w[e]) + bf16_hi(w[e]) * bf16_hi(w[e]);
+            }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        __shared__ float wave_ss[kGemvThreads / 64];
+        if ((t & 63) == 0) wave_ss[t >> 6] = ss;
+        __syncthreads();
+        const float total = (wave_ss[0] + wave_ss[1]) + (wave_ss[2] + wave_ss[3]);
+        const float r = rsqrtf(total / static_cast<float>(nb * kQK) + eps);
+#pragma unroll
+        for (int j = 0; j < kGemvMaxXChunksPerThread; ++j)
+            if (t + j * kGemvThreads < nxc) {
+                const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+                const uint32_t q[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = pack_bf16x2(bf16_lo(w[e]) * r * bf16_lo(q[e]),
+                                       bf16_hi(w[e]) * r * bf16_hi(q[e]));
+                xv[j] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
     }
 
     // Stage x; each quad of lanes holds one half sub-block (4 chunks of 8),
@@ -227,6 +268,14 @@ __global__ __launch_bounds__(kGemvThreads) void q4k_gemv_kernel(
     gemv_tile<false>(W, nullptr, X, Y, N, nb, R, blockIdx.x, smem);
 }
 
+// RMSNorm ahead of the projection at M = 1: Y = W . x_hat.
+__global__ __launch_bounds__(kGemvThreads) void q4k_gemv_rmsnorm_kernel(
+    const uint8_t* __restrict__ W, const uint4* __restrict__ X, const uint4* __restrict__ gamma,
+    float eps, float* __restrict__ Y, int N, int nb, int R) {
+    extern __shared__ uint4 smem[];
+    gemv_tile<false, true>(W, nullptr, X, Y, N, nb, R, blockIdx.x, smem, gamma, eps);
+}
+
 // SwiGLU of a gate/up pair at M = 1: H[n] = silu(Wg[n] . x) * (Wu[n] . x).
 __global__ __launch_bounds__(kGemvThreads) void q4k_gemv_swiglu_kernel(
     const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu, const uint4* __restrict__ X,
@@ -281,6 +330,16 @@ hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X
 size_t gemv_lds_bytes(int nb, int R) {
     return static_cast<size_t>(nb) * 4 * kXGroupStride * 16 + static_cast<size_t>(nb) * 4 * 8 +
            static_cast<size_t>(R) * nb * 4;
+}
+
+hipError_t launch_gemv_rmsnorm(const uint8_t* W, const uint16_t* X, const uint16_t* gamma,
+                               float eps, float* Y, int N, int K, int R, hipStream_t stream) {
+    const int nb = K / kQK;
+    const unsigned grid = static_cast<unsigned>((static_cast<long>(N) + R - 1) / R);
+    hipLaunchKernelGGL(q4k_gemv_rmsnorm_kernel, dim3(grid), dim3(kGemvThreads),
+                       gemv_lds_bytes(nb, R), stream, W, reinterpret_cast<const uint4*>(X),
+                       reinterpret_cast<const uint4*>(gamma), eps, Y, N, nb, R);
+    return hipGetLastError();
 }
 
 // R rows of each matrix per workgroup; the partials of both sit in LDS

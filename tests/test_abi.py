@@ -199,3 +199,16 @@ def test_gemm_swiglu_argument_checks(L):
     assert f(A, B, C, D, 4, 8, jq4k.MFMA_MAX_K + 256, None) == jq4k.EINVAL
     assert f(0, 0, 0, 0, 0, 8, 256, None) == jq4k.OK               # M == 0
     assert f(0, 0, 0, 0, 3, 0, 256, None) == jq4k.OK               # N == 0
+
+
+def test_gemv_rmsnorm_argument_checks(L):
+    f = L.jq4k_gemv_rmsnorm
+    A, B, C, D = ALIGNED, ALIGNED2, ALIGNED3, ALIGNED4
+    assert f(A, B, C, 1e-6, D, 8, 300, None) == jq4k.EINVAL        # K not a multiple of 256
+    assert f(A, B, C, -1.0, D, 8, 256, None) == jq4k.EINVAL        # eps < 0
+    assert f(A, B, C, float("nan"), D, 8, 256, None) == jq4k.EINVAL
+    assert f(A, B, C, float("inf"), D, 8, 256, None) == jq4k.EINVAL
+    assert f(A, B, 0, 1e-6, D, 8, 256, None) == jq4k.EINVAL        # no gamma
+    assert f(A, B, C + 4, 1e-6, D, 8, 256, None) == jq4k.EALIGN    # gamma misaligned
+    assert f(A, B, C, 1e-6, D, 8, jq4k.GEMV_MAX_K + 256, None) == jq4k.EINVAL
+    assert f(0, 0, 0, 1e-6, 0, 0, 256, None) == jq4k.OK            # N == 0

@@ -18,7 +18,7 @@ def _bench_module():
 
 def test_entry_points_defined():
     b = _bench_module()
-    for name in ("decode_leg", "lm_head_leg", "prefill_leg", "prefill_m33_leg", "lm_head_m512_leg", "swiglu_leg",
+    for name in ("decode_leg", "lm_head_leg", "prefill_leg", "prefill_m33_leg", "lm_head_m512_leg", "swiglu_leg", "rmsnorm_leg",
                  "profile_run", "measured_traffic",
                  "cpu_baseline", "cpu_baseline_prefill", "main"):
         assert callable(getattr(b, name)), name

@@ -383,3 +383,39 @@ def test_swiglu_quick_returns(gpu):
     """M == 0 or N == 0: nothing is launched, whatever the pointers."""
     assert gpu.raw().jq4k_gemm_swiglu(0, 0, 0, 0, 0, 5, 256, None) == 0
     assert gpu.raw().jq4k_gemm_swiglu(0, 0, 0, 0, 7, 0, 256, None) == 0
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm fused ahead of the decode GEMV (jq4k_gemv_rmsnorm)
+
+@pytest.mark.parametrize("N,K", [(2560, 2560), (1000, 512), (300, 16384), (1024, 9728), (7, 256)])
+def test_gemv_rmsnorm(gpu, N, K):
+    g = np.random.default_rng(500 + N)
+    W = qi.weight_bytes(g, N, K)
+    X = qi.activations(g, 1, K)
+    gamma = qi.f32_to_bf16_bits((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    eps = 1e-6
+    Y = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    announce(f"gemv rmsnorm N={N} K={K}")
+    gpu.gemv_rmsnorm(dev(W), dev(X).view(torch.bfloat16), dev(gamma).view(torch.bfloat16),
+                     eps, Y)
+    Yr, A, _ = oracle.gemm_rmsnorm(W, X, gamma, eps, N, K)
+    parity(host(Y), Yr, A, f"gemv rmsnorm N={N} K={K}")
+
+
+def test_gemv_rmsnorm_scale_invariance(gpu):
+    """x and 4x normalise to the same x_hat (eps = 0), so the outputs are
+    identical bit for bit."""
+    g = np.random.default_rng(510)
+    N, K = 777, 2560
+    W = qi.weight_bytes(g, N, K)
+    X = qi.activations(g, 1, K)
+    X4 = qi.f32_to_bf16_bits((qi.bf16_bits_to_f32(X) * 4.0).astype(np.float32))
+    gamma = qi.f32_to_bf16_bits(np.ones(K, np.float32))
+    outs = []
+    for x in (X, X4):
+        Y = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+        gpu.gemv_rmsnorm(dev(W), dev(x).view(torch.bfloat16), dev(gamma).view(torch.bfloat16),
+                         0.0, Y)
+        outs.append(host(Y))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
