@@ -246,9 +246,11 @@ def prefill_leg(torch, jq4k, args):
 
 def prefill_m33_leg(torch, jq4k, args):
     """M = 33 through all 36 layers' seven projections (252 matmuls, 2.04 GB of
-    Q4_K weights, child seeds [2, layer, p]): one jq4k_gemm_batched launch per
-    layer, 36 per pass.  HBM-bound: the attainable roofline counts W, X and Y
-    bytes at 8 TB/s."""
+    Q4_K weights, child seeds [2, layer, p]): one jq4k_gemm_batched_ws launch
+    per layer (split K: o in 2 K ranges, down in 4), 36 per pass, one
+    workspace reused layer after layer.  HBM-bound: the attainable roofline
+    counts W, X and Y bytes at 8 TB/s.  The same pass through
+    jq4k_gemm_batched (whole K per tile) is timed beside it."""
     import ctypes
     M, L = 33, jq4k.raw()
     keep, arrs = [], []
@@ -266,24 +268,40 @@ def prefill_m33_leg(torch, jq4k, args):
             xybytes += X.nbytes + M * N * 4
             flops += 2.0 * M * N * K
         arrs.append(arr)
+    need = ctypes.c_size_t(0)
+    rc = L.jq4k_gemm_workspace_size(ctypes.addressof(arrs[0]), 7, ctypes.byref(need))
+    if rc:
+        raise RuntimeError(jq4k.strerror(rc))
+    ws = torch.zeros(max(need.value, 256), dtype=torch.uint8, device="cuda:0")
 
-    def one_pass(i):
+    def pass_ws(i):
+        s = torch.cuda.current_stream().cuda_stream
+        for arr in arrs:
+            rc = L.jq4k_gemm_batched_ws(ctypes.addressof(arr), 7, ws.data_ptr(), ws.numel(), s)
+            if rc:
+                raise RuntimeError(jq4k.strerror(rc))
+
+    def pass_whole_k(i):
         s = torch.cuda.current_stream().cuda_stream
         for arr in arrs:
             rc = L.jq4k_gemm_batched(ctypes.addressof(arr), 7, s)
             if rc:
                 raise RuntimeError(jq4k.strerror(rc))
     steps = max(3, args.prefill_steps // 2)
-    t = timed(torch, one_pass, steps, 1, not args.eager) / steps
+    t = timed(torch, pass_ws, steps, 1, not args.eager) / steps
+    t_whole = timed(torch, pass_whole_k, steps, 1, not args.eager) / steps
     allb = wbytes + xybytes
     return {"workload": "Qwen3-4B cold prefill, M=33 through 36 layers x 7 Q4_K projections "
-                        "(252 matmuls), seeds [2,l,p]; one jq4k_gemm_batched launch per layer",
+                        "(252 matmuls), seeds [2,l,p]; one jq4k_gemm_batched_ws (split-K) "
+                        "launch per layer",
             "launches_per_pass": 36, "us_per_pass": round(t * 1e6, 1),
+            "workspace_bytes": int(need.value),
             "weight_GB_s": round(wbytes / t / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(allb / t / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(allb / t / 1e9 / HBM_PEAK_GBS, 4),
                          "bytes_per_pass": allb},
-            "TFLOP_s": round(flops / t / 1e12, 2)}
+            "TFLOP_s": round(flops / t / 1e12, 2),
+            "whole_k_us_per_pass": round(t_whole * 1e6, 1)}
 
 
 def lm_head_m512_leg(torch, jq4k, args):

@@ -130,9 +130,10 @@ int jq4k_gemv_batched(const jq4k_gemv_desc *problems, int count, hipStream_t str
 
 /* Matmul for any M >= 0: Y (M x N) = X (M x K) . W^T.
  * The genie-ai-runtime README, "At a glance": tensor-core MMQ Q4_K prefill.
- * M == 1 runs the decode GEMV when K <= JQ4K_GEMV_MAX_K; larger M runs the
- * dequantise-to-LDS bf16 MFMA kernels (K <= JQ4K_MFMA_MAX_K, else
- * JQ4K_EINVAL).  M == 0 or N == 0 returns 0 without launching.  Same
+ * M == 1 runs the decode GEMV when K <= JQ4K_GEMV_MAX_K; 2 <= M <= 64 the
+ * small-M MFMA kernel (W dequantised in registers, whole K per workgroup);
+ * larger M the dequantise-to-LDS bf16 MFMA kernels (K <= JQ4K_MFMA_MAX_K,
+ * else JQ4K_EINVAL).  M == 0 or N == 0 returns 0 without launching.  Same
  * pointer and alignment rules as jq4k_gemv. */
 int jq4k_gemm(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
               int M, int N, int K, hipStream_t stream);
@@ -163,6 +164,36 @@ typedef struct {
  * problem that jq4k_gemm rejects (JQ4K_EALIGN likewise); nothing is launched
  * then. */
 int jq4k_gemm_batched(const jq4k_gemm_desc *problems, int count, hipStream_t stream);
+
+/* Grouped matmul with a caller-provided workspace, for the small-M (M <= 64)
+ * launches (the genie-ai-runtime README, "At a glance": tensor-core MMQ Q4_K
+ * prefill, here at the short-prompt sizes).  There each output tile is only
+ * 64 wide and a long row of W (K = 9728, say) would keep one workgroup busy
+ * after the others finish; instead the K of such problems is cut into ranges
+ * of whole blocks, one workgroup each.  Each range writes an fp32 partial tile
+ * to the workspace and the last to finish adds them in range order, so the
+ * result is the same whichever finishes last, run to run.  Same problems,
+ * results and errors as jq4k_gemm_batched; when no problem is split (M > 64,
+ * or nothing to gain) this is jq4k_gemm_batched and the workspace is unused.
+ *   workspace        device memory of at least the size that
+ *                    jq4k_gemm_workspace_size reports for the same problems,
+ *                    256-byte aligned, all zero before its first use; each
+ *                    call leaves it ready for the next (its counters back at
+ *                    zero once the call completes).  Owned by the caller.
+ *   workspace_bytes  its size.
+ * Calls that may run at the same time (other streams) need workspaces of
+ * their own.  Errors, besides jq4k_gemm_batched's: JQ4K_EINVAL if a
+ * workspace is needed and `workspace` is null or smaller than needed,
+ * JQ4K_EALIGN if it is not 256-byte aligned; nothing is launched then. */
+int jq4k_gemm_batched_ws(const jq4k_gemm_desc *problems, int count, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes jq4k_gemm_batched_ws needs for these problems (0 when no
+ * problem splits K; the size depends on the shapes and on the number of
+ * compute units of the current device).  Host only, launches nothing.
+ * Errors: those of jq4k_gemm_batched for the problems (with *bytes = 0),
+ * JQ4K_EINVAL for a null `bytes`. */
+int jq4k_gemm_workspace_size(const jq4k_gemm_desc *problems, int count, size_t *bytes);
 
 /* Decode GEMV with the RMSNorm of x fused into its staging (the
  * genie-ai-runtime README, "At a glance": fused RMSNorm + RoPE + SwiGLU;
@@ -195,14 +226,18 @@ int jq4k_gemm_swiglu(const block_q4_K *Wg, const block_q4_K *Wu, const jq4k_bf16
 /* Kernel paths for jq4k_gemm_path (tests and benchmarks reach every path). */
 #define JQ4K_PATH_AUTO 0 /* what jq4k_gemm picks                        */
 #define JQ4K_PATH_GEMV 1 /* the M = 1 kernel (M must be 1)               */
-#define JQ4K_PATH_MFMA 2 /* the MFMA kernel, tile chosen by shape        */
+#define JQ4K_PATH_MFMA 2 /* the MFMA kernels, chosen by shape (M <= 64:  */
+                         /* the small-M kernel)                         */
 #define JQ4K_PATH_MFMA_T64 3  /* MFMA kernel, 64-row M tile              */
 #define JQ4K_PATH_MFMA_T128 4 /* MFMA kernel, 128-row M tile             */
 #define JQ4K_PATH_MFMA_T256 5 /* MFMA kernel, 256-row M tile, eight waves  */
                               /* (four dequantise, four multiply)         */
+#define JQ4K_PATH_SKINNY 6    /* small-M MFMA kernel (M <= 64), whole K;  */
+                              /* W dequantised in registers, X in LDS     */
 
-/* jq4k_gemm with an explicit kernel path; JQ4K_EINVAL for an unknown path
- * or JQ4K_PATH_GEMV with M != 1.  Results meet the same bound on every path. */
+/* jq4k_gemm with an explicit kernel path; JQ4K_EINVAL for an unknown path,
+ * JQ4K_PATH_GEMV with M != 1 or JQ4K_PATH_SKINNY with M > 64.  Results meet
+ * the same bound on every path. */
 int jq4k_gemm_path(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
                    int M, int N, int K, int path, hipStream_t stream);
 

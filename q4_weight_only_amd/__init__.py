@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libjq4k.so")
 HEADER = os.path.join(HERE, "..", "include", "jq4k.h")
 
 OK, EINVAL, EALIGN = 0, -1, -2
-PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_T64, PATH_MFMA_T128, PATH_MFMA_T256 = range(6)
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_T64, PATH_MFMA_T128, PATH_MFMA_T256, PATH_SKINNY = range(7)
 GEMV_MAX_K = 16384
 MFMA_MAX_K = 4194304
 BLOCK_BYTES = 144
@@ -72,6 +72,10 @@ def _load():
         L.jq4k_gemv_batched.restype = i
         L.jq4k_gemm_batched.argtypes = [vp, i, vp]
         L.jq4k_gemm_batched.restype = i
+        L.jq4k_gemm_batched_ws.argtypes = [vp, i, vp, ctypes.c_size_t, vp]
+        L.jq4k_gemm_batched_ws.restype = i
+        L.jq4k_gemm_workspace_size.argtypes = [vp, i, ctypes.POINTER(ctypes.c_size_t)]
+        L.jq4k_gemm_workspace_size.restype = i
         L.jq4k_gemm_path.argtypes = [vp, vp, vp, i, i, i, i, vp]
         L.jq4k_gemm_swiglu.argtypes = [vp, vp, vp, vp, i, i, i, vp]
         L.jq4k_gemm_swiglu.restype = i
@@ -183,6 +187,28 @@ def gemm_batched(problems, stream=None):
     arr = gemm_descs(problems)
     _check(_load().jq4k_gemm_batched(ctypes.addressof(arr), len(problems), _stream(stream)),
            "jq4k_gemm_batched")
+
+
+def gemm_workspace_size(problems):
+    """Bytes of workspace jq4k_gemm_batched_ws needs for [(W, X, Y), ...]."""
+    arr = gemm_descs(problems)
+    n = ctypes.c_size_t(0)
+    _check(_load().jq4k_gemm_workspace_size(ctypes.addressof(arr), len(problems),
+                                            ctypes.byref(n)), "jq4k_gemm_workspace_size")
+    return n.value
+
+
+def gemm_batched_ws(problems, workspace, stream=None):
+    """jq4k_gemm_batched with a workspace (split K at M <= 64): `workspace`
+    is a device tensor of at least gemm_workspace_size(problems) bytes,
+    zero-filled before its first use (torch.zeros), or None when that size
+    is 0."""
+    arr = gemm_descs(problems)
+    ptr, nbytes = None, 0
+    if workspace is not None:
+        ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(_load().jq4k_gemm_batched_ws(ctypes.addressof(arr), len(problems), ptr, nbytes,
+                                        _stream(stream)), "jq4k_gemm_batched_ws")
 
 
 def gemm(W, X, Y, stream=None, path=PATH_AUTO):

@@ -18,7 +18,13 @@ hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X
 hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
                             const int* M, const int* N, const int* K, int count, int tile,
                             hipStream_t stream);
-long gemm_launch_size(const int* M, const int* N, int count, int tile);
+long gemm_launch_size(const int* M, const int* N, int count, int tile,
+                      const int* splits = nullptr);
+long gemm_splitk_plan(const int* M, const int* N, const int* K, int count, long min_items,
+                      int* splits);
+hipError_t launch_gemm_skinny(const uint8_t* const* W, const uint16_t* const* X,
+                              float* const* Y, const int* M, const int* N, const int* K,
+                              int count, const int* splits, void* ws, hipStream_t stream);
 hipError_t launch_gemm_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
                               int M, int N, int K, hipStream_t stream);
 long gemm_swiglu_launch_size(int M, int N);
@@ -132,6 +138,80 @@ int run_mfma(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, in
     return static_cast<int>(jq4k::launch_gemm_mfma(&w, &X, &Y, &M, &N, &K, 1, tile, stream));
 }
 
+// The small-M kernel (M <= 64), whole K per workgroup.
+int run_skinny(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,
+               hipStream_t stream) {
+    if (M > 64 || K > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
+    if (jq4k::gemm_launch_size(&M, &N, 1, 64) > 0x7FFFFFFFL) return JQ4K_EINVAL;
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
+    return static_cast<int>(
+        jq4k::launch_gemm_skinny(&w, &X, &Y, &M, &N, &K, 1, nullptr, nullptr, stream));
+}
+
+// The MFMA kernel for the shape: small-M up to M = 64, else the tile of
+// mfma_tile_for.
+int run_mfma_auto(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,
+                  hipStream_t stream) {
+    if (M <= 64) return run_skinny(W, X, Y, M, N, K, stream);
+    return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, false), stream);
+}
+
+// The problems of a grouped matmul, checked, with the empty ones dropped.
+struct GemmBatchArgs {
+    const uint8_t* W[JQ4K_GEMM_BATCH_MAX];
+    const uint16_t* X[JQ4K_GEMM_BATCH_MAX];
+    float* Y[JQ4K_GEMM_BATCH_MAX];
+    int M[JQ4K_GEMM_BATCH_MAX], N[JQ4K_GEMM_BATCH_MAX], K[JQ4K_GEMM_BATCH_MAX];
+    int live = 0, max_m = 0, tile = 0;
+};
+
+// 0 = go (a.live > 0), kQuickReturn = nothing to do, < 0 = error code.
+int collect_gemm_batch(const jq4k_gemm_desc* problems, int count, GemmBatchArgs& a) {
+    if (count < 0 || count > JQ4K_GEMM_BATCH_MAX) return JQ4K_EINVAL;
+    if (count == 0) return kQuickReturn;
+    if (problems == nullptr) return JQ4K_EINVAL;
+    for (int i = 0; i < count; ++i) {
+        const jq4k_gemm_desc& d = problems[i];
+        const int rc = check_matmul(d.W, d.X, d.Y, d.M, d.N, d.K);
+        if (rc == kQuickReturn) continue;
+        if (rc != 0) return rc;
+        a.W[a.live] = reinterpret_cast<const uint8_t*>(d.W);
+        a.X[a.live] = d.X;
+        a.Y[a.live] = d.Y;
+        a.M[a.live] = d.M;
+        a.N[a.live] = d.N;
+        a.K[a.live] = d.K;
+        a.max_m = d.M > a.max_m ? d.M : a.max_m;
+        ++a.live;
+    }
+    if (a.live == 0) return kQuickReturn;
+    for (int i = 0; i < a.live; ++i)
+        if (a.K[i] > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
+    a.tile = mfma_tile_for(a.max_m, true);
+    if (jq4k::gemm_launch_size(a.M, a.N, a.live, a.tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
+    return 0;
+}
+
+// Split K applies to the 64-row tiles (M <= 64), whose launches are short of
+// workgroups and whose long-K problems would otherwise run alone at the end.
+// Returns the workspace bytes (0: no problem splits) and the K ranges.
+long splitk_for(const GemmBatchArgs& a, int* splits) {
+    for (int i = 0; i < a.live; ++i) splits[i] = 1;
+    if (a.tile != 64) return 0;
+    return jq4k::gemm_splitk_plan(a.M, a.N, a.K, a.live, 2L * cu_count(), splits);
+}
+
+// The launch of a checked batch: M <= 64 (the 64-row tile) on the small-M
+// kernel of gemm_skinny.hip (split K when `splits` is given), else the MFMA
+// tile the batch's largest M picks.
+int launch_batch(const GemmBatchArgs& a, const int* splits, void* ws, hipStream_t stream) {
+    if (a.tile == 64)
+        return static_cast<int>(jq4k::launch_gemm_skinny(a.W, a.X, a.Y, a.M, a.N, a.K, a.live,
+                                                         splits, ws, stream));
+    return static_cast<int>(
+        jq4k::launch_gemm_mfma(a.W, a.X, a.Y, a.M, a.N, a.K, a.live, a.tile, stream));
+}
+
 int check_export(const void* W, long nblocks, const void* out, uintptr_t out_align) {
     if (nblocks < 0) return JQ4K_EINVAL;
     if (nblocks == 0) return kQuickReturn;
@@ -195,34 +275,36 @@ int jq4k_gemv_batched(const jq4k_gemv_desc* problems, int count, hipStream_t str
 }
 
 int jq4k_gemm_batched(const jq4k_gemm_desc* problems, int count, hipStream_t stream) {
-    if (count < 0 || count > JQ4K_GEMM_BATCH_MAX) return JQ4K_EINVAL;
-    if (count == 0) return JQ4K_OK;
-    if (problems == nullptr) return JQ4K_EINVAL;
-    const uint8_t* W[JQ4K_GEMM_BATCH_MAX];
-    const uint16_t* X[JQ4K_GEMM_BATCH_MAX];
-    float* Y[JQ4K_GEMM_BATCH_MAX];
-    int M[JQ4K_GEMM_BATCH_MAX], N[JQ4K_GEMM_BATCH_MAX], K[JQ4K_GEMM_BATCH_MAX];
-    int live = 0, max_m = 0;
-    for (int i = 0; i < count; ++i) {
-        const jq4k_gemm_desc& d = problems[i];
-        const int rc = check_matmul(d.W, d.X, d.Y, d.M, d.N, d.K);
-        if (rc == kQuickReturn) continue;
-        if (rc != 0) return rc;
-        W[live] = reinterpret_cast<const uint8_t*>(d.W);
-        X[live] = d.X;
-        Y[live] = d.Y;
-        M[live] = d.M;
-        N[live] = d.N;
-        K[live] = d.K;
-        max_m = d.M > max_m ? d.M : max_m;
-        ++live;
-    }
-    if (live == 0) return JQ4K_OK;
-    for (int i = 0; i < live; ++i)
-        if (K[i] > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
-    const int tile = mfma_tile_for(max_m, true);
-    if (jq4k::gemm_launch_size(M, N, live, tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
-    return static_cast<int>(jq4k::launch_gemm_mfma(W, X, Y, M, N, K, live, tile, stream));
+    GemmBatchArgs a;
+    const int rc = collect_gemm_batch(problems, count, a);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    return launch_batch(a, nullptr, nullptr, stream);
+}
+
+int jq4k_gemm_workspace_size(const jq4k_gemm_desc* problems, int count, size_t* bytes) {
+    if (bytes == nullptr) return JQ4K_EINVAL;
+    *bytes = 0;
+    GemmBatchArgs a;
+    const int rc = collect_gemm_batch(problems, count, a);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    int splits[JQ4K_GEMM_BATCH_MAX];
+    *bytes = static_cast<size_t>(splitk_for(a, splits));
+    return JQ4K_OK;
+}
+
+int jq4k_gemm_batched_ws(const jq4k_gemm_desc* problems, int count, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    GemmBatchArgs a;
+    const int rc = collect_gemm_batch(problems, count, a);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    int splits[JQ4K_GEMM_BATCH_MAX];
+    const long need = splitk_for(a, splits);
+    if (need == 0) return launch_batch(a, nullptr, nullptr, stream);
+    if (workspace == nullptr || workspace_bytes < static_cast<size_t>(need)) return JQ4K_EINVAL;
+    if (misaligned(workspace, 256)) return JQ4K_EALIGN;
+    if (jq4k::gemm_launch_size(a.M, a.N, a.live, a.tile, splits) > 0x7FFFFFFFL)
+        return JQ4K_EINVAL;
+    return launch_batch(a, splits, workspace, stream);
 }
 
 int jq4k_gemv_rmsnorm(const block_q4_K* W, const jq4k_bf16* X, const jq4k_bf16* gamma,
@@ -260,19 +342,21 @@ int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16
 
 int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,
                    int path, hipStream_t stream) {
-    if (path < JQ4K_PATH_AUTO || path > JQ4K_PATH_MFMA_T256) return JQ4K_EINVAL;
+    if (path < JQ4K_PATH_AUTO || path > JQ4K_PATH_SKINNY) return JQ4K_EINVAL;
     if (path == JQ4K_PATH_GEMV && (M != 1 || K > JQ4K_GEMV_MAX_K)) return JQ4K_EINVAL;
+    if (path == JQ4K_PATH_SKINNY && M > 64) return JQ4K_EINVAL;
     const int rc = check_matmul(W, X, Y, M, N, K);
     if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
     switch (path) {
         case JQ4K_PATH_GEMV: return run_gemv(W, X, Y, N, K, 0, stream);
-        case JQ4K_PATH_MFMA: return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, false), stream);
+        case JQ4K_PATH_MFMA: return run_mfma_auto(W, X, Y, M, N, K, stream);
         case JQ4K_PATH_MFMA_T64: return run_mfma(W, X, Y, M, N, K, 64, stream);
         case JQ4K_PATH_MFMA_T128: return run_mfma(W, X, Y, M, N, K, 128, stream);
         case JQ4K_PATH_MFMA_T256: return run_mfma(W, X, Y, M, N, K, 256, stream);
+        case JQ4K_PATH_SKINNY: return run_skinny(W, X, Y, M, N, K, stream);
         default:
             if (M == 1 && K <= JQ4K_GEMV_MAX_K) return run_gemv(W, X, Y, N, K, 0, stream);
-            return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, false), stream);
+            return run_mfma_auto(W, X, Y, M, N, K, stream);
     }
 }
 

@@ -258,8 +258,8 @@ __global__ __launch_bounds__(kGemmThreads) void q4k_gemm_mfma_kernel(const GemmB
     using C = GemmCfg<BM, BN, WM, WN>;
     __shared__ uint4 lds[2][C::kLdsChunks];
     constexpr int kOutN = kPair ? BN / 2 : BN;   // output columns per tile
-    int q, tm, tn;
-    if (!tile_sched_next(batch.s, blockIdx.x, &q, &tm, &tn)) return;
+    int q, tm, tn, split;   // split: always 0 (these launches take whole K)
+    if (!tile_sched_next(batch.s, blockIdx.x, &q, &tm, &tn, &split)) return;
     const GemmProblem& pr = batch.p[q];
     gemm_tile<BM, BN, WM, WN, kPair>(pr.W, pr.W2, pr.X, pr.Y, pr.M, pr.N, pr.K, tn * kOutN,
                                      tm * BM, qmask, lds);
@@ -308,15 +308,24 @@ hipError_t launch_gemm_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16
 // Workgroups a SwiGLU launch takes (the largest of its tile choices).
 long gemm_swiglu_launch_size(int M, int N) {
     TileSched s;
-    return tile_sched_init(s, &M, &N, 1, 64, 64, 1);
+    return tile_sched_init(s, &M, &N, nullptr, 1, 64, 64, 1);
 }
 
-// Workgroups a launch of these problems takes (tiles plus at most seven idle
-// workgroups per problem).
-long gemm_launch_size(const int* M, const int* N, int count, int tile) {
+// Workgroups a launch of these problems takes (tiles, times the K ranges
+// when splits is given, plus idle workgroups at the ends of XCD shares).
+long gemm_launch_size(const int* M, const int* N, int count, int tile,
+                      const int* splits) {
     const int bn = tile == 64 ? 64 : 128;
     TileSched s;
-    return tile_sched_init(s, M, N, count, tile, bn, 1);
+    return tile_sched_init(s, M, N, splits, count, tile, bn, 1);
+}
+
+// Split K for the 64 x 64 tiles (M <= 64, the small-M kernel): the K ranges
+// of every problem and the workspace they take (see splitk_plan).
+long gemm_splitk_plan(const int* M, const int* N, const int* K, int count, long min_items,
+                      int* splits) {
+    splitk_plan(M, N, K, count, 64, 64, min_items, splits);
+    return splitk_workspace_bytes(M, N, splits, count, 64, 64);
 }
 
 // tile: 64, 128 or 256 rows of M per workgroup, for the whole batch.  The

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
     const int wave = t >> 6, lane = t & 63;
 
     int q, tm, tn;
-    if (!tile_sched_next(batch.s, blockIdx.x, &q, &tm, &tn)) return;
+    int split;   // always 0: this kernel takes whole K
+    if (!tile_sched_next(batch.s, blockIdx.x, &q, &tm, &tn, &split)) return;
     const GemmProblem& pr = batch.p[q];
     const uint8_t* __restrict__ W = pr.W;
     const uint16_t* __restrict__ X = pr.X;

@@ -66,9 +66,14 @@ def test_gemv_requires_one_token_and_bounded_k(L):
 
 
 def test_unknown_path_is_rejected(L):
-    for path in (-1, 6, 99):
+    for path in (-1, 7, 99):
         assert L.jq4k_gemm_path(ALIGNED, ALIGNED2, ALIGNED3, 4, 8, 256, path,
                                 None) == jq4k.EINVAL
+    # the small-M kernel takes M <= 64 only
+    assert L.jq4k_gemm_path(ALIGNED, ALIGNED2, ALIGNED3, 65, 8, 256, jq4k.PATH_SKINNY,
+                            None) == jq4k.EINVAL
+    assert L.jq4k_gemm_path(ALIGNED, ALIGNED2, ALIGNED3, 0, 8, 256, jq4k.PATH_SKINNY,
+                            None) == jq4k.OK
 
 
 def test_null_pointers_are_rejected(L):
@@ -186,6 +191,60 @@ def test_gemm_batched_argument_checks(L):
         assert f(ctypes.addressof(descs(good, bad)), 2, None) == code, bad
     empty = descs((0, 0, 0, 0, 8, 256), (0, 0, 0, 5, 0, 512))
     assert f(ctypes.addressof(empty), 2, None) == jq4k.OK
+
+
+def _gemm_descs(*rows):
+    arr = (jq4k.GemmDesc * max(len(rows), 1))()
+    for i, r in enumerate(rows):
+        arr[i] = jq4k.GemmDesc(*r)
+    return arr
+
+
+def _ws_size(L, arr, count):
+    n = ctypes.c_size_t(12345)
+    rc = L.jq4k_gemm_workspace_size(ctypes.addressof(arr) if arr is not None else None, count,
+                                    ctypes.byref(n))
+    return rc, n.value
+
+
+def test_gemm_workspace_size(L):
+    """Host-side sizing of the split-K workspace: the M = 33 layer splits o
+    in 2 and down in 4 (with 256 compute units, the count this host assumes
+    without a GPU); M > 64 or one short problem needs none."""
+    A, B, C = ALIGNED, ALIGNED2, ALIGNED3
+    layer = _gemm_descs(*[(A, B, C, 33, n, k) for n, k in
+                          ((4096, 2560), (1024, 2560), (1024, 2560), (2560, 4096),
+                           (9728, 2560), (9728, 2560), (2560, 9728))])
+    rc, n = _ws_size(L, layer, 7)
+    assert rc == jq4k.OK
+    assert n == (80 * 4 + 255) // 256 * 256 + (40 * 2 + 40 * 4) * 64 * 64 * 4
+    for rows in (((A, B, C, 65, 4096, 9728),), ((A, B, C, 8, 64, 256),), ()):
+        rc, n = _ws_size(L, _gemm_descs(*rows), len(rows))
+        assert (rc, n) == (jq4k.OK, 0), rows
+    assert _ws_size(L, _gemm_descs((A, B, C, 4, 8, 300)), 1) == (jq4k.EINVAL, 0)
+    assert _ws_size(L, _gemm_descs((A, B + 2, C, 4, 8, 256)), 1) == (jq4k.EALIGN, 0)
+    assert _ws_size(L, None, 1) == (jq4k.EINVAL, 0)
+    assert L.jq4k_gemm_workspace_size(ctypes.addressof(layer), 7, None) == jq4k.EINVAL
+
+
+def test_gemm_batched_ws_argument_checks(L):
+    """A needed workspace must be given, large enough and 256-byte aligned;
+    every rejection happens before any launch."""
+    f = L.jq4k_gemm_batched_ws
+    A, B, C = ALIGNED, ALIGNED2, ALIGNED3
+    down = _gemm_descs((A, B, C, 33, 2560, 9728))
+    _, need = _ws_size(L, down, 1)
+    assert need > 0
+    WS = 0x100000000
+    assert f(ctypes.addressof(down), 1, None, need, None) == jq4k.EINVAL
+    assert f(ctypes.addressof(down), 1, WS, need - 1, None) == jq4k.EINVAL
+    assert f(ctypes.addressof(down), 1, WS + 128, need, None) == jq4k.EALIGN
+    assert f(None, 0, None, 0, None) == jq4k.OK
+    assert f(None, 1, None, 0, None) == jq4k.EINVAL
+    bad = _gemm_descs((A, B, C, 33, 2560, 9728), (A, B, C + 2, 33, 8, 256))
+    assert f(ctypes.addressof(bad), 2, WS, 1 << 30, None) == jq4k.EALIGN
+    empty = _gemm_descs((0, 0, 0, 0, 8, 256), (0, 0, 0, 5, 0, 512))
+    assert f(ctypes.addressof(empty), 2, None, 0, None) == jq4k.OK
 
 
 def test_gemm_swiglu_argument_checks(L):

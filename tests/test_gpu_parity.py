@@ -178,13 +178,14 @@ def test_gemv_batched_decode_layer(gpu):
 
 # ------------------------------------------------------------ M > 1 (MFMA)
 
-PATHS = ["mfma64", "mfma128", "mfma256"]
+PATHS = ["mfma64", "mfma128", "mfma256", "skinny"]
 
 
 def _path(name):
     import q4_weight_only_amd as jq4k
     return {"mfma": jq4k.PATH_MFMA, "mfma64": jq4k.PATH_MFMA_T64,
-            "mfma128": jq4k.PATH_MFMA_T128, "mfma256": jq4k.PATH_MFMA_T256}[name]
+            "mfma128": jq4k.PATH_MFMA_T128, "mfma256": jq4k.PATH_MFMA_T256,
+            "skinny": jq4k.PATH_SKINNY}[name]
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -192,6 +193,8 @@ def _path(name):
                                    (33, 300, 2560), (64, 129, 512), (65, 257, 256),
                                    (128, 64, 1024), (200, 383, 512), (300, 140, 256)])
 def test_mfma_paths_ragged(gpu, path, M, N, K):
+    if path == "skinny" and M > 64:
+        pytest.skip("the small-M kernel takes M <= 64")
     g = np.random.default_rng([105, M, N, K])
     W = qi.weight_bytes(g, N, K)
     X = qi.activations(g, M, K)
@@ -203,17 +206,20 @@ def test_mfma_paths_ragged(gpu, path, M, N, K):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_mfma_identity_probe(gpu, path):
-    """X = I_K gives Y = bf16(w)^T exactly: every output is one weight."""
+    """X = I_K gives Y = bf16(w)^T exactly: every output is one weight (the
+    small-M kernel takes the identity 64 rows at a time)."""
     g = np.random.default_rng(106)
     N, K = 48, 512
     W = qi.weight_bytes(g, N, K)
-    X = np.zeros((K, K), np.uint16)
-    X[np.arange(K), np.arange(K)] = 0x3F80
-    announce(f"{path} identity probe")
-    y = run_gemm(W, X, N, K, path=_path(path))
     wb = oracle.dequant_bf16(W).reshape(N, K)
     ref = (wb.astype(np.uint32) << 16).view(np.float32)
-    assert np.array_equal(y, ref.T)
+    rows = 64 if path == "skinny" else K
+    for k0 in range(0, K, rows):
+        X = np.zeros((rows, K), np.uint16)
+        X[np.arange(rows), k0 + np.arange(rows)] = 0x3F80
+        announce(f"{path} identity probe, k {k0}..{k0 + rows - 1}")
+        y = run_gemm(W, X, N, K, path=_path(path))
+        assert np.array_equal(y, ref.T[k0:k0 + rows])
 
 
 @pytest.mark.parametrize("M", [2, 33, 300])
@@ -237,6 +243,9 @@ def test_gemm_auto_and_determinism(gpu, M):
     # largest M from 512: the 256-row wave-specialised kernel, ragged in M and N
     (111, [(600, 200, 512), (512, 130, 768), (1, 64, 256), (37, 300, 256), (259, 0, 512)],
      "PATH_MFMA_T256"),
+    # largest M up to 64: the small-M kernel, whole K (no workspace)
+    (112, [(33, 130, 2560), (64, 64, 768), (1, 300, 256), (17, 1000, 9728), (0, 64, 256)],
+     "PATH_SKINNY"),
 ])
 def test_gemm_batched_mixed_problems(gpu, seed, shapes, path):
     """One MFMA launch for independent problems of different shapes: each
@@ -263,6 +272,53 @@ def test_gemm_batched_mixed_problems(gpu, seed, shapes, path):
         parity(got, Y, A, f"gemm batched M={M} N={N} K={K}")
 
 
+# ---------------------------------------------------------------------------
+# Split K with a workspace (jq4k_gemm_batched_ws, M <= 64)
+
+@pytest.mark.parametrize("seed,shapes", [
+    # the down projection alone at M = 33: 40 tiles x 10 K ranges of 3 or 4 blocks
+    (120, [(33, 2560, 9728)]),
+    # small M, ragged N, K from one block to 64 (ragged ranges), an empty problem
+    (121, [(1, 37, 2560), (5, 300, 4096), (64, 129, 9728), (17, 64, 256), (0, 64, 512),
+           (33, 70, 16384)]),
+])
+def test_gemm_batched_ws_split_k(gpu, seed, shapes):
+    """Every output of a split-K launch meets the bound.  The workspace
+    starts with zero counters and NaN in the partial-tile storage (which is
+    always written before it is read); a second identical call, with the
+    counters left at zero by the first and last call's partials in place,
+    gives the same bits."""
+    g = np.random.default_rng(seed)
+    probs = [(M, N, K, qi.weight_bytes(g, N, K), qi.activations(g, M, K)) for M, N, K in shapes]
+    Wd = [dev(W) for *_, W, _ in probs]
+    Xd = [dev(X).view(torch.bfloat16) for *_, X in probs]
+    Yd = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+          for M, N, *_ in probs]
+    triples = list(zip(Wd, Xd, Yd))
+    n = gpu.gemm_workspace_size(triples)
+    assert n > 0 and n % 4 == 0
+    # an upper bound on the counter bytes: one int per tile of every problem
+    tiles = sum(-(-M // 64) * -(-N // 64) for M, N, *_ in shapes)
+    cbytes = min(n, (4 * tiles + 255) // 256 * 256)
+    ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws[:cbytes // 4] = 0
+    ws = ws.view(torch.uint8)
+    announce(f"gemm batched split-K {len(probs)} problems, workspace {n} bytes")
+    gpu.gemm_batched_ws(triples, ws)
+    first = [host(y) for y in Yd]
+    for (M, N, K, W, X), got in zip(probs, first):
+        if M == 0 or N == 0:
+            continue
+        Y, A = oracle.gemm(W, X, N, K)
+        parity(got, Y, A, f"split-K M={M} N={N} K={K}")
+    for y in Yd:
+        y.fill_(float("nan"))
+    announce("gemm batched split-K, second call on the same workspace")
+    gpu.gemm_batched_ws(triples, ws)
+    for y, f in zip(Yd, first):
+        assert np.array_equal(host(y).view(np.uint32), f.view(np.uint32))
+
+
 def test_prefill_m33_one_layer(gpu):
     for p in range(7):
         name, N, K, W, X = qi.prefill_projection(2, 0, p, 33)
@@ -272,14 +328,21 @@ def test_prefill_m33_one_layer(gpu):
         parity(y, Y, A, f"M=33 {name}")
 
 
-def _grouped_layer(gpu, projs, M):
+def _grouped_layer(gpu, projs, M, ws=False):
     """The seven projections of a layer in one grouped launch (as the
-    benchmark times them); returns the host outputs."""
+    benchmark times them: with a workspace, split K, at M <= 64); returns the
+    host outputs."""
     Wd = [dev(W) for _, _, _, W, _ in projs]
     Xd = [dev(X).view(torch.bfloat16) for _, _, _, _, X in projs]
     Yd = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
           for _, N, _, _, _ in projs]
-    gpu.gemm_batched(list(zip(Wd, Xd, Yd)))
+    triples = list(zip(Wd, Xd, Yd))
+    if ws:
+        n = gpu.gemm_workspace_size(triples)
+        assert n > 0
+        gpu.gemm_batched_ws(triples, torch.zeros(n, dtype=torch.uint8, device="cuda:0"))
+    else:
+        gpu.gemm_batched(triples)
     return [host(y) for y in Yd]
 
 
@@ -300,13 +363,13 @@ def test_prefill_m2048_sampled(gpu):
 
 def test_prefill_m33_all_layers_sampled(gpu):
     """M = 33 through all 36 layers (252 matmuls), each layer one grouped
-    launch: 12 sampled rows of every output, all 33 tokens, against the
-    oracle."""
+    split-K launch with a workspace (o in 2 K ranges, down in 4): 12 sampled
+    rows of every output, all 33 tokens, against the oracle."""
     g = np.random.default_rng(113)
     for layer in range(36):
         projs = [qi.prefill_projection(2, layer, p, 33) for p in range(7)]
-        announce(f"prefill M=33 layer {layer}, one grouped launch")
-        ys = _grouped_layer(gpu, projs, 33)
+        announce(f"prefill M=33 layer {layer}, one grouped split-K launch")
+        ys = _grouped_layer(gpu, projs, 33, ws=True)
         for (name, N, K, W, X), y in zip(projs, ys):
             rows = np.sort(g.choice(N, 12, replace=False))
             Y, A = oracle.gemm(W[rows], X, len(rows), K)

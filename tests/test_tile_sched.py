@@ -1,7 +1,10 @@
 """Host checks of the matmul tile schedule (csrc/tile_sched.h), compiled into
-a small host program: every tile of every problem is computed by exactly one
-workgroup, each XCD (workgroup index mod 8) gets an equal share of every
-problem, and the grouped order keeps bands of tile rows together."""
+a small host program: every tile of every problem (and every K range of a
+split tile) is computed by exactly one workgroup, each XCD (workgroup index
+mod 8) gets an equal share of every problem, the K ranges of a tile sit next
+to each other on one XCD, the grouped order keeps bands of tile rows
+together, and the split-K plan gives every workgroup about the same number of
+K stages."""
 import collections
 import os
 import subprocess
@@ -23,32 +26,54 @@ def driver(tmp_path_factory):
     return exe
 
 
-def schedule(driver, BM, BN, group_m, shapes):
-    inp = f"{len(shapes)} {BM} {BN} {group_m} " + " ".join(f"{m} {n}" for m, n in shapes)
+def schedule(driver, BM, BN, group_m, shapes, splits=None):
+    """Rows (q, tile_m, tile_n) per workgroup (split K: (q, tile_m, tile_n,
+    range)); (-1,) for an idle one."""
+    whole_k = splits is None
+    splits = splits or [1] * len(shapes)
+    inp = f"{len(shapes)} {BM} {BN} {group_m} " + " ".join(
+        f"{m} {n} {s}" for (m, n), s in zip(shapes, splits))
     out = subprocess.run([driver], input=inp, capture_output=True, text=True, check=True)
     lines = out.stdout.split("\n")
     grid = int(lines[0])
     rows = [tuple(map(int, l.split())) for l in lines[1:1 + grid]]
     assert len(rows) == grid and grid % 8 == 0
+    if whole_k:
+        assert all(r == (-1,) or r[3] == 0 for r in rows)
+        rows = [r if r == (-1,) else r[:3] for r in rows]
     return rows
 
 
-def check(rows, BM, BN, shapes):
+def plan(driver, BM, BN, min_items, shapes):
+    """splitk_plan: (splits per problem, items, workspace bytes)."""
+    inp = f"plan {len(shapes)} {BM} {BN} {min_items} " + " ".join(
+        f"{m} {n} {k}" for m, n, k in shapes)
+    out = subprocess.run([driver], input=inp, capture_output=True, text=True, check=True)
+    v = list(map(int, out.stdout.split()))
+    return v[:len(shapes)], v[-2], v[-1]
+
+
+def check(rows, BM, BN, shapes, splits=None):
+    whole_k = splits is None
+    splits = splits or [1] * len(shapes)
     seen = collections.Counter(r for r in rows if r != (-1,))
-    for q, (m, n) in enumerate(shapes):
+    for q, ((m, n), S) in enumerate(zip(shapes, splits)):
         tm, tn = -(-m // BM), -(-n // BN)
-        want = {(q, i, j) for i in range(tm) for j in range(tn)}
+        if whole_k:
+            want = {(q, i, j) for i in range(tm) for j in range(tn)}
+        else:
+            want = {(q, i, j, s) for i in range(tm) for j in range(tn) for s in range(S)}
         got = {k for k in seen if k[0] == q}
         assert got == want, f"problem {q}: tiles missing or extra"
     assert all(c == 1 for c in seen.values()), "a tile computed twice"
     # equal share per XCD: per problem, the XCD counts differ by at most one
     # whole per-XCD share boundary (the last XCDs may come up short)
-    for q, (m, n) in enumerate(shapes):
+    for q, ((m, n), S) in enumerate(zip(shapes, splits)):
         total = -(-m // BM) * -(-n // BN)
-        per = -(-total // 8)
+        per = -(-total // 8) * S
         counts = [sum(1 for b, r in enumerate(rows) if b % 8 == x and r[0] == q and r != (-1,))
                   for x in range(8)]
-        assert sum(counts) == total
+        assert sum(counts) == total * S
         assert max(counts) == per
 
 
@@ -89,3 +114,53 @@ def test_single_tile_and_ragged_band(driver):
     shapes = [(5 * 128 + 3, 3 * 128)]        # 6 tile rows: one full band, one of 2
     rows = schedule(driver, 128, 128, 4, shapes)
     check(rows, 128, 128, shapes)
+
+
+def test_split_ranges_adjacent_on_one_xcd(driver):
+    """The K ranges of a tile are consecutive entries of one XCD's queue."""
+    rng = np.random.default_rng(5)
+    for count in (1, 3, 7):
+        shapes = [(int(rng.integers(1, 65)), int(rng.integers(1, 3000))) for _ in range(count)]
+        splits = [int(rng.integers(1, 11)) for _ in range(count)]
+        rows = schedule(driver, 64, 64, 4, shapes, splits)
+        check(rows, 64, 64, shapes, splits)
+        for x in range(8):
+            queue = [r for r in rows[x::8] if r != (-1,)]
+            i = 0
+            while i < len(queue):
+                q, tm, tn, s = queue[i]
+                S = splits[q]
+                assert s == 0
+                assert queue[i:i + S] == [(q, tm, tn, u) for u in range(S)]
+                i += S
+
+
+def test_splitk_plan(driver):
+    """The seven projections of a Qwen3-4B layer at M = 33: q, k, v, gate and
+    up keep whole K (40 stages), o splits in 2 (32 stages each), down in 4
+    (38); 640 workgroups, and a workspace of one counter and S partial
+    64 x 64 tiles per split tile."""
+    layer = [(33, 4096, 2560), (33, 1024, 2560), (33, 1024, 2560), (33, 2560, 4096),
+             (33, 9728, 2560), (33, 9728, 2560), (33, 2560, 9728)]
+    S, items, ws = plan(driver, 64, 64, 512, layer)
+    assert S == [1, 1, 1, 2, 1, 1, 4]
+    assert items == 64 + 16 + 16 + 40 * 2 + 152 + 152 + 40 * 4
+    counters = 40 + 40
+    assert ws == (counters * 4 + 255) // 256 * 256 + (40 * 2 + 40 * 4) * 64 * 64 * 4
+    # down alone: too few tiles, so the target halves down to 16 stages
+    S, items, _ = plan(driver, 64, 64, 512, [(33, 2560, 9728)])
+    assert S == [10] and items == 400
+    # short K never splits below one block per range, nor below 16 stages
+    S, items, ws = plan(driver, 64, 64, 512, [(8, 64, 256), (8, 64, 512)])
+    assert S == [1, 1] and ws == 0
+    # per-range stage counts stay within a factor of two of each other
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        shapes = [(int(rng.integers(1, 65)), int(rng.integers(1, 20000)),
+                   256 * int(rng.integers(1, 80))) for _ in range(int(rng.integers(1, 8)))]
+        S, items, _ = plan(driver, 64, 64, 512, shapes)
+        assert all(1 <= s <= k // 256 for s, (_, _, k) in zip(S, shapes))
+        assert items == sum(-(-m // 64) * -(-n // 64) * s for s, (m, n, _) in zip(S, shapes))
+        lens = [k / 64 / s for s, (_, _, k) in zip(S, shapes)]
+        if min(k for _, _, k in shapes) >= 16 * 64 * 2:
+            assert max(lens) <= 2 * min(lens) + 16
