@@ -10,10 +10,10 @@
 //   * each wave loads its W straight into registers and dequantises it there
 //     (fma(d*sc, q, -dmin*m), the exact value rounded once, then RNE to
 //     bf16) into the B operand of v_mfma_f32_16x16x32_bf16;
-//   * X (bf16) goes through LDS, one half block (128 of K) per stage, double
-//     buffered and shared by the four waves; its rows past M read as zeros
-//     (buffer loads with a range check), so M is padded to 16 MT rows;
-//   * one barrier per stage; W has kSkDepth stages in flight per wave.
+//   * X (bf16, its M rows) goes through LDS two blocks (512 of K) at a time,
+//     shared by the four waves; the next two blocks wait in registers while
+//     the current ones are used, so there are two barriers per two blocks;
+//   * W has kSkDepth half blocks in flight per wave.
 //
 // Operand layout.  The matrix instruction sums over its 32 k positions in
 // any order, so the kernel assigns k to (lane, item) to fit Q4_K: lane l of a
@@ -24,8 +24,8 @@
 // (sub-block 2c+1).  K-step t = 0..3 of the stage takes the low nibbles of
 // dwords {0,1}, {2,3}, then the high nibbles of {0,1}, {2,3} as the lane's
 // 8 B-operand values; the A operand (X) of lane (m = l % 16, p) supplies the
-// 8 matching x values, chunk 8(p/2) + 4(t/2) + 2(p&1) + (t&1) of the stage's
-// 16 chunks of row m.  The accumulators of lane l hold D[m][n] for
+// 8 matching x values, chunk 8(p/2) + 4(t/2) + 2(p&1) + (t&1) of the half
+// block's 16 chunks of row m.  The accumulators of lane l hold D[m][n] for
 // n = l % 16 and m = 4 (l / 16) + r, r = 0..3 (D = X . W^T, 16 x 16).
 //
 // Split K works as in gemm.hip (the 64 x 64 tile schedule and workspace are
@@ -42,21 +42,26 @@ typedef __attribute__((ext_vector_type(4))) float float4_t;
 
 constexpr int kSkThreads = 256;   // four waves
 constexpr int kSkBN = 64;         // rows of W per workgroup: 16 per wave
-constexpr int kSkDepth = 4;       // stages of W in flight per wave
-constexpr int kSkChunks = 16;     // 16-byte chunks of X per row per stage
+constexpr int kSkDepth = 4;       // stages (half blocks) of W in flight per wave
+constexpr int kSkSuper = 4;       // stages per X staging step (two blocks)
+constexpr int kSkRowChunks = 16 * kSkSuper;   // 16-byte chunks of X per row per step
+// LDS row stride in chunks: one chunk of padding, so that 16 rows read at
+// one chunk (row stride 1040 bytes = 260 banks, 4 mod 64) hit 16 different
+// 16-byte slots of the 64 banks, and a lane's reads differ only by
+// compile-time offsets
+constexpr int kSkRowStride = kSkRowChunks + 1;
 // word 3 of a raw buffer resource (see gemm.hip)
 constexpr int kSkBufferConfig = 0x00020000;
 
-// LDS slot of chunk j of X row r in a stage buffer: rows of 16 chunks, the
-// chunk index XOR-ed with the row so that 16 rows read at one chunk hit 16
-// different 16-byte slots of the 256-byte bank window.
-__device__ __forceinline__ int sk_slot(int row, int j) { return row * kSkChunks + (j ^ (row & 15)); }
+// LDS bytes of the X buffer for batches whose largest M is max_m.
+size_t gemm_skinny_lds_bytes(int max_m) {
+    return static_cast<size_t>(max_m) * kSkRowStride * 16;
+}
 
 template <int MT>
 __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmBatch batch,
                                                                      uint32_t qmask) {
-    constexpr int kRows = 16 * MT;   // rows of X staged (M padded)
-    __shared__ uint4 xs[2][kRows * kSkChunks];
+    extern __shared__ uint4 xs[];   // M rows x kSkRowStride chunks
     int q, tm, tn, split;
     if (!tile_sched_next(batch.s, blockIdx.x, &q, &tm, &tn, &split)) return;
     const GemmProblem& pr = batch.p[q];
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmB
     const int nb = K / kQK;
     const int S = batch.s.splits[q];
     const int kb0 = split * nb / S, kb1 = (split + 1) * nb / S;
-    const int nstage = 2 * (kb1 - kb0);   // half blocks
+    const int nstage = 2 * (kb1 - kb0);   // half blocks (even)
     const int hb0 = 2 * kb0;
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -72,19 +77,18 @@ __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmB
     const int n0 = tn * kSkBN;
 
     // ---- W: row n0 + 16 wave + li (clamped: rows past N feed outputs that
-    // are never stored)
+    // are never stored).  Stage st is half hb = hb0 + st of block hb / 2;
+    // hb0 is even and the steps below are unrolled by kSkDepth (even), so the
+    // half of ring entry u is u & 1.  The block header travels with the even
+    // (first-half) entries; the even stage decodes the scales of both halves
+    // and keeps the second half's in `hold` for the odd stage after it.
     const int wn = min(n0 + 16 * wave + li, N - 1);
     const uint8_t* wrow = pr.W + static_cast<long>(wn) * nb * kBlockBytes;
-    // Stage st is half hb = hb0 + st of block hb / 2; hb0 is even and the
-    // pipeline below is unrolled by kSkDepth (even), so the half of ring
-    // entry u is u & 1.  The block header travels with the even (first-half)
-    // entries; the even stage decodes the scales of both halves and keeps
-    // the second half's in `hold` for the odd stage after it.
     struct WRegs {
         uint4 hdr;   // even entries only
         uint4 qs;
     };
-    static_assert(kSkDepth % 2 == 0, "the ring alternates block halves");
+    static_assert(kSkDepth % 2 == 0 && kSkDepth == kSkSuper, "ring entry = stage in step");
     WRegs ring[kSkDepth];
     QuarterScales hold;
     auto load_w = [&](int st, WRegs& r, bool first_half) {
@@ -95,111 +99,116 @@ __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmB
         r.qs = load16(blk + 16 + 64 * (hb & 1) + 16 * p);
     };
 
-    // ---- X: rows 0 .. kRows-1 of the M rows, chunk g = t + 256 j -> row
-    // g / 16, chunk g % 16; rows past M read as zeros
+    // ---- X: the M rows, kSkSuper stages at a time.  Chunk g = t + 256 j of
+    // a step is row g / 64 = 4 j + wave, chunk g % 64 = lane.  The loads of
+    // step j + 1 are requested at the start of step j and stored to LDS at
+    // its end, so their latency is covered by the step's four stages.
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(pr.X), 0, static_cast<int>(static_cast<long>(M) * K * 2),
         kSkBufferConfig);
-    // X of the next kSkDepth stages waits in registers, as far ahead as W:
-    // the hardware counts loads back in issue order, so a wait for an X load
-    // issued after some W load also waits for that W load.
-    uint4 xring[kSkDepth][MT];
-    auto load_x = [&](int st, uint4 (&xr)[MT]) {
-        const int hb = hb0 + min(st, nstage - 1);
+    constexpr int kXLoads = 4 * MT;   // covers rows < 16 MT
+    const int nsuper = (nstage + kSkSuper - 1) / kSkSuper;
+    uint4 xr[kXLoads];
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
+    auto load_x = [&](int j) {
+        const int hbs = hb0 + kSkSuper * min(j, nsuper - 1);
+        const int hb = min(hbs + (lane >> 4), hb0 + nstage - 1);
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
-            const int g = t + j * kSkThreads;
-            const int row = g >> 4, ch = g & 15;
+        for (int i = 0; i < kXLoads; ++i) {
+            const int row = min(4 * i + wave_s, M - 1);
             const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-                xres, (row * K + hb * 128 + ch * 8) * 2, 0, 0);
-            xr[j] = make_uint4(v.x, v.y, v.z, v.w);
+                xres, (row * K + hb * 128 + (lane & 15) * 8) * 2, 0, 0);
+            xr[i] = make_uint4(v.x, v.y, v.z, v.w);
         }
     };
-    auto store_x = [&](const uint4 (&xr)[MT], uint4* buf) {
+    // rows 4 i + wave past M are row M - 1 again: the same values to the
+    // same place (no branch, so the waits for W loads stay exact)
+    auto store_x = [&]() {
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
-            const int g = t + j * kSkThreads;
-            buf[sk_slot(g >> 4, g & 15)] = xr[j];
-        }
+        for (int i = 0; i < kXLoads; ++i)
+            xs[min(4 * i + wave_s, M - 1) * kSkRowStride + lane] = xr[i];
     };
 
     float4_t acc[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+    // A operand rows of the lane, one per M tile (rows past M read row M - 1:
+    // their outputs are never stored), from chunk 8 (p / 2) + 2 (p & 1)
+    const uint4* xa[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        xa[mt] = xs + min(16 * mt + li, M - 1) * kSkRowStride + 8 * (p >> 1) + 2 * (p & 1);
 
     // One stage of the wave: dequantise the 32 weights of the lane into four
     // B operands and multiply them with the A operands of every M tile.
-    auto compute = [&](const QuarterScales& sc, const uint4& qs, const uint4* buf) {
-        const WRegs r{uint4{}, qs};
+    auto compute = [&](const QuarterScales& sc, const uint4& qs, int hb_in_step) {
         uint32_t lo[4][2], hi[4][2];
-        dequant_dword_bf16(r.qs.x, sc, lo[0], hi[0], qmask);
-        dequant_dword_bf16(r.qs.y, sc, lo[1], hi[1], qmask);
-        dequant_dword_bf16(r.qs.z, sc, lo[2], hi[2], qmask);
-        dequant_dword_bf16(r.qs.w, sc, lo[3], hi[3], qmask);
+        dequant_dword_bf16(qs.x, sc, lo[0], hi[0], qmask);
+        dequant_dword_bf16(qs.y, sc, lo[1], hi[1], qmask);
+        dequant_dword_bf16(qs.z, sc, lo[2], hi[2], qmask);
+        dequant_dword_bf16(qs.w, sc, lo[3], hi[3], qmask);
         const uint4 bq[4] = {make_uint4(lo[0][0], lo[0][1], lo[1][0], lo[1][1]),
                              make_uint4(lo[2][0], lo[2][1], lo[3][0], lo[3][1]),
                              make_uint4(hi[0][0], hi[0][1], hi[1][0], hi[1][1]),
                              make_uint4(hi[2][0], hi[2][1], hi[3][0], hi[3][1])};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int ch = 8 * (p >> 1) + 4 * (ks >> 1) + 2 * (p & 1) + (ks & 1);
+            const int c = 16 * hb_in_step + 4 * (ks >> 1) + (ks & 1);   // + the lane's part
             const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bq[ks]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8_t a =
-                    __builtin_bit_cast(bf16x8_t, buf[sk_slot(16 * mt + li, ch)]);
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa[mt][c]);
                 acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mt], 0, 0, 0);
             }
         }
     };
 
-    // ---- pipeline.  Stage st's X and W are requested kSkDepth iterations
-    // ahead (X first), X of stage st is stored to LDS buffer st & 1 in the
-    // iteration before it is used, and each iteration ends with one barrier:
-    //   iteration st: compute stage st (W from ring st % D, X from LDS);
-    //                 store X of stage st + 1 to the other buffer;
-    //                 request X of stage st + 1 + D, then W of stage st + D.
-    // Indices past the end are clamped (harmless repeats).
-#pragma unroll
-    for (int u = 0; u < kSkDepth; ++u) {
-        load_x(u, xring[u]);
-        load_w(u, ring[u], (u & 1) == 0);
-    }
-    store_x(xring[0], xs[0]);
-    load_x(kSkDepth, xring[0]);
-    __syncthreads();
-
-    // One pipeline step; `u` (compile-time) is st % kSkDepth, with the parity
-    // of st.
+    // One stage: `u` (compile-time) is the stage's place in its X step and
+    // its W ring entry (with the parity of the stage).
     auto step = [&](int st, auto u_c) {
         constexpr int u = decltype(u_c)::value;
-        constexpr int un = (u + 1) % kSkDepth;
         if constexpr ((u & 1) == 0) {
             // quarter 2h + p/2 of the lane, h = 0 now and h = 1 next stage
             const QuarterScales sc = quarter_scales(ring[u].hdr, static_cast<uint32_t>(p >> 1));
             hold = quarter_scales(ring[u].hdr, static_cast<uint32_t>(2 + (p >> 1)));
-            compute(sc, ring[u].qs, xs[0]);
+            compute(sc, ring[u].qs, u);
         } else {
-            compute(hold, ring[u].qs, xs[1]);
+            compute(hold, ring[u].qs, u);
         }
-        store_x(xring[un], xs[(u + 1) & 1]);
-        load_x(st + 1 + kSkDepth, xring[un]);
         load_w(st + kSkDepth, ring[u], (u & 1) == 0);
-        __syncthreads();
     };
-    // Whole groups of kSkDepth stages run without branches (so that the
-    // waits for each stage's loads stay exact), then the last few stages.
-    const int nfull = nstage - nstage % kSkDepth;
-    for (int s = 0; s < nfull; s += kSkDepth) {
-        step(s + 0, std::integral_constant<int, 0>{});
-        step(s + 1, std::integral_constant<int, 1>{});
-        step(s + 2, std::integral_constant<int, 2>{});
-        step(s + 3, std::integral_constant<int, 3>{});
+    using U0 = std::integral_constant<int, 0>;
+    using U1 = std::integral_constant<int, 1>;
+    using U2 = std::integral_constant<int, 2>;
+    using U3 = std::integral_constant<int, 3>;
+
+    // ---- pipeline: X of step 0 in LDS, W of stages 0 .. kSkDepth-1 in
+    // flight.  Step j: request X of step j + 1 (past the end: a harmless
+    // repeat), run its kSkSuper stages (each requesting W kSkDepth stages
+    // ahead), then barrier, X of step j + 1 to LDS, barrier.  nstage is even,
+    // so a last partial step has exactly two stages.
+    load_x(0);
+#pragma unroll
+    for (int u = 0; u < kSkDepth; ++u) load_w(u, ring[u], (u & 1) == 0);
+    store_x();
+    __syncthreads();
+    const int nfull = nstage / kSkSuper;
+    for (int j = 0; j < nfull; ++j) {
+        const int s0 = kSkSuper * j;
+        load_x(j + 1);
+        step(s0 + 0, U0{});
+        step(s0 + 1, U1{});
+        step(s0 + 2, U2{});
+        step(s0 + 3, U3{});
+        __syncthreads();
+        store_x();
+        __syncthreads();
     }
-    if (nfull + 0 < nstage) step(nfull + 0, std::integral_constant<int, 0>{});
-    if (nfull + 1 < nstage) step(nfull + 1, std::integral_constant<int, 1>{});
-    if (nfull + 2 < nstage) step(nfull + 2, std::integral_constant<int, 2>{});
-    static_assert(kSkDepth == 4, "the unrolled steps above");
+    if (nstage % kSkSuper != 0) {
+        step(nstage - 2, U0{});
+        step(nstage - 1, U1{});
+    }
+    static_assert(kSkSuper == 4, "the unrolled steps above");
 
     // ---- split K: publish the partial; the last K range adds them all
     if (S > 1) {
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmB
         // the partials of the workgroup, then the counter (agent scope)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
-        int* last = reinterpret_cast<int*>(&xs[0][0]);
+        int* last = reinterpret_cast<int*>(&xs[0]);
         int* cnt = pr.cnt + tm * batch.s.tn[q] + tn;
         if (t == 0) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -263,11 +272,12 @@ hipError_t launch_gemm_skinny(const uint8_t* const* W, const uint16_t* const* X,
     int max_m = 1;
     for (int i = 0; i < count; ++i) max_m = M[i] > max_m ? M[i] : max_m;
     const dim3 g(static_cast<unsigned>(grid)), blk(kSkThreads);
+    const size_t lds = gemm_skinny_lds_bytes(max_m);
     switch ((max_m + 15) / 16) {
-        case 1: hipLaunchKernelGGL(q4k_gemm_skinny_kernel<1>, g, blk, 0, stream, b, kNibbleMask); break;
-        case 2: hipLaunchKernelGGL(q4k_gemm_skinny_kernel<2>, g, blk, 0, stream, b, kNibbleMask); break;
-        case 3: hipLaunchKernelGGL(q4k_gemm_skinny_kernel<3>, g, blk, 0, stream, b, kNibbleMask); break;
-        default: hipLaunchKernelGGL(q4k_gemm_skinny_kernel<4>, g, blk, 0, stream, b, kNibbleMask); break;
+        case 1: hipLaunchKernelGGL(q4k_gemm_skinny_kernel<1>, g, blk, lds, stream, b, kNibbleMask); break;
+        case 2: hipLaunchKernelGGL(q4k_gemm_skinny_kernel<2>, g, blk, lds, stream, b, kNibbleMask); break;
+        case 3: hipLaunchKernelGGL(q4k_gemm_skinny_kernel<3>, g, blk, lds, stream, b, kNibbleMask); break;
+        default: hipLaunchKernelGGL(q4k_gemm_skinny_kernel<4>, g, blk, lds, stream, b, kNibbleMask); break;
     }
     return hipGetLastError();
 }
