@@ -84,6 +84,7 @@ def timed(torch, fn, steps, warmup, use_graph):
 
 DEPENDENCY_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]   # q|k|v, o, gate|up, down
 PREFILL_KERNEL = "jq4k::q4k_gemm_ws_kernel<false>"   # jq4k_gemm_batched at M = 2048 (256-row tile)
+SKINNY_KERNEL = "jq4k::q4k_gemm_skinny_kernel<3>"    # jq4k_gemm_batched_ws at M = 33
 
 
 def decode_leg(torch, jq4k, args):
@@ -299,7 +300,9 @@ def prefill_m33_leg(torch, jq4k, args):
             "weight_GB_s": round(wbytes / t / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(allb / t / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(allb / t / 1e9 / HBM_PEAK_GBS, 4),
-                         "bytes_per_pass": allb},
+                         "bytes_per_pass": allb,
+                         "traffic_per_launch": measured_traffic(SKINNY_KERNEL),
+                         "kernel": SKINNY_KERNEL},
             "TFLOP_s": round(flops / t / 1e12, 2),
             "whole_k_us_per_pass": round(t_whole * 1e6, 1)}
 
@@ -429,8 +432,8 @@ def rmsnorm_leg(torch, jq4k, args):
 def profile_run(torch, jq4k):
     """Launches for rocprofv3 runs: a 512 MiB device copy (the reference for
     scaling FETCH_SIZE / WRITE_SIZE), then 20 batched decode-layer GEMVs, 20
-    LM-head GEMVs and 3 batched launches of the M=2048 layer, eagerly,
-    synchronised."""
+    LM-head GEMVs, 3 batched launches of the M=2048 layer and 5 split-K
+    launches of one M=33 layer, eagerly, synchronised."""
     import ctypes
     a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
@@ -468,6 +471,23 @@ def profile_run(torch, jq4k):
         garr[p] = jq4k.GemmDesc(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K)
     for _ in range(3):
         assert L.jq4k_gemm_batched(ctypes.addressof(garr), 7, s) == 0
+    torch.cuda.synchronize()
+    del keep
+    M = 33
+    keep = []
+    sarr = (jq4k.GemmDesc * 7)()
+    for p in range(7):
+        _, N, K, W, X = qi.prefill_projection(2, 0, p, M)
+        Wd = torch.from_numpy(W).to("cuda:0")
+        Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+        Yd = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        keep.append((Wd, Xd, Yd))
+        sarr[p] = jq4k.GemmDesc(Wd.data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K)
+    need = ctypes.c_size_t(0)
+    assert L.jq4k_gemm_workspace_size(ctypes.addressof(sarr), 7, ctypes.byref(need)) == 0
+    ws = torch.zeros(max(need.value, 256), dtype=torch.uint8, device="cuda:0")
+    for _ in range(5):
+        assert L.jq4k_gemm_batched_ws(ctypes.addressof(sarr), 7, ws.data_ptr(), ws.numel(), s) == 0
     torch.cuda.synchronize()
     print("profile run done", flush=True)
 
