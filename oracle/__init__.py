@@ -7,6 +7,8 @@ imports, links or calls anything here, and this package shares no code with it.
 Contents
   * ctypes wrappers over ``q4k_oracle.c`` (fp16/bf16 scalars, field unpack,
     fp32 dequant, bf16 of the fp32 weight, fp64 contraction with sum |w*x|);
+  * ctypes wrappers over ``kv_oracle.c`` (the FP16 <-> INT8 KV-cache convert:
+    per-vector absmax scale, round-half-even codes, fp16 dequantisation);
   * ``q4k_pack`` -- an independent bit-writer that packs fields into blocks,
     and the min/max quantiser used for the round-trip invariant.
 
@@ -56,6 +58,15 @@ def lib():
         L.oracle_gemm.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
+        i8p = ctypes.POINTER(ctypes.c_int8)
+        L.oracle_float_to_half_rne.argtypes = [ctypes.c_float]
+        L.oracle_float_to_half_rne.restype = ctypes.c_uint16
+        L.oracle_half_to_float.argtypes = [ctypes.c_uint16]
+        L.oracle_half_to_float.restype = ctypes.c_float
+        L.oracle_kv_quant.argtypes = [u16p, ctypes.c_long, ctypes.c_int, i8p, f32p]
+        L.oracle_kv_quant.restype = None
+        L.oracle_kv_dequant.argtypes = [i8p, f32p, ctypes.c_long, ctypes.c_int, u16p]
+        L.oracle_kv_dequant.restype = None
         _lib = L
     return _lib
 
@@ -227,3 +238,43 @@ def gemm_rmsnorm(W, X_bf16, gamma_bf16, eps: float, N: int, K: int):
     Xh = rmsnorm_bf16(X_bf16, gamma_bf16, eps)
     Y, A = gemm(W, Xh, N, K)
     return Y, A, Xh
+
+
+# ---------------------------------------------------------------------------
+# FP16 <-> INT8 KV-cache convert (kv_oracle.c; genie-ai-runtime README,
+# "Project layout" and "At a glance": INT8 KV cache with FP16-ULP-bounded
+# drift).  One fp32 scale per KV vector (a token's head), s = max|v| / 127,
+# codes rint(v / s), dequantised values fp16(fp32(q * s)).
+
+KV_QMAX = 127
+
+
+def float_to_half_rne(x: float) -> int:
+    return int(lib().oracle_float_to_half_rne(float(x)))
+
+
+def half_to_float(h: int) -> float:
+    return float(lib().oracle_half_to_float(int(h)))
+
+
+def kv_quant(v16):
+    """v16: uint16 binary16 patterns, shape (nvec, dim).  Returns the int8
+    codes (same shape) and the fp32 scale of every vector."""
+    v16 = np.ascontiguousarray(v16, dtype=np.uint16)
+    nvec, dim = v16.shape
+    q = np.empty((nvec, dim), np.int8)
+    s = np.empty(nvec, np.float32)
+    lib().oracle_kv_quant(_ptr(v16, ctypes.c_uint16), nvec, dim, _ptr(q, ctypes.c_int8),
+                          _ptr(s, ctypes.c_float))
+    return q, s
+
+
+def kv_dequant(q, s):
+    """Codes (nvec, dim) int8 and scales (nvec,) fp32 -> binary16 patterns."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    nvec, dim = q.shape
+    v = np.empty((nvec, dim), np.uint16)
+    lib().oracle_kv_dequant(_ptr(q, ctypes.c_int8), _ptr(s, ctypes.c_float), nvec, dim,
+                            _ptr(v, ctypes.c_uint16))
+    return v

@@ -1,4 +1,5 @@
-"""Compile the CPU oracle into oracle/liboracle_q4k.so (test infrastructure).
+"""Compile the CPU oracle (the Q4_K matmul and the KV-cache convert) into
+oracle/liboracle_q4k.so (test infrastructure).
 
 Plain gcc, -O2 with OpenMP, IEEE semantics kept: no -ffast-math, and no
 floating-point contraction so every expression rounds as written.
@@ -8,14 +9,14 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "q4k_oracle.c")
+SRCS = [os.path.join(HERE, "q4k_oracle.c"), os.path.join(HERE, "kv_oracle.c")]
 LIB = os.path.join(HERE, "liboracle_q4k.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
            "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
-           SRC, "-o", LIB + ".tmp", "-lm"]
+           *SRCS, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

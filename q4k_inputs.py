@@ -19,6 +19,13 @@ Workloads (shapes of Qwen3-4B, whose CLI banner in the genie-ai-runtime README
 reports 36 layers, 2560 hidden): projections q 4096x2560, k 1024x2560,
 v 1024x2560, o 2560x4096, gate 9728x2560, up 9728x2560, down 2560x9728 (N x K),
 and a Q4_K LM head 151936x2560.
+
+KV cache.  FP16 KV vectors of 128 values (one token's head; the README's CLI
+banner gives 8 KV heads, and Qwen3-4B's head size is 128), for 36 layers x
+K and V x 8 heads x 1024 tokens (the README's KV pool is sized at 1024
+context): 589,824 vectors.  Values are binary16 of s_v * z, z ~ N(0, 1), with
+one magnitude s_v per vector drawn log-uniform in [2^-4, 2^4], and a few
+outlier values per vector times 8 (attention activations have a heavy tail).
 """
 import numpy as np
 
@@ -110,3 +117,28 @@ def lm_head(seed=4, M=512):
     W = weight_bytes(g, N, K)
     X = activations(g, M, K)
     return W, X
+
+
+# ---------------------------------------------------------------------------
+# KV cache vectors
+
+KV_DIM = 128
+KV_HEADS = 8
+KV_CTX = 1024
+
+
+def kv_vectors(g, nvec, dim=KV_DIM):
+    """(nvec, dim) binary16 bit patterns (uint16): per-vector magnitude
+    log-uniform in [2^-4, 2^4], two outliers per vector scaled by 8."""
+    mag = np.exp2(g.uniform(-4.0, 4.0, size=(nvec, 1)))
+    z = g.standard_normal((nvec, dim)) * mag
+    cols = g.integers(0, dim, size=(nvec, 2))
+    rows = np.arange(nvec)[:, None]
+    z[rows, cols] *= 8.0
+    return z.astype(np.float16).view(np.uint16)
+
+
+def kv_cache(seed=5, ctx=KV_CTX):
+    """The whole cache of the workload: 36 layers x (K, V) x ctx tokens x 8
+    heads vectors of 128 values, as (nvec, 128) binary16 bit patterns."""
+    return kv_vectors(rng(seed), N_LAYERS * 2 * ctx * KV_HEADS)

@@ -475,3 +475,90 @@ def test_rmsnorm_bf16_rounding_and_contraction():
     assert np.all(np.abs(back - f) <= np.abs(f) * 2.0 ** -8 + 1e-300)
     Y2, A2 = oracle.gemm(W, Xh, N, K)
     assert np.array_equal(Y, Y2) and np.array_equal(A, A2)
+
+
+# ---------------------------------------------------------------------------
+# FP16 <-> INT8 KV-cache convert (oracle/kv_oracle.c)
+
+def test_kv_half_to_float_exhaustive():
+    """Every binary16 pattern decodes as numpy's float16 -> float32 (a
+    library routine)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.half_to_float(int(b)) for b in bits], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_kv_float_to_half_rne_matches_numpy():
+    """fp32 -> binary16 round-to-nearest-even against numpy's conversion, on
+    every binary16 value, every midpoint between neighbours (the ties), points
+    just beside them, subnormals, the overflow edge and random floats."""
+    pos = np.arange(0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2                          # exact in fp32
+    pts = np.concatenate([pos, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                          np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                          [65504.0, 65519.99, 65520.0, 70000.0, 2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -26]])
+    g = np.random.default_rng(7)
+    pts = np.concatenate([pts, np.exp2(g.uniform(-30, 17, 20000)) * g.choice([-1, 1], 20000)])
+    x = np.concatenate([pts, -pts]).astype(np.float32)
+    ref = x.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.float_to_half_rne(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_kv_quant_closed_form():
+    """A vector whose largest magnitude is 127 * 2^k has the exact scale 2^k
+    and codes rint(v / 2^k): ties go to even (2.5 -> 2, 3.5 -> 4, -2.5 -> -2),
+    and dequantisation returns the values exactly."""
+    base = np.array([127, -127, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, 0.0, -0.0, 126.5, 0.25,
+                     64, -1, 100, 7], np.float64)
+    codes = np.array([127, -127, 2, 4, -2, -4, 0, 2, 0, 0, 126, 0, 64, -1, 100, 7], np.int8)
+    for k in (0, -6, 3):
+        v = (base * 2.0 ** k).astype(np.float16).view(np.uint16)[None, :]
+        q, s = oracle.kv_quant(v)
+        assert s[0] == np.float32(2.0 ** k)
+        assert np.array_equal(q[0], codes)
+        back = oracle.kv_dequant(q, s).view(np.float16).astype(np.float64)[0]
+        assert np.array_equal(back, codes.astype(np.float64) * 2.0 ** k)
+
+
+def test_kv_quant_zero_vector_and_sign():
+    v = np.zeros((2, 8), np.float16)
+    v[1] = [-1, 1, -0.5, 0.5, -127, 127, 0, -0.0]
+    q, s = oracle.kv_quant(v.view(np.uint16))
+    assert s[0] == 0 and not q[0].any()
+    assert np.array_equal(oracle.kv_dequant(q, s)[0], np.zeros(8, np.uint16))
+    assert s[1] == 1.0 and list(q[1]) == [-1, 1, 0, 0, -127, 127, 0, 0]
+
+
+def test_kv_dequant_rounding_matches_numpy():
+    """v' = fp16(fp32(q * s)): numpy's fp32 product, then its fp16
+    conversion, agrees bit for bit (this also fixes the two-step rounding)."""
+    g = np.random.default_rng(11)
+    q = g.integers(-127, 128, size=(4000, 16)).astype(np.int8)
+    s = (np.exp2(g.uniform(-20, 8, 4000)) * g.uniform(1, 2, 4000)).astype(np.float32)
+    ref = (q.astype(np.float32) * s[:, None]).astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.kv_dequant(q, s), ref)
+
+
+def test_kv_round_trip_contract():
+    """On the workload's vectors: |q| <= 127 with 127 reached; the round trip
+    stays within s/2 (plus half a binary16 ulp of v' and the fp32 rounding
+    of s and of v/s); quantising v' again gives the same codes and the
+    values move by at most one binary16 ulp (no drift beyond the first round
+    trip)."""
+    v = qi.kv_vectors(qi.rng(12), 3000, 128)
+    q, s = oracle.kv_quant(v)
+    assert np.abs(q.astype(int)).max(axis=1).tolist() == [127] * 3000
+    x = v.view(np.float16).astype(np.float64)
+    back = oracle.kv_dequant(q, s)
+    xb = back.view(np.float16).astype(np.float64)
+    ulp16 = np.spacing(np.abs(back.view(np.float16))).astype(np.float64)
+    bound = s.astype(np.float64)[:, None] * (0.5 + 2.0 ** -16) + ulp16 / 2
+    assert np.all(np.abs(xb - x) <= bound)
+    q2, s2 = oracle.kv_quant(back)
+    assert np.array_equal(q2, q)
+    back2 = oracle.kv_dequant(q2, s2).view(np.float16).astype(np.float64)
+    assert np.all(np.abs(back2 - xb) <= ulp16)
