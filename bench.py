@@ -307,6 +307,54 @@ def prefill_m33_leg(torch, jq4k, args):
             "whole_k_us_per_pass": round(t_whole * 1e6, 1)}
 
 
+def kv_convert_leg(torch, jq4k, args):
+    """FP16 <-> INT8 KV-cache convert over the whole 1024-token cache of the
+    workload (36 layers x K, V x 8 heads x 1024 tokens = 589,824 vectors of
+    128 values, 151 MB in fp16): one jq4k_kv_quant_i8 launch and one
+    jq4k_kv_dequant_f16 launch, each timed over two rotating copies (456 MB,
+    above the last-level cache).  HBM-bound: bytes = 2 B read + 1 B written
+    per value + 4 B per vector (or the reverse)."""
+    import ctypes
+    L = jq4k.raw()
+    v = qi.kv_cache(5)
+    nvec, dim = v.shape
+    vs = [torch.from_numpy(v.view(np.int16)).to("cuda:0")]
+    vs.append(vs[0].clone())
+    qs = [torch.empty((nvec, dim), dtype=torch.int8, device="cuda:0") for _ in range(2)]
+    ss = [torch.empty(nvec, dtype=torch.float32, device="cuda:0") for _ in range(2)]
+    outs = [torch.empty((nvec, dim), dtype=torch.int16, device="cuda:0") for _ in range(2)]
+    s0 = torch.cuda.current_stream().cuda_stream
+    for i in range(2):
+        assert L.jq4k_kv_quant_i8(vs[i].data_ptr(), qs[i].data_ptr(), ss[i].data_ptr(), nvec, dim,
+                                  s0) == 0
+
+    def quant(i):
+        s = torch.cuda.current_stream().cuda_stream
+        rc = L.jq4k_kv_quant_i8(vs[i % 2].data_ptr(), qs[i % 2].data_ptr(), ss[i % 2].data_ptr(),
+                                nvec, dim, s)
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+
+    def dequant(i):
+        s = torch.cuda.current_stream().cuda_stream
+        rc = L.jq4k_kv_dequant_f16(qs[i % 2].data_ptr(), ss[i % 2].data_ptr(),
+                                   outs[i % 2].data_ptr(), nvec, dim, s)
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+    steps = max(10, args.prefill_steps)
+    nbytes = nvec * dim * 3 + nvec * 4
+    res = {"workload": "Qwen3-4B KV cache at 1024 tokens: 589,824 vectors x 128 fp16 "
+                       "(36 layers x K,V x 8 heads), seed 5; one launch per direction",
+           "bytes_per_launch": nbytes}
+    for name, fn in (("fp16_to_int8", quant), ("int8_to_fp16", dequant)):
+        t = timed(torch, fn, steps, 2, not args.eager) / steps
+        gbs = nbytes / t / 1e9
+        res[name] = {"us": round(t * 1e6, 2), "GB_s": round(gbs, 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    return res
+
+
 def lm_head_m512_leg(torch, jq4k, args):
     """The 151936 x 2560 Q4_K LM head at M = 512 (a prefill chunk): one
     jq4k_gemm launch, MFMA-bound."""
@@ -566,6 +614,7 @@ def main():
     lm512 = lm_head_m512_leg(torch, jq4k, args)
     swiglu = swiglu_leg(torch, jq4k, args)
     rmsnorm = rmsnorm_leg(torch, jq4k, args)
+    kv = kv_convert_leg(torch, jq4k, args)
     tflops = flops * args.prefill_steps / psecs / 1e12
 
     out = {
@@ -621,6 +670,7 @@ def main():
         "lm_head_m512": lm512,
         "swiglu_gate_up": swiglu,
         "rmsnorm_gate_m1": rmsnorm,
+        "kv_convert": kv,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layer)

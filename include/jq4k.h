@@ -74,6 +74,7 @@ _Static_assert(sizeof(block_q4_K) == 144, "block_q4_K must be 144 bytes");
 #endif
 
 typedef uint16_t jq4k_bf16; /* bfloat16 bit pattern */
+typedef uint16_t jq4k_f16;  /* IEEE binary16 bit pattern */
 
 #define JQ4K_OK 0
 #define JQ4K_EINVAL (-1) /* bad size, null pointer with a nonzero size,  */
@@ -240,6 +241,35 @@ int jq4k_gemm_swiglu(const block_q4_K *Wg, const block_q4_K *Wu, const jq4k_bf16
  * the same bound on every path. */
 int jq4k_gemm_path(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
                    int M, int N, int K, int path, hipStream_t stream);
+
+/* ---- FP16 <-> INT8 KV-cache convert (the genie-ai-runtime README,
+ * "Project layout": FP16<->INT8 KV convert; "At a glance": INT8 KV cache by
+ * default, FP16-ULP-bounded drift).  The pages give no scheme; the one here:
+ * each KV vector (dim binary16 values, e.g. one token's head) has one fp32
+ * scale s = max|v| / 127 and int8 codes q = rint(v / s) (round half to even,
+ * q = 0 when s = 0); dequantised values are fp16(fp32(q * s)), round to
+ * nearest even.  Each step is one IEEE operation, so codes, scales and
+ * values are fixed bit for bit.  Contract (for vectors with max|v| >= 2^-14,
+ * the binary16 normal range): |v' - v| <= s / 2 (plus half a binary16 ulp of
+ * v'), and quantising v' again gives the same codes (no drift beyond the
+ * first round trip).  Non-finite inputs are outside the contract. */
+#define JQ4K_KV_MAX_DIM 512
+
+/* Quantise nvec vectors of dim binary16 values.
+ *   v      device, nvec * dim values, row-major, 16-byte aligned
+ *   q      device, nvec * dim int8 codes (same layout), 8-byte aligned
+ *   scale  device, nvec fp32 scales, 4-byte aligned
+ *   dim    a multiple of 8, 8 <= dim <= JQ4K_KV_MAX_DIM
+ * nvec == 0 returns 0 without launching.  Errors: JQ4K_EINVAL (nvec < 0, bad
+ * dim, a null pointer, a size that overflows), JQ4K_EALIGN; nothing is
+ * launched then. */
+int jq4k_kv_quant_i8(const jq4k_f16 *v, int8_t *q, float *scale, long nvec, int dim,
+                     hipStream_t stream);
+
+/* Dequantise: v[r][i] = fp16(fp32(q[r][i] * scale[r])).  Same sizes, layouts,
+ * alignment and errors as jq4k_kv_quant_i8. */
+int jq4k_kv_dequant_f16(const int8_t *q, const float *scale, jq4k_f16 *v, long nvec, int dim,
+                        hipStream_t stream);
 
 /* Test exports.  They run the same device unpacking code as the matmul
  * kernels, one block per 256 outputs, so their outputs pin that code.

@@ -76,6 +76,10 @@ def _load():
         L.jq4k_gemm_batched_ws.restype = i
         L.jq4k_gemm_workspace_size.argtypes = [vp, i, ctypes.POINTER(ctypes.c_size_t)]
         L.jq4k_gemm_workspace_size.restype = i
+        L.jq4k_kv_quant_i8.argtypes = [vp, vp, vp, l, i, vp]
+        L.jq4k_kv_quant_i8.restype = i
+        L.jq4k_kv_dequant_f16.argtypes = [vp, vp, vp, l, i, vp]
+        L.jq4k_kv_dequant_f16.restype = i
         L.jq4k_gemm_path.argtypes = [vp, vp, vp, i, i, i, i, vp]
         L.jq4k_gemm_swiglu.argtypes = [vp, vp, vp, vp, i, i, i, vp]
         L.jq4k_gemm_swiglu.restype = i
@@ -242,6 +246,21 @@ def gemm_swiglu(Wg, Wu, X, H, stream=None):
     _check(_load().jq4k_gemm_swiglu(Wg.data_ptr(), Wu.data_ptr(), X.data_ptr(), H.data_ptr(),
                                     M, N, K, _stream(stream)), "jq4k_gemm_swiglu")
     return H
+
+
+def kv_quant_i8(v, q, scale, stream=None):
+    """FP16 -> INT8 KV convert: v (nvec, dim) float16 or int16/uint16 bit
+    patterns, q (nvec, dim) int8, scale (nvec,) float32, all device tensors."""
+    nvec, dim = v.shape
+    _check(_load().jq4k_kv_quant_i8(v.data_ptr(), q.data_ptr(), scale.data_ptr(), nvec, dim,
+                                    _stream(stream)), "jq4k_kv_quant_i8")
+
+
+def kv_dequant_f16(q, scale, v, stream=None):
+    """INT8 -> FP16 KV convert (the inverse mapping of kv_quant_i8's codes)."""
+    nvec, dim = q.shape
+    _check(_load().jq4k_kv_dequant_f16(q.data_ptr(), scale.data_ptr(), v.data_ptr(), nvec, dim,
+                                       _stream(stream)), "jq4k_kv_dequant_f16")
 
 
 def _nblocks(W):

@@ -33,6 +33,12 @@ hipError_t launch_gemv_rmsnorm(const uint8_t* W, const uint16_t* X, const uint16
 hipError_t launch_gemv_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
                               int N, int K, int R, hipStream_t stream);
 
+hipError_t launch_kv_quant(const uint16_t* v, int8_t* q, float* scale, long nvec, int dim,
+                           hipStream_t stream);
+hipError_t launch_kv_dequant(const int8_t* q, const float* scale, uint16_t* v, long nvec, int dim,
+                             hipStream_t stream);
+long kv_grid(long nvec, int dim);
+
 hipError_t launch_unpack_fields(const uint8_t* W, long nblocks, uint8_t* q, uint8_t* sc,
                                 uint8_t* m, hipStream_t stream);
 hipError_t launch_dequant_f32(const uint8_t* W, long nblocks, float* w, hipStream_t stream);
@@ -212,6 +218,19 @@ int launch_batch(const GemmBatchArgs& a, const int* splits, void* ws, hipStream_
         jq4k::launch_gemm_mfma(a.W, a.X, a.Y, a.M, a.N, a.K, a.live, a.tile, stream));
 }
 
+// KV convert: 0 = go, kQuickReturn = nothing to do, < 0 = error code.
+int check_kv(const void* in, const void* out, const float* scale, long nvec, int dim,
+             uintptr_t v_align, uintptr_t q_align, const void* v, const void* q) {
+    if (nvec < 0 || dim < 8 || dim > JQ4K_KV_MAX_DIM || dim % 8 != 0) return JQ4K_EINVAL;
+    if (nvec == 0) return kQuickReturn;
+    if (nvec > 0x7FFFFFFFFFFFFFFFL / dim) return JQ4K_EINVAL;
+    if (in == nullptr || out == nullptr || scale == nullptr) return JQ4K_EINVAL;
+    if (misaligned(v, v_align) || misaligned(q, q_align) || misaligned(scale, 4))
+        return JQ4K_EALIGN;
+    if (jq4k::kv_grid(nvec, dim) > 0x7FFFFFFFL) return JQ4K_EINVAL;
+    return 0;
+}
+
 int check_export(const void* W, long nblocks, const void* out, uintptr_t out_align) {
     if (nblocks < 0) return JQ4K_EINVAL;
     if (nblocks == 0) return kQuickReturn;
@@ -386,6 +405,20 @@ int jq4k_dequant_bf16(const block_q4_K* W, long nblocks, jq4k_bf16* w, hipStream
     if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
     return static_cast<int>(
         jq4k::launch_dequant_bf16(reinterpret_cast<const uint8_t*>(W), nblocks, w, stream));
+}
+
+int jq4k_kv_quant_i8(const jq4k_f16* v, int8_t* q, float* scale, long nvec, int dim,
+                     hipStream_t stream) {
+    const int rc = check_kv(v, q, scale, nvec, dim, 16, 8, v, q);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    return static_cast<int>(jq4k::launch_kv_quant(v, q, scale, nvec, dim, stream));
+}
+
+int jq4k_kv_dequant_f16(const int8_t* q, const float* scale, jq4k_f16* v, long nvec, int dim,
+                        hipStream_t stream) {
+    const int rc = check_kv(q, v, scale, nvec, dim, 16, 8, v, q);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    return static_cast<int>(jq4k::launch_kv_dequant(q, scale, v, nvec, dim, stream));
 }
 
 const char* jq4k_strerror(int code) {

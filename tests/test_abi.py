@@ -271,3 +271,23 @@ def test_gemv_rmsnorm_argument_checks(L):
     assert f(A, B, C + 4, 1e-6, D, 8, 256, None) == jq4k.EALIGN    # gamma misaligned
     assert f(A, B, C, 1e-6, D, 8, jq4k.GEMV_MAX_K + 256, None) == jq4k.EINVAL
     assert f(0, 0, 0, 1e-6, 0, 0, 256, None) == jq4k.OK            # N == 0
+
+
+def test_kv_convert_argument_checks(L):
+    """dim a multiple of 8 in 8..512, nvec >= 0, non-null pointers, v
+    16-byte / q 8-byte / scale 4-byte alignment; nvec == 0 is a no-op."""
+    V, Q, S = ALIGNED, ALIGNED2, ALIGNED3
+    for f, args in ((L.jq4k_kv_quant_i8, lambda v, q, s: (v, q, s)),
+                    (L.jq4k_kv_dequant_f16, lambda v, q, s: (q, s, v))):
+        call = lambda v, q, s, n, d: f(*args(v, q, s), n, d, None)
+        for dim in (0, 4, 12, 520, 1024, -8):
+            assert call(V, Q, S, 4, dim) == jq4k.EINVAL, dim
+        assert call(V, Q, S, -1, 128) == jq4k.EINVAL
+        assert call(V, Q, S, 0, 128) == jq4k.OK
+        assert call(0, Q, S, 0, 128) == jq4k.OK
+        for v, q, s in ((0, Q, S), (V, 0, S), (V, Q, 0)):
+            assert call(v, q, s, 4, 128) == jq4k.EINVAL
+        assert call(V + 8, Q, S, 4, 128) == jq4k.EALIGN
+        assert call(V, Q + 4, S, 4, 128) == jq4k.EALIGN
+        assert call(V, Q, S + 2, 4, 128) == jq4k.EALIGN
+        assert call(V, Q, S, 1 << 62, 512) == jq4k.EINVAL

@@ -482,3 +482,66 @@ def test_gemv_rmsnorm_scale_invariance(gpu):
                          0.0, Y)
         outs.append(host(Y))
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# FP16 <-> INT8 KV-cache convert (jq4k_kv_quant_i8, jq4k_kv_dequant_f16)
+
+def _kv_gpu(gpu, v):
+    nvec, dim = v.shape
+    vd = dev(v.view(np.int16))
+    qd = torch.full((nvec, dim), 99, dtype=torch.int8, device="cuda:0")
+    sd = torch.full((nvec,), float("nan"), dtype=torch.float32, device="cuda:0")
+    gpu.kv_quant_i8(vd, qd, sd)
+    back = torch.full((nvec, dim), -1, dtype=torch.int16, device="cuda:0")
+    gpu.kv_dequant_f16(qd, sd, back)
+    return host(qd), host(sd), host(back).view(np.uint16)
+
+
+def _kv_check(gpu, v, what):
+    announce(f"kv convert {what} nvec={v.shape[0]} dim={v.shape[1]}")
+    q, s, back = _kv_gpu(gpu, v)
+    q_ref, s_ref = oracle.kv_quant(v)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32)), what
+    assert np.array_equal(q, q_ref), what
+    assert np.array_equal(back, oracle.kv_dequant(q_ref, s_ref)), what
+
+
+@pytest.mark.parametrize("dim", [8, 24, 64, 128, 136, 512])
+@pytest.mark.parametrize("nvec", [1, 3, 17, 1000])
+def test_kv_convert_bit_exact(gpu, dim, nvec):
+    """Codes, scales and dequantised values bit-identical to the oracle,
+    ragged in nvec (partial workgroups) and in dim (idle lanes of a group)."""
+    v = qi.kv_vectors(qi.rng([130, dim, nvec]), nvec, dim)
+    _kv_check(gpu, v, "ragged")
+
+
+def test_kv_convert_edge_values(gpu):
+    """Zero vectors, signed zeros, the fp16 extremes (65504, subnormals),
+    exact ties at power-of-two scales, one nonzero value per vector (all
+    finite: non-finite inputs are outside the contract)."""
+    dim = 128
+    g = qi.rng(131)
+    rows = [np.zeros(dim), -np.zeros(dim), np.full(dim, 65504.0), np.full(dim, -6e-8),
+            np.clip(g.standard_normal(dim) * 65000 / 4.5, -65504, 65504),
+            g.standard_normal(dim) * 1e-6]
+    tie = np.tile([127, -127, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5], dim // 8)
+    rows += [tie * 2.0 ** k for k in (-10, -3, 0, 5)]
+    one = np.zeros(dim)
+    one[77] = -3.0
+    rows.append(one)
+    v = np.array(rows).astype(np.float16).view(np.uint16)
+    _kv_check(gpu, v, "edge values")
+
+
+def test_kv_convert_full_cache(gpu):
+    """The whole 1024-token cache of the workload (36 layers x K, V x 8
+    heads x 1024 tokens = 589,824 vectors of 128 values), in the launch the
+    benchmark times: every code, scale and value against the oracle, then
+    the GPU's own round trip (quantising its dequantised cache) gives the
+    same codes."""
+    v = qi.kv_cache(5)
+    _kv_check(gpu, v, "full cache")
+    q, s, back = _kv_gpu(gpu, v)
+    q2, _, _ = _kv_gpu(gpu, back)
+    assert np.array_equal(q2, q)
