@@ -248,7 +248,7 @@ def prefill_leg(torch, jq4k, args):
 def prefill_m33_leg(torch, jq4k, args):
     """M = 33 through all 36 layers' seven projections (252 matmuls, 2.04 GB of
     Q4_K weights, child seeds [2, layer, p]): one jq4k_gemm_batched_ws launch
-    per layer (split K: o in 2 K ranges, down in 4), 36 per pass, one
+    per layer (split K: down in 2 K ranges), 36 per pass, one
     workspace reused layer after layer.  HBM-bound: the attainable roofline
     counts W, X and Y bytes at 8 TB/s.  The same pass through
     jq4k_gemm_batched (whole K per tile) is timed beside it."""

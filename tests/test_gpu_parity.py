@@ -363,7 +363,7 @@ def test_prefill_m2048_sampled(gpu):
 
 def test_prefill_m33_all_layers_sampled(gpu):
     """M = 33 through all 36 layers (252 matmuls), each layer one grouped
-    split-K launch with a workspace (o in 2 K ranges, down in 4): 12 sampled
+    split-K launch with a workspace (down in 2 K ranges): 12 sampled
     rows of every output, all 33 tokens, against the oracle."""
     g = np.random.default_rng(113)
     for layer in range(36):

@@ -136,24 +136,24 @@ def test_split_ranges_adjacent_on_one_xcd(driver):
 
 
 def test_splitk_plan(driver):
-    """The seven projections of a Qwen3-4B layer at M = 33: q, k, v, gate and
-    up keep whole K (40 stages), o splits in 2 (32 stages each), down in 4
-    (38); 640 workgroups, and a workspace of one counter and S partial
-    64 x 64 tiles per split tile."""
+    """The seven projections of a Qwen3-4B layer at M = 33: ranges of about
+    twice the shortest whole K (80 stages): every projection keeps whole K
+    but down, which splits in 2 (76 stages each); 560 workgroups, and a
+    workspace of one counter and S partial 64 x 64 tiles per split tile."""
     layer = [(33, 4096, 2560), (33, 1024, 2560), (33, 1024, 2560), (33, 2560, 4096),
              (33, 9728, 2560), (33, 9728, 2560), (33, 2560, 9728)]
     S, items, ws = plan(driver, 64, 64, 512, layer)
-    assert S == [1, 1, 1, 2, 1, 1, 4]
-    assert items == 64 + 16 + 16 + 40 * 2 + 152 + 152 + 40 * 4
-    counters = 40 + 40
-    assert ws == (counters * 4 + 255) // 256 * 256 + (40 * 2 + 40 * 4) * 64 * 64 * 4
+    assert S == [1, 1, 1, 1, 1, 1, 2]
+    assert items == 64 + 16 + 16 + 40 + 152 + 152 + 40 * 2
+    counters = 40
+    assert ws == (counters * 4 + 255) // 256 * 256 + 40 * 2 * 64 * 64 * 4
     # down alone: too few tiles, so the target halves down to 16 stages
     S, items, _ = plan(driver, 64, 64, 512, [(33, 2560, 9728)])
     assert S == [10] and items == 400
     # short K never splits below one block per range, nor below 16 stages
     S, items, ws = plan(driver, 64, 64, 512, [(8, 64, 256), (8, 64, 512)])
     assert S == [1, 1] and ws == 0
-    # per-range stage counts stay within a factor of two of each other
+    # per-range stage counts stay within a factor of about three of each other
     rng = np.random.default_rng(9)
     for _ in range(20):
         shapes = [(int(rng.integers(1, 65)), int(rng.integers(1, 20000)),
@@ -163,4 +163,4 @@ def test_splitk_plan(driver):
         assert items == sum(-(-m // 64) * -(-n // 64) * s for s, (m, n, _) in zip(S, shapes))
         lens = [k / 64 / s for s, (_, _, k) in zip(S, shapes)]
         if min(k for _, _, k in shapes) >= 16 * 64 * 2:
-            assert max(lens) <= 2 * min(lens) + 16
+            assert max(lens) <= 3 * min(lens) + 16
