@@ -15,7 +15,8 @@
 // vector ALU and the matrix core run side by side.  The K loop advances one
 // quarter block (64 weights) per stage; LDS holds two stages and one barrier
 // per stage hands a filled buffer from producers to consumers.  Producers keep
-// two register sets, so global data has two stages of time to arrive.
+// register rings of fetched data: X (re-read by every column tile, mostly
+// L2 hits) two stages ahead, W (streamed from HBM) four stages ahead.
 #include "q4k_device.h"
 #include "tile_sched.h"
 
@@ -36,8 +37,16 @@ __device__ __forceinline__ int ws_chunk(int row, int chunk) {
     return row * kWsRowChunks + (chunk ^ (((row >> 1) ^ ((row & 1) << 2)) & 7));
 }
 
-struct WsRegs {
+// A producer thread's global data for one stage, X and W in separate
+// register rings: X (mostly L2 hits) is fetched two stages ahead, W (a
+// stream from HBM, with the longer latency) kWsWDepth stages ahead.
+constexpr int kWsWDepth = 4;
+
+struct WsXRegs {
     uint4 x[kWsXChunks];
+};
+
+struct WsWRegs {
     uint4 hdr;
     uint4 q;  // 16 quant bytes: half of the row's quarter
 };
@@ -99,21 +108,24 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
         const int wlds_lo1 = kWsBM * kWsRowChunks + ws_chunk(wr, (qoff >> 3) + 1);
         const int wlds_hi0 = kWsBM * kWsRowChunks + ws_chunk(wr, 4 + (qoff >> 3));
         const int wlds_hi1 = kWsBM * kWsRowChunks + ws_chunk(wr, 5 + (qoff >> 3));
-        WsRegs rs[2];
-        auto load_stage = [&](int s, WsRegs& r) {
+        WsXRegs xr[2];
+        WsWRegs wq[kWsWDepth];
+        auto load_x = [&](int s, WsXRegs& r) {
 #pragma unroll
             for (int j = 0; j < kWsXChunks; ++j) {
                 const u32x4_t v =
                     __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[j] + s * kWsBK * 2, 0, 0);
                 r.x[j] = make_uint4(v.x, v.y, v.z, v.w);
             }
+        };
+        auto load_w = [&](int s, WsWRegs& r) {
             const uint8_t* blk = wrow + (s >> 2) * kBlockBytes;
             r.hdr = *reinterpret_cast<const uint4*>(blk);
             r.q = *reinterpret_cast<const uint4*>(blk + 16 + 32 * (s & 3) + qoff);
         };
-        auto store_stage = [&](int s, const WsRegs& r, uint4* buf) {
+        auto store_stage = [&](int s, const WsXRegs& xq, const WsWRegs& r, uint4* buf) {
 #pragma unroll
-            for (int j = 0; j < kWsXChunks; ++j) buf[xlds[j]] = r.x[j];
+            for (int j = 0; j < kWsXChunks; ++j) buf[xlds[j]] = xq.x[j];
             const QuarterScales sc = quarter_scales(r.hdr, static_cast<uint32_t>(s & 3));
             uint32_t lo_a[2], hi_a[2], lo_b[2], hi_b[2];
             dequant_dword_bf16(r.q.x, sc, lo_a, hi_a, qmask);
@@ -125,17 +137,35 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
             buf[wlds_lo1] = make_uint4(lo_a[0], lo_a[1], lo_b[0], lo_b[1]);
             buf[wlds_hi1] = make_uint4(hi_a[0], hi_a[1], hi_b[0], hi_b[1]);
         };
-        load_stage(0, rs[0]);
-        load_stage(last(1), rs[1]);
-        store_stage(0, rs[0], lds[0]);
-        load_stage(last(2), rs[0]);
+        // Stage j is stored (buffer j & 1) one turn before the consumers use
+        // it; its X was fetched two turns before the store, its W four.  W
+        // slot j % 4 and X slot j & 1 hold stage j.  nstage is a multiple of
+        // 4, so the loop body is four turns with constant slot indices.
+        static_assert(kWsWDepth == 4, "the loop below is unrolled for a ring of four");
+        load_x(0, xr[0]);
+#pragma unroll
+        for (int u = 0; u < kWsWDepth; ++u) load_w(last(u), wq[u]);
+        load_x(last(1), xr[1]);
+        store_stage(0, xr[0], wq[0], lds[0]);
+        load_x(last(2), xr[0]);
+        load_w(last(4), wq[0]);
         __syncthreads();
-        for (int s = 0; s < nstage; s += 2) {
-            store_stage(last(s + 1), rs[1], lds[1]);
-            load_stage(last(s + 3), rs[1]);
+        for (int s = 0; s < nstage; s += 4) {
+            store_stage(last(s + 1), xr[1], wq[1], lds[1]);
+            load_x(last(s + 3), xr[1]);
+            load_w(last(s + 5), wq[1]);
             __syncthreads();
-            store_stage(last(s + 2), rs[0], lds[0]);
-            load_stage(last(s + 4), rs[0]);
+            store_stage(last(s + 2), xr[0], wq[2], lds[0]);
+            load_x(last(s + 4), xr[0]);
+            load_w(last(s + 6), wq[2]);
+            __syncthreads();
+            store_stage(last(s + 3), xr[1], wq[3], lds[1]);
+            load_x(last(s + 5), xr[1]);
+            load_w(last(s + 7), wq[3]);
+            __syncthreads();
+            store_stage(last(s + 4), xr[0], wq[0], lds[0]);
+            load_x(last(s + 6), xr[0]);
+            load_w(last(s + 8), wq[0]);
             __syncthreads();
         }
         return;
