@@ -235,6 +235,8 @@ int jq4k_gemm_swiglu(const block_q4_K *Wg, const block_q4_K *Wu, const jq4k_bf16
                               /* (four dequantise, four multiply)         */
 #define JQ4K_PATH_SKINNY 6    /* small-M MFMA kernel (M <= 64), whole K;  */
                               /* W dequantised in registers, X in LDS     */
+#define JQ4K_PATH_MFMA_BIG 7  /* MFMA kernel, 256 x 256 tiles, four waves */
+                              /* that each load, dequantise and multiply  */
 
 /* jq4k_gemm with an explicit kernel path; JQ4K_EINVAL for an unknown path,
  * JQ4K_PATH_GEMV with M != 1 or JQ4K_PATH_SKINNY with M > 64.  Results meet

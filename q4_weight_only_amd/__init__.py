@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libjq4k.so")
 HEADER = os.path.join(HERE, "..", "include", "jq4k.h")
 
 OK, EINVAL, EALIGN = 0, -1, -2
-PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_T64, PATH_MFMA_T128, PATH_MFMA_T256, PATH_SKINNY = range(7)
+(PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_T64, PATH_MFMA_T128, PATH_MFMA_T256, PATH_SKINNY,
+ PATH_MFMA_BIG) = range(8)
 GEMV_MAX_K = 16384
 MFMA_MAX_K = 4194304
 BLOCK_BYTES = 144

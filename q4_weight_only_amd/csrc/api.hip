@@ -20,6 +20,7 @@ hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, f
                             hipStream_t stream);
 long gemm_launch_size(const int* M, const int* N, int count, int tile,
                       const int* splits = nullptr);
+constexpr int kTileBig = 512;   // tile code of the 256 x 256 kernel (gemm_big.hip)
 long gemm_splitk_plan(const int* M, const int* N, const int* K, int count, long min_items,
                       int* splits);
 hipError_t launch_gemm_skinny(const uint8_t* const* W, const uint16_t* const* X,
@@ -361,7 +362,7 @@ int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16
 
 int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,
                    int path, hipStream_t stream) {
-    if (path < JQ4K_PATH_AUTO || path > JQ4K_PATH_SKINNY) return JQ4K_EINVAL;
+    if (path < JQ4K_PATH_AUTO || path > JQ4K_PATH_MFMA_BIG) return JQ4K_EINVAL;
     if (path == JQ4K_PATH_GEMV && (M != 1 || K > JQ4K_GEMV_MAX_K)) return JQ4K_EINVAL;
     if (path == JQ4K_PATH_SKINNY && M > 64) return JQ4K_EINVAL;
     const int rc = check_matmul(W, X, Y, M, N, K);
@@ -373,6 +374,7 @@ int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int
         case JQ4K_PATH_MFMA_T128: return run_mfma(W, X, Y, M, N, K, 128, stream);
         case JQ4K_PATH_MFMA_T256: return run_mfma(W, X, Y, M, N, K, 256, stream);
         case JQ4K_PATH_SKINNY: return run_skinny(W, X, Y, M, N, K, stream);
+        case JQ4K_PATH_MFMA_BIG: return run_mfma(W, X, Y, M, N, K, jq4k::kTileBig, stream);
         default:
             if (M == 1 && K <= JQ4K_GEMV_MAX_K) return run_gemv(W, X, Y, N, K, 0, stream);
             return run_mfma_auto(W, X, Y, M, N, K, stream);

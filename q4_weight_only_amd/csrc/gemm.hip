@@ -292,6 +292,10 @@ static hipError_t launch_pair_cfg(const uint8_t* Wg, const uint8_t* Wu, const ui
 hipError_t launch_gemm_ws(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
                           const int* M, const int* N, const int* K, int count,
                           hipStream_t stream);
+hipError_t launch_gemm_big(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
+                           const int* M, const int* N, const int* K, int count,
+                           hipStream_t stream);
+constexpr int kTileBig = 512;   // tile code of the 256 x 256 kernel (gemm_big.hip)
 
 hipError_t launch_gemm_ws_pair(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
                                int M, int N, int K, hipStream_t stream);
@@ -315,9 +319,10 @@ long gemm_swiglu_launch_size(int M, int N) {
 // when splits is given, plus idle workgroups at the ends of XCD shares).
 long gemm_launch_size(const int* M, const int* N, int count, int tile,
                       const int* splits) {
-    const int bn = tile == 64 ? 64 : 128;
+    const int bm = tile == kTileBig ? 256 : tile;
+    const int bn = tile == 64 ? 64 : tile == kTileBig ? 256 : 128;
     TileSched s;
-    return tile_sched_init(s, M, N, splits, count, tile, bn, 1);
+    return tile_sched_init(s, M, N, splits, count, bm, bn, 1);
 }
 
 // Split K for the 64 x 64 tiles (M <= 64, the small-M kernel): the K ranges
@@ -338,6 +343,7 @@ hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, f
                             hipStream_t stream) {
     if (tile == 64) return launch_cfg<64, 64, 2, 2>(W, X, Y, M, N, K, count, stream);
     if (tile == 256) return launch_gemm_ws(W, X, Y, M, N, K, count, stream);
+    if (tile == kTileBig) return launch_gemm_big(W, X, Y, M, N, K, count, stream);
     return launch_cfg<128, 128, 2, 2>(W, X, Y, M, N, K, count, stream);
 }
 

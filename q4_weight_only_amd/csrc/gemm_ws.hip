@@ -142,6 +142,15 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
         // slot j % 4 and X slot j & 1 hold stage j.  nstage is a multiple of
         // 4, so the loop body is four turns with constant slot indices.
         static_assert(kWsWDepth == 4, "the loop below is unrolled for a ring of four");
+        // Scheduling barriers close every turn: without them the compiler
+        // moves a turn's global loads (whose registers are read turns
+        // later) down to the end of the loop body, and the next iteration
+        // then waits for them at once.
+        auto turn_end = [] {
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
         load_x(0, xr[0]);
 #pragma unroll
         for (int u = 0; u < kWsWDepth; ++u) load_w(last(u), wq[u]);
@@ -149,24 +158,24 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
         store_stage(0, xr[0], wq[0], lds[0]);
         load_x(last(2), xr[0]);
         load_w(last(4), wq[0]);
-        __syncthreads();
+        turn_end();
         for (int s = 0; s < nstage; s += 4) {
             store_stage(last(s + 1), xr[1], wq[1], lds[1]);
             load_x(last(s + 3), xr[1]);
             load_w(last(s + 5), wq[1]);
-            __syncthreads();
+            turn_end();
             store_stage(last(s + 2), xr[0], wq[2], lds[0]);
             load_x(last(s + 4), xr[0]);
             load_w(last(s + 6), wq[2]);
-            __syncthreads();
+            turn_end();
             store_stage(last(s + 3), xr[1], wq[3], lds[1]);
             load_x(last(s + 5), xr[1]);
             load_w(last(s + 7), wq[3]);
-            __syncthreads();
+            turn_end();
             store_stage(last(s + 4), xr[0], wq[0], lds[0]);
             load_x(last(s + 6), xr[0]);
             load_w(last(s + 8), wq[0]);
-            __syncthreads();
+            turn_end();
         }
         return;
     }
@@ -204,17 +213,29 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
     // a stage is issued after the barrier, behind the reads of the next
     // stage's first fragments, so the matrix cores stay busy while the LDS
     // latency of the new stage passes.
+    // The scheduling barriers keep that order: without them the compiler
+    // sinks each fragment read to just before its first use and waits for
+    // it there, which exposes the LDS latency every two matrix instructions.
     bf16x8_t a0[kWsTM], b0[kWsTN], a1[kWsTM], b1[kWsTN];
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
     auto half = [&](const uint4* cur, const uint4* nxt) {
         mma(a0, b0);
+        fence();
         read_frags(cur, 2, a0, b0);
+        fence();
         mma(a1, b1);
+        fence();
         read_frags(cur, 3, a1, b1);
+        fence();
         mma(a0, b0);
+        fence();
         __syncthreads();
         read_frags(nxt, 0, a0, b0);
+        fence();
         mma(a1, b1);
+        fence();
         read_frags(nxt, 1, a1, b1);
+        fence();
     };
     __syncthreads();
     read_frags(lds[0], 0, a0, b0);

@@ -178,14 +178,14 @@ def test_gemv_batched_decode_layer(gpu):
 
 # ------------------------------------------------------------ M > 1 (MFMA)
 
-PATHS = ["mfma64", "mfma128", "mfma256", "skinny"]
+PATHS = ["mfma64", "mfma128", "mfma256", "mfma_big", "skinny"]
 
 
 def _path(name):
     import q4_weight_only_amd as jq4k
     return {"mfma": jq4k.PATH_MFMA, "mfma64": jq4k.PATH_MFMA_T64,
             "mfma128": jq4k.PATH_MFMA_T128, "mfma256": jq4k.PATH_MFMA_T256,
-            "skinny": jq4k.PATH_SKINNY}[name]
+            "skinny": jq4k.PATH_SKINNY, "mfma_big": jq4k.PATH_MFMA_BIG}[name]
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -358,6 +358,21 @@ def test_prefill_m2048_sampled(gpu):
         ms = np.sort(g.choice(2048, 24, replace=False))
         Y, A = oracle.gemm(W[rows], X[ms], len(rows), K)
         parity(y[np.ix_(ms, rows)], Y, A, f"M=2048 {name} sampled")
+        assert np.all(np.isfinite(y))
+
+
+def test_big_tile_m2048_sampled(gpu):
+    """The 256 x 256 tile kernel at M = 2048 on the gate (K = 2560) and down
+    (K = 9728) projections: sampled rows and tokens against the oracle."""
+    g = np.random.default_rng(118)
+    for p in (4, 6):
+        name, N, K, W, X = qi.prefill_projection(3, 0, p, 2048)
+        announce(f"big tile M=2048 {name}")
+        y = run_gemm(W, X, N, K, path=_path("mfma_big"))
+        rows = np.sort(g.choice(N, 48, replace=False))
+        ms = np.sort(g.choice(2048, 24, replace=False))
+        Y, A = oracle.gemm(W[rows], X[ms], len(rows), K)
+        parity(y[np.ix_(ms, rows)], Y, A, f"big tile M=2048 {name} sampled")
         assert np.all(np.isfinite(y))
 
 
