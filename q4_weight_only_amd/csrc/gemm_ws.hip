@@ -6,17 +6,21 @@
 // vector-ALU work of about three instructions per weight, done once per tile;
 // instead of interleaving it with the matrix instructions in one stream, the
 // workgroup splits the roles by wave:
-//   * waves 0..3 (consumers) only read operand fragments from LDS and issue
+//   * waves 0..3 (consumers) read operand fragments from LDS and issue
 //     v_mfma_f32_32x32x16_bf16 into fp32 accumulators (each owns 128 x 64);
-//   * waves 4..7 (producers) fetch the next stages of X (bf16) and W (header
-//     + quant bytes), dequantise W to bf16 (fma(d*sc, q, -dmin*m) rounded
-//     once, then rounded to bf16) and write both slabs to LDS.
+//     between their matrix instructions they also copy the next stage of X
+//     (bf16, no conversion) from global memory to LDS;
+//   * waves 4..7 (producers) fetch W (header + quant bytes), dequantise it to
+//     bf16 (fma(d*sc, q, -dmin*m) rounded once, then rounded to bf16) and
+//     write the W slab to LDS.
 // The hardware places one consumer and one producer wave on each SIMD, so the
 // vector ALU and the matrix core run side by side.  The K loop advances one
 // quarter block (64 weights) per stage; LDS holds two stages and one barrier
-// per stage hands a filled buffer from producers to consumers.  Producers keep
-// register rings of fetched data: X (re-read by every column tile, mostly
-// L2 hits) two stages ahead, W (streamed from HBM) four stages ahead.
+// per stage hands filled buffers on.  X is fetched one stage ahead (mostly L2
+// hits: every column tile re-reads it), W four stages ahead (from HBM).
+// Splitting the LDS writes over all eight waves matters: measured on the
+// chip, four waves write LDS at about 40 bytes per clock per CU, eight at
+// about 70, and a stage writes 48 KB.
 #include "q4k_device.h"
 #include "tile_sched.h"
 
@@ -79,6 +83,35 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
     const int nstage = K / kWsBK;  // a multiple of 4
     auto last = [&](int s) { return min(s, nstage - 1); };
 
+    // X through a buffer resource over rows m0 .. m0 + BM - 1 below M
+    // (zeros past the end; the loads stay in registers until stored).  The
+    // consumer waves fetch and store X: chunk g = t + 256 j of a stage is
+    // row g / 8, chunk g % 8.
+    const long xrows = min(static_cast<long>(kWsBM), static_cast<long>(M - m0));
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(X + static_cast<long>(m0) * K), 0,
+        static_cast<int>(xrows * K * 2), kWsBufferConfig);
+    auto x_off = [&](int j) {
+        const int g = (t & 255) + j * 256;
+        return ((g >> 3) * K + (g & 7) * 8) * 2;
+    };
+    auto x_lds = [&](int j) {
+        const int g = (t & 255) + j * 256;
+        return ws_chunk(g >> 3, g & 7);
+    };
+    auto load_x = [&](int s, WsXRegs& r) {
+#pragma unroll
+        for (int j = 0; j < kWsXChunks; ++j) {
+            const u32x4_t v =
+                __builtin_amdgcn_raw_buffer_load_b128(xres, x_off(j) + s * kWsBK * 2, 0, 0);
+            r.x[j] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+    auto store_x = [&](const WsXRegs& r, uint4* buf) {
+#pragma unroll
+        for (int j = 0; j < kWsXChunks; ++j) buf[x_lds(j)] = r.x[j];
+    };
+
     // The two roles run separate loops (their registers never need to be
     // live together); both loops pass the same 1 + nstage barriers.
     if (wave >= 4) {
@@ -90,42 +123,17 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
         const int wn_row = kPair ? n0 + 32 * (wr >> 6) + (wr & 31) : n0 + wr;
         const uint8_t* wsrc = kPair && ((wr >> 5) & 1) ? pr.W2 : W;
         const uint8_t* wrow = wsrc + static_cast<long>(min(wn_row, N - 1)) * nb * kBlockBytes;
-        // X through a buffer resource over rows m0 .. m0 + BM - 1 below M
-        // (zeros past the end; the loads stay in registers until stored)
-        const long xrows = min(static_cast<long>(kWsBM), static_cast<long>(M - m0));
-        const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(X + static_cast<long>(m0) * K), 0,
-            static_cast<int>(xrows * K * 2), kWsBufferConfig);
-        int xoff[kWsXChunks];
-        int xlds[kWsXChunks];
-#pragma unroll
-        for (int j = 0; j < kWsXChunks; ++j) {
-            const int g = pt + j * 256;
-            xoff[j] = ((g >> 3) * K + (g & 7) * 8) * 2;
-            xlds[j] = ws_chunk(g >> 3, g & 7);
-        }
         const int wlds_lo0 = kWsBM * kWsRowChunks + ws_chunk(wr, (qoff >> 3));
         const int wlds_lo1 = kWsBM * kWsRowChunks + ws_chunk(wr, (qoff >> 3) + 1);
         const int wlds_hi0 = kWsBM * kWsRowChunks + ws_chunk(wr, 4 + (qoff >> 3));
         const int wlds_hi1 = kWsBM * kWsRowChunks + ws_chunk(wr, 5 + (qoff >> 3));
-        WsXRegs xr[2];
         WsWRegs wq[kWsWDepth];
-        auto load_x = [&](int s, WsXRegs& r) {
-#pragma unroll
-            for (int j = 0; j < kWsXChunks; ++j) {
-                const u32x4_t v =
-                    __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[j] + s * kWsBK * 2, 0, 0);
-                r.x[j] = make_uint4(v.x, v.y, v.z, v.w);
-            }
-        };
         auto load_w = [&](int s, WsWRegs& r) {
             const uint8_t* blk = wrow + (s >> 2) * kBlockBytes;
             r.hdr = *reinterpret_cast<const uint4*>(blk);
             r.q = *reinterpret_cast<const uint4*>(blk + 16 + 32 * (s & 3) + qoff);
         };
-        auto store_stage = [&](int s, const WsXRegs& xq, const WsWRegs& r, uint4* buf) {
-#pragma unroll
-            for (int j = 0; j < kWsXChunks; ++j) buf[xlds[j]] = xq.x[j];
+        auto store_w = [&](int s, const WsWRegs& r, uint4* buf) {
             const QuarterScales sc = quarter_scales(r.hdr, static_cast<uint32_t>(s & 3));
             uint32_t lo_a[2], hi_a[2], lo_b[2], hi_b[2];
             dequant_dword_bf16(r.q.x, sc, lo_a, hi_a, qmask);
@@ -137,10 +145,10 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
             buf[wlds_lo1] = make_uint4(lo_a[0], lo_a[1], lo_b[0], lo_b[1]);
             buf[wlds_hi1] = make_uint4(hi_a[0], hi_a[1], hi_b[0], hi_b[1]);
         };
-        // Stage j is stored (buffer j & 1) one turn before the consumers use
-        // it; its X was fetched two turns before the store, its W four.  W
-        // slot j % 4 and X slot j & 1 hold stage j.  nstage is a multiple of
-        // 4, so the loop body is four turns with constant slot indices.
+        // Stage j's W is stored (buffer j & 1) one turn before the consumers
+        // use it, four turns after it was fetched; W slot j % 4 holds stage j.
+        // nstage is a multiple of 4, so the loop body is four turns with
+        // constant slot indices.
         static_assert(kWsWDepth == 4, "the loop below is unrolled for a ring of four");
         // Scheduling barriers close every turn: without them the compiler
         // moves a turn's global loads (whose registers are read turns
@@ -151,29 +159,22 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         };
-        load_x(0, xr[0]);
 #pragma unroll
         for (int u = 0; u < kWsWDepth; ++u) load_w(last(u), wq[u]);
-        load_x(last(1), xr[1]);
-        store_stage(0, xr[0], wq[0], lds[0]);
-        load_x(last(2), xr[0]);
+        store_w(0, wq[0], lds[0]);
         load_w(last(4), wq[0]);
         turn_end();
         for (int s = 0; s < nstage; s += 4) {
-            store_stage(last(s + 1), xr[1], wq[1], lds[1]);
-            load_x(last(s + 3), xr[1]);
+            store_w(last(s + 1), wq[1], lds[1]);
             load_w(last(s + 5), wq[1]);
             turn_end();
-            store_stage(last(s + 2), xr[0], wq[2], lds[0]);
-            load_x(last(s + 4), xr[0]);
+            store_w(last(s + 2), wq[2], lds[0]);
             load_w(last(s + 6), wq[2]);
             turn_end();
-            store_stage(last(s + 3), xr[1], wq[3], lds[1]);
-            load_x(last(s + 5), xr[1]);
+            store_w(last(s + 3), wq[3], lds[1]);
             load_w(last(s + 7), wq[3]);
             turn_end();
-            store_stage(last(s + 4), xr[0], wq[0], lds[0]);
-            load_x(last(s + 6), xr[0]);
+            store_w(last(s + 4), wq[0], lds[0]);
             load_w(last(s + 8), wq[0]);
             turn_end();
         }
@@ -218,10 +219,18 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
     // it there, which exposes the LDS latency every two matrix instructions.
     bf16x8_t a0[kWsTM], b0[kWsTN], a1[kWsTM], b1[kWsTN];
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    auto half = [&](const uint4* cur, const uint4* nxt) {
+    // The consumers also move X: during stage s they store X of stage s + 1
+    // (fetched one stage earlier) into the next buffer and fetch X of stage
+    // s + 2 into the same registers.
+    WsXRegs xr;
+    auto half = [&](int s, const uint4* cur, uint4* nxt, WsXRegs& xq) {
         mma(a0, b0);
         fence();
         read_frags(cur, 2, a0, b0);
+        fence();
+        store_x(xq, nxt);
+        fence();
+        load_x(last(s + 2), xq);
         fence();
         mma(a1, b1);
         fence();
@@ -237,12 +246,15 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
         read_frags(nxt, 1, a1, b1);
         fence();
     };
+    load_x(0, xr);
+    store_x(xr, lds[0]);
+    load_x(last(1), xr);
     __syncthreads();
     read_frags(lds[0], 0, a0, b0);
     read_frags(lds[0], 1, a1, b1);
     for (int s = 0; s < nstage; s += 2) {
-        half(lds[0], lds[1]);
-        half(lds[1], lds[0]);
+        half(s, lds[0], lds[1], xr);
+        half(s + 1, lds[1], lds[0], xr);
     }
     if constexpr (kPair) {
         static_assert(kWsTN == 2, "one gate/up pair of k-tiles per consumer wave");
