@@ -42,7 +42,7 @@ typedef __attribute__((ext_vector_type(4))) float float4_t;
 
 constexpr int kSkThreads = 256;   // four waves
 constexpr int kSkBN = 64;         // rows of W per workgroup: 16 per wave
-constexpr int kSkDepth = 4;       // stages (half blocks) of W in flight per wave
+constexpr int kSkDepth = 8;       // stages (half blocks) of W in flight per wave
 constexpr int kSkSuper = 4;       // stages per X staging step (two blocks)
 constexpr int kSkRowChunks = 16 * kSkSuper;   // 16-byte chunks of X per row per step
 // LDS row stride in chunks: one chunk of padding, so that 16 rows read at
@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmB
     // ---- W: row n0 + 16 wave + li (clamped: rows past N feed outputs that
     // are never stored).  Stage st is half hb = hb0 + st of block hb / 2;
     // hb0 is even and the steps below are unrolled by kSkDepth (even), so the
-    // half of ring entry u is u & 1.  The block header travels with the even
+    // half of ring entry u is u & 1, and ring entry u holds the stages st
+    // with st % kSkDepth == u.  The block header travels with the even
     // (first-half) entries; the even stage decodes the scales of both halves
     // and keeps the second half's in `hold` for the odd stage after it.
     const int wn = min(n0 + 16 * wave + li, N - 1);
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmB
         uint4 hdr;   // even entries only
         uint4 qs;
     };
-    static_assert(kSkDepth % 2 == 0 && kSkDepth == kSkSuper, "ring entry = stage in step");
+    static_assert(kSkDepth % 2 == 0 && kSkDepth == 2 * kSkSuper, "two X steps per ring");
     WRegs ring[kSkDepth];
     QuarterScales hold;
     auto load_w = [&](int st, WRegs& r, bool first_half) {
@@ -163,27 +164,40 @@ __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmB
         }
     };
 
-    // One stage: `u` (compile-time) is the stage's place in its X step and
-    // its W ring entry (with the parity of the stage).
+    // One stage: `u` (compile-time) is the stage's W ring entry (with the
+    // parity of the stage); u % kSkSuper is its place in its X step.
     auto step = [&](int st, auto u_c) {
         constexpr int u = decltype(u_c)::value;
         if constexpr ((u & 1) == 0) {
             // quarter 2h + p/2 of the lane, h = 0 now and h = 1 next stage
             const QuarterScales sc = quarter_scales(ring[u].hdr, static_cast<uint32_t>(p >> 1));
             hold = quarter_scales(ring[u].hdr, static_cast<uint32_t>(2 + (p >> 1)));
-            compute(sc, ring[u].qs, u);
+            compute(sc, ring[u].qs, u % kSkSuper);
         } else {
-            compute(hold, ring[u].qs, u);
+            compute(hold, ring[u].qs, u % kSkSuper);
         }
+        __builtin_amdgcn_sched_barrier(0);
         load_w(st + kSkDepth, ring[u], (u & 1) == 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // the four stages of one X step, ring entries u0 .. u0 + 3
+    auto xstep = [&](int s0, auto u0_c) {
+        constexpr int u0 = decltype(u0_c)::value;
+        step(s0 + 0, std::integral_constant<int, u0 + 0>{});
+        step(s0 + 1, std::integral_constant<int, u0 + 1>{});
+        step(s0 + 2, std::integral_constant<int, u0 + 2>{});
+        step(s0 + 3, std::integral_constant<int, u0 + 3>{});
     };
     using U0 = std::integral_constant<int, 0>;
     using U1 = std::integral_constant<int, 1>;
-    using U2 = std::integral_constant<int, 2>;
-    using U3 = std::integral_constant<int, 3>;
+    using U4 = std::integral_constant<int, 4>;
+    using U5 = std::integral_constant<int, 5>;
 
     // ---- pipeline: X of step 0 in LDS, W of stages 0 .. kSkDepth-1 in
-    // flight.  Step j: request X of step j + 1 (past the end: a harmless
+    // flight.  Scheduling barriers keep every load where it is written: the
+    // compiler otherwise moves the loads (whose registers are read stages
+    // later) to the end of the loop body, next to their first use, and
+    // waits for them there.  Step j: request X of step j + 1 (past the end: a harmless
     // repeat), run its kSkSuper stages (each requesting W kSkDepth stages
     // ahead), then barrier, X of step j + 1 to LDS, barrier.  nstage is even,
     // so a last partial step has exactly two stages.
@@ -193,22 +207,32 @@ __global__ __launch_bounds__(kSkThreads) void q4k_gemm_skinny_kernel(const GemmB
     store_x();
     __syncthreads();
     const int nfull = nstage / kSkSuper;
-    for (int j = 0; j < nfull; ++j) {
-        const int s0 = kSkSuper * j;
+    // two X steps per iteration: the ring's kSkDepth stages
+    auto full_step = [&](int j, auto u0_c) {
         load_x(j + 1);
-        step(s0 + 0, U0{});
-        step(s0 + 1, U1{});
-        step(s0 + 2, U2{});
-        step(s0 + 3, U3{});
+        __builtin_amdgcn_sched_barrier(0);
+        xstep(kSkSuper * j, u0_c);
         __syncthreads();
         store_x();
         __syncthreads();
+    };
+    int j = 0;
+    for (; j + 1 < nfull; j += 2) {
+        full_step(j, U0{});
+        full_step(j + 1, U4{});
     }
+    if (j < nfull) full_step(j++, U0{});
     if (nstage % kSkSuper != 0) {
-        step(nstage - 2, U0{});
-        step(nstage - 1, U1{});
+        // stages 4 nfull and 4 nfull + 1: ring entries 0, 1 or 4, 5
+        if ((nfull & 1) == 0) {
+            step(nstage - 2, U0{});
+            step(nstage - 1, U1{});
+        } else {
+            step(nstage - 2, U4{});
+            step(nstage - 1, U5{});
+        }
     }
-    static_assert(kSkSuper == 4, "the unrolled steps above");
+    static_assert(kSkSuper == 4 && kSkDepth == 8, "the unrolled steps above");
 
     // ---- split K: publish the partial; the last K range adds them all
     if (S > 1) {
