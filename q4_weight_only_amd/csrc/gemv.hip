@@ -167,19 +167,25 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     const int nxc = nb * 32;  // 16-byte chunks of x, at most 2048 (K <= 16384)
     uint4 xv[kGemvMaxXChunksPerThread];
     uint4 gv[kNorm ? kGemvMaxXChunksPerThread : 1];
+    // Every load below is unconditional, past the end a repeat of the last
+    // chunk or block: with loads under branches the compiler's count of
+    // loads in flight turns pessimistic at the joins and it waits for all
+    // of them, which undoes the prefetch.
+    const int nround = (ntask + kGemvThreads - 1) / kGemvThreads;   // same for every thread
+    const int nblk_all = ntask >> 2;
+    auto round_block = [&](int round) { return min(b0 + 64 * round, nblk_all - 1); };
 #pragma unroll
-    for (int j = 0; j < kGemvMaxXChunksPerThread; ++j)
-        if (t + j * kGemvThreads < nxc) {
-            xv[j] = X[t + j * kGemvThreads];
-            if constexpr (kNorm) gv[j] = gamma[t + j * kGemvThreads];
+    for (int j = 0; j < kGemvMaxXChunksPerThread; ++j) {
+        // j beyond the chunks of the largest K: no load at all (compile-time)
+        if (j * kGemvThreads < nxc) {
+            const int g = min(t + j * kGemvThreads, nxc - 1);
+            xv[j] = X[g];
+            if constexpr (kNorm) gv[j] = gamma[g];
         }
+    }
     QuarterLoad ld[kGemvDepth];
 #pragma unroll
-    for (int u = 0; u < kGemvDepth; ++u) {
-        ld[u] = {};
-        if (t + u * kGemvThreads < ntask)
-            ld[u] = load_quarter(blk_ptr(b0 + 64 * u), c);
-    }
+    for (int u = 0; u < kGemvDepth; ++u) ld[u] = load_quarter(blk_ptr(round_block(u)), c);
 
     if constexpr (kNorm) {
         float ss = 0.f;
@@ -229,25 +235,31 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     }
     __syncthreads();
 
+    // A round past the thread's last task (the last round of a span whose
+    // task count is not a multiple of 256) computes on a repeated block and
+    // stores nothing; the four lanes of a block agree, so the quad sum sees
+    // only its own block.  The loop runs whole groups of kGemvDepth rounds
+    // without a branch; the remaining rounds follow it, without prefetch.
     const int kb_step = 64 % nb;
     int kb = b0 % nb;
-    for (int r0 = 0; t + r0 * kGemvThreads < ntask; r0 += kGemvDepth) {
+    auto task = [&](int round, QuarterLoad& l, bool prefetch) {
+        const int b = b0 + 64 * round;
+        const float2 xsm = xsum[kb * 4 + c];
+        float p = quarter_dot(l, c, xs, kb, xsm);
+        p = quad_sum(p);
+        if (c == 0 && b < nblk_all) part[b] = p;
+        if (prefetch) l = load_quarter(blk_ptr(round_block(round + kGemvDepth)), c);
+        kb += kb_step;
+        if (kb >= nb) kb -= nb;
+    };
+    int r0 = 0;
+    for (; r0 + kGemvDepth <= nround; r0 += kGemvDepth) {
 #pragma unroll
-        for (int u = 0; u < kGemvDepth; ++u) {
-            const int tau = t + (r0 + u) * kGemvThreads;
-            if (tau < ntask) {
-                const int b = b0 + 64 * (r0 + u);
-                const float2 xsm = xsum[kb * 4 + c];
-                float p = quarter_dot(ld[u], c, xs, kb, xsm);
-                p = quad_sum(p);
-                if (c == 0) part[b] = p;
-                if (tau + kGemvDepth * kGemvThreads < ntask)
-                    ld[u] = load_quarter(blk_ptr(b + 64 * kGemvDepth), c);
-            }
-            kb += kb_step;
-            if (kb >= nb) kb -= nb;
-        }
+        for (int u = 0; u < kGemvDepth; ++u) task(r0 + u, ld[u], true);
     }
+#pragma unroll
+    for (int u = 0; u + 1 < kGemvDepth; ++u)
+        if (r0 + u < nround) task(r0 + u, ld[u], false);
     __syncthreads();
     for (int r = t; r < rows; r += kGemvThreads) {
         float s = 0.f;
