@@ -8,17 +8,17 @@
 // workgroup splits the roles by wave:
 //   * waves 0..3 (consumers) read operand fragments from LDS and issue
 //     v_mfma_f32_32x32x16_bf16 into fp32 accumulators (each owns 128 x 64);
-//     between their matrix instructions they also copy the next stage of X
-//     (bf16, no conversion) from global memory to LDS;
 //   * waves 4..7 (producers) fetch W (header + quant bytes), dequantise it to
 //     bf16 (fma(d*sc, q, -dmin*m) rounded once, then rounded to bf16) and
-//     write the W slab to LDS.
+//     write the W slab to LDS;
+//   * both roles copy the next stage of X (bf16, no conversion) from global
+//     memory to LDS, rows 0..127 the consumers, rows 128..255 the producers.
 // The hardware places one consumer and one producer wave on each SIMD, so the
 // vector ALU and the matrix core run side by side.  The K loop advances one
 // quarter block (64 weights) per stage; LDS holds two stages and one barrier
 // per stage hands filled buffers on.  X is fetched one stage ahead (mostly L2
 // hits: every column tile re-reads it), W four stages ahead (from HBM).
-// Splitting the LDS writes over all eight waves matters: measured on the
+// Spreading the LDS writes over all eight waves matters: measured on the
 // chip, four waves write LDS at about 40 bytes per clock per CU, eight at
 // about 70, and a stage writes 48 KB.
 #include "q4k_device.h"
@@ -32,7 +32,7 @@ constexpr int kWsThreads = 512;
 constexpr int kWsBM = 256, kWsBN = 128, kWsBK = 64;
 constexpr int kWsRowChunks = kWsBK / 8;
 constexpr int kWsLdsChunks = (kWsBM + kWsBN) * kWsRowChunks;   // per buffer
-constexpr int kWsXChunks = kWsBM * kWsRowChunks / 256;          // per producer thread
+constexpr int kWsXChunks = kWsBM * kWsRowChunks / 256;          // X chunks of a stage per 256 threads
 constexpr int kWsTM = 4, kWsTN = 2;                             // 32x32 tiles per consumer
 constexpr int kWsBufferConfig = 0x00020000;   // raw buffer resource word 3 (gfx9 family)
 
@@ -46,8 +46,11 @@ __device__ __forceinline__ int ws_chunk(int row, int chunk) {
 // stream from HBM, with the longer latency) kWsWDepth stages ahead.
 constexpr int kWsWDepth = 4;
 
+// X chunks a thread copies per stage: each role copies half of the slab.
+constexpr int kWsXHalf = kWsXChunks / 2;
+
 struct WsXRegs {
-    uint4 x[kWsXChunks];
+    uint4 x[kWsXHalf];
 };
 
 struct WsWRegs {
@@ -91,17 +94,20 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(X + static_cast<long>(m0) * K), 0,
         static_cast<int>(xrows * K * 2), kWsBufferConfig);
+    // chunk j of the thread's half: consumers take rows 0..127, producers
+    // rows 128..255 of the slab
+    const int xj0 = wave >= 4 ? kWsXHalf : 0;
     auto x_off = [&](int j) {
-        const int g = (t & 255) + j * 256;
+        const int g = (t & 255) + (xj0 + j) * 256;
         return ((g >> 3) * K + (g & 7) * 8) * 2;
     };
     auto x_lds = [&](int j) {
-        const int g = (t & 255) + j * 256;
+        const int g = (t & 255) + (xj0 + j) * 256;
         return ws_chunk(g >> 3, g & 7);
     };
     auto load_x = [&](int s, WsXRegs& r) {
 #pragma unroll
-        for (int j = 0; j < kWsXChunks; ++j) {
+        for (int j = 0; j < kWsXHalf; ++j) {
             const u32x4_t v =
                 __builtin_amdgcn_raw_buffer_load_b128(xres, x_off(j) + s * kWsBK * 2, 0, 0);
             r.x[j] = make_uint4(v.x, v.y, v.z, v.w);
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
     };
     auto store_x = [&](const WsXRegs& r, uint4* buf) {
 #pragma unroll
-        for (int j = 0; j < kWsXChunks; ++j) buf[x_lds(j)] = r.x[j];
+        for (int j = 0; j < kWsXHalf; ++j) buf[x_lds(j)] = r.x[j];
     };
 
     // The two roles run separate loops (their registers never need to be
@@ -159,22 +165,35 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         };
+        // The producers' half of X goes one stage ahead, like the consumers'.
+        WsXRegs xp;
+        load_x(0, xp);
 #pragma unroll
         for (int u = 0; u < kWsWDepth; ++u) load_w(last(u), wq[u]);
         store_w(0, wq[0], lds[0]);
+        store_x(xp, lds[0]);
+        load_x(last(1), xp);
         load_w(last(4), wq[0]);
         turn_end();
         for (int s = 0; s < nstage; s += 4) {
             store_w(last(s + 1), wq[1], lds[1]);
+            store_x(xp, lds[1]);
+            load_x(last(s + 2), xp);
             load_w(last(s + 5), wq[1]);
             turn_end();
             store_w(last(s + 2), wq[2], lds[0]);
+            store_x(xp, lds[0]);
+            load_x(last(s + 3), xp);
             load_w(last(s + 6), wq[2]);
             turn_end();
             store_w(last(s + 3), wq[3], lds[1]);
+            store_x(xp, lds[1]);
+            load_x(last(s + 4), xp);
             load_w(last(s + 7), wq[3]);
             turn_end();
             store_w(last(s + 4), wq[0], lds[0]);
+            store_x(xp, lds[0]);
+            load_x(last(s + 5), xp);
             load_w(last(s + 8), wq[0]);
             turn_end();
         }
@@ -219,9 +238,9 @@ __global__ __launch_bounds__(kWsThreads) void q4k_gemm_ws_kernel(const GemmBatch
     // it there, which exposes the LDS latency every two matrix instructions.
     bf16x8_t a0[kWsTM], b0[kWsTN], a1[kWsTM], b1[kWsTN];
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    // The consumers also move X: during stage s they store X of stage s + 1
-    // (fetched one stage earlier) into the next buffer and fetch X of stage
-    // s + 2 into the same registers.
+    // The consumers also move their half of X: during stage s they store X
+    // of stage s + 1 (fetched one stage earlier) into the next buffer and
+    // fetch X of stage s + 2 into the same registers.
     WsXRegs xr;
     auto half = [&](int s, const uint4* cur, uint4* nxt, WsXRegs& xq) {
         mma(a0, b0);
