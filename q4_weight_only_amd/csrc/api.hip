@@ -160,7 +160,14 @@ int run_skinny(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, 
 int run_mfma_auto(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,
                   hipStream_t stream) {
     if (M <= 64) return run_skinny(W, X, Y, M, N, K, stream);
-    return run_mfma(W, X, Y, M, N, K, mfma_tile_for(M, false), stream);
+    int tile = mfma_tile_for(M, false);
+    // A single matmul wide enough to give every CU two 256 x 128 tiles
+    // takes the 256-row kernel from M = 512, as a grouped launch does
+    // (the 151936-row LM head at M = 512: 562 vs 705 us with 128 rows).
+    if (tile == 128 && M >= 512 &&
+        static_cast<long>((M + 255) / 256) * ((N + 127) / 128) >= 2L * cu_count())
+        tile = 256;
+    return run_mfma(W, X, Y, M, N, K, tile, stream);
 }
 
 // The problems of a grouped matmul, checked, with the empty ones dropped.
