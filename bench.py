@@ -473,8 +473,31 @@ def rmsnorm_leg(torch, jq4k, args):
             raise RuntimeError(jq4k.strerror(rc))
     tf = timed(torch, fused, args.steps, 4, not args.eager) / args.steps
     tp = timed(torch, plain, args.steps, 4, not args.eager) / args.steps
-    return {"N": N, "K": K, "fused_us": round(tf * 1e6, 2),
-            "fused_GB_s": round(W.nbytes / tf / 1e9, 1), "plain_gemv_us": round(tp * 1e6, 2)}
+    out = {"N": N, "K": K, "fused_us": round(tf * 1e6, 2),
+           "fused_GB_s": round(W.nbytes / tf / 1e9, 1), "plain_gemv_us": round(tp * 1e6, 2)}
+    # M > 1: the rows normalised once (jq4k_rmsnorm_bf16) ahead of the
+    # prefill matmuls, 2048 x 2560 bf16, rotating over copies of X
+    M = 2048
+    Xp = qi.activations(qi.rng(8), M, K)
+    xcopies = max(2, math.ceil(ROTATION_BYTES / (2 * Xp.nbytes)))
+    Xs = [torch.from_numpy(Xp.view(np.int16)).to("cuda:0")]
+    Xs += [Xs[0].clone() for _ in range(xcopies - 1)]
+    Xh = [torch.empty_like(x) for x in Xs]
+
+    def rows(i):
+        c = i % xcopies
+        rc = L.jq4k_rmsnorm_bf16(Xs[c].data_ptr(), Gd.data_ptr(), 1e-6, Xh[c].data_ptr(), M, K,
+                                 torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(jq4k.strerror(rc))
+    tr = timed(torch, rows, args.steps, 4, not args.eager) / args.steps
+    moved = 2 * Xp.nbytes   # read X, write x_hat (gamma: 5 KB, L2-resident)
+    out["rows_m2048"] = {"M": M, "K": K, "us": round(tr * 1e6, 2),
+                         "roofline": {"bound": "hbm", "achieved": round(moved / tr / 1e9, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(moved / tr / 1e9 / HBM_PEAK_GBS, 4),
+                                      "bytes_per_launch": moved}}
+    return out
 
 
 def profile_run(torch, jq4k):

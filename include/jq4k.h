@@ -209,6 +209,22 @@ int jq4k_gemm_workspace_size(const jq4k_gemm_desc *problems, int count, size_t *
 int jq4k_gemv_rmsnorm(const block_q4_K *W, const jq4k_bf16 *X, const jq4k_bf16 *gamma,
                       float eps, float *Y, int N, int K, hipStream_t stream);
 
+/* RMSNorm of M bf16 activation rows ahead of a prefill projection (the
+ * genie-ai-runtime README, "At a glance": fused RMSNorm + RoPE + SwiGLU
+ * kernels; the norm is Qwen3's): Xhat[m][k] = bf16(X[m][k] * r_m * gamma[k]),
+ * r_m = 1 / sqrt(mean_k X[m][k]^2 + eps), computed in fp32 with the same
+ * reduction order and products as jq4k_gemv_rmsnorm, so that composing it
+ * with jq4k_gemv gives that function's result.  X and Xhat are M x K
+ * row-major, gamma K values; Xhat may be X itself (in place), any other
+ * overlap is undefined.  Feed Xhat to jq4k_gemm / jq4k_gemm_batched: at
+ * M > 1 the rows are normalised once here rather than in every matmul
+ * workgroup.  Errors: JQ4K_EINVAL for M < 0, K not a positive multiple of
+ * 256 or K > JQ4K_GEMV_MAX_K, eps < 0, infinite or NaN, or a null pointer
+ * with M > 0; JQ4K_EALIGN unless X, gamma and Xhat are 16-byte aligned.
+ * M == 0 returns 0 without launching. */
+int jq4k_rmsnorm_bf16(const jq4k_bf16 *X, const jq4k_bf16 *gamma, float eps, jq4k_bf16 *Xhat,
+                      int M, int K, hipStream_t stream);
+
 /* SwiGLU of a gate/up projection pair, one launch for any M >= 0:
  * H (M x N) = silu(X . Wg^T) * (X . Wu^T), elementwise, silu(z) = z / (1 +
  * exp(-z)) (the genie-ai-runtime README, "At a glance": fused RMSNorm + RoPE

@@ -86,6 +86,8 @@ def _load():
         L.jq4k_gemm_swiglu.restype = i
         L.jq4k_gemv_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_float, vp, i, i, vp]
         L.jq4k_gemv_rmsnorm.restype = i
+        L.jq4k_rmsnorm_bf16.argtypes = [vp, vp, ctypes.c_float, vp, i, i, vp]
+        L.jq4k_rmsnorm_bf16.restype = i
         L.jq4k_gemm_path.restype = i
         L.jq4k_unpack_fields.argtypes = [vp, l, vp, vp, vp, vp]
         L.jq4k_unpack_fields.restype = i
@@ -237,6 +239,17 @@ def gemv_rmsnorm(W, X, gamma, eps, Y, stream=None):
     _check(_load().jq4k_gemv_rmsnorm(W.data_ptr(), X.data_ptr(), gamma.data_ptr(), float(eps),
                                      Y.data_ptr(), N, K, _stream(stream)), "jq4k_gemv_rmsnorm")
     return Y
+
+
+def rmsnorm_bf16(X, gamma, eps, Xhat, stream=None):
+    """Xhat = bf16(rmsnorm(X) * gamma) row by row (jq4k_rmsnorm_bf16); X and
+    Xhat are M x K bf16 (Xhat may be X), gamma K bf16 values."""
+    if X.dim() != 2 or Xhat.shape != X.shape or gamma.numel() != X.shape[1]:
+        raise ValueError("rmsnorm_bf16 takes X and Xhat of one M x K shape and K gamma values")
+    M, K = X.shape
+    _check(_load().jq4k_rmsnorm_bf16(X.data_ptr(), gamma.data_ptr(), float(eps), Xhat.data_ptr(),
+                                     M, K, _stream(stream)), "jq4k_rmsnorm_bf16")
+    return Xhat
 
 
 def gemm_swiglu(Wg, Wu, X, H, stream=None):

@@ -29,6 +29,8 @@ hipError_t launch_gemm_skinny(const uint8_t* const* W, const uint16_t* const* X,
 hipError_t launch_gemm_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
                               int M, int N, int K, hipStream_t stream);
 long gemm_swiglu_launch_size(int M, int N);
+hipError_t launch_rmsnorm_rows(const uint16_t* X, const uint16_t* gamma, float eps, uint16_t* Xh,
+                               int M, int K, hipStream_t stream);
 hipError_t launch_gemv_rmsnorm(const uint8_t* W, const uint16_t* X, const uint16_t* gamma,
                                float eps, float* Y, int N, int K, int R, hipStream_t stream);
 hipError_t launch_gemv_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
@@ -344,6 +346,16 @@ int jq4k_gemv_rmsnorm(const block_q4_K* W, const jq4k_bf16* X, const jq4k_bf16* 
     const int R = gemv_rows_per_block(N, K);
     return static_cast<int>(jq4k::launch_gemv_rmsnorm(reinterpret_cast<const uint8_t*>(W), X,
                                                       gamma, eps, Y, N, K, R, stream));
+}
+
+int jq4k_rmsnorm_bf16(const jq4k_bf16* X, const jq4k_bf16* gamma, float eps, jq4k_bf16* Xhat,
+                      int M, int K, hipStream_t stream) {
+    if (M < 0 || K <= 0 || K % jq4k::kQK != 0 || K > JQ4K_GEMV_MAX_K) return JQ4K_EINVAL;
+    if (!(eps >= 0.0f) || eps == __builtin_inff()) return JQ4K_EINVAL;
+    if (M == 0) return JQ4K_OK;
+    if (X == nullptr || gamma == nullptr || Xhat == nullptr) return JQ4K_EINVAL;
+    if (misaligned(X, 16) || misaligned(gamma, 16) || misaligned(Xhat, 16)) return JQ4K_EALIGN;
+    return static_cast<int>(jq4k::launch_rmsnorm_rows(X, gamma, eps, Xhat, M, K, stream));
 }
 
 int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16* X, float* H,

@@ -273,6 +273,25 @@ def test_gemv_rmsnorm_argument_checks(L):
     assert f(0, 0, 0, 1e-6, 0, 0, 256, None) == jq4k.OK            # N == 0
 
 
+def test_rmsnorm_rows_argument_checks(L):
+    f = L.jq4k_rmsnorm_bf16
+    A, B, C = ALIGNED, ALIGNED2, ALIGNED3
+    assert f(A, B, 1e-6, C, 4, 300, None) == jq4k.EINVAL          # K not a multiple of 256
+    assert f(A, B, 1e-6, C, 4, 0, None) == jq4k.EINVAL
+    assert f(A, B, 1e-6, C, 4, jq4k.GEMV_MAX_K + 256, None) == jq4k.EINVAL
+    assert f(A, B, 1e-6, C, -1, 256, None) == jq4k.EINVAL         # M < 0
+    assert f(A, B, -1.0, C, 4, 256, None) == jq4k.EINVAL          # eps < 0
+    assert f(A, B, float("nan"), C, 4, 256, None) == jq4k.EINVAL
+    assert f(A, B, float("inf"), C, 4, 256, None) == jq4k.EINVAL
+    assert f(0, B, 1e-6, C, 4, 256, None) == jq4k.EINVAL           # null X
+    assert f(A, 0, 1e-6, C, 4, 256, None) == jq4k.EINVAL           # null gamma
+    assert f(A, B, 1e-6, 0, 4, 256, None) == jq4k.EINVAL           # null Xhat
+    assert f(A + 8, B, 1e-6, C, 4, 256, None) == jq4k.EALIGN
+    assert f(A, B + 2, 1e-6, C, 4, 256, None) == jq4k.EALIGN
+    assert f(A, B, 1e-6, C + 4, 4, 256, None) == jq4k.EALIGN
+    assert f(0, 0, 1e-6, 0, 0, 256, None) == jq4k.OK               # M == 0
+
+
 def test_kv_convert_argument_checks(L):
     """dim a multiple of 8 in 8..512, nvec >= 0, non-null pointers, v
     16-byte / q 8-byte / scale 4-byte alignment; nvec == 0 is a no-op."""

@@ -499,6 +499,90 @@ def test_gemv_rmsnorm_scale_invariance(gpu):
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 
+def _rmsnorm_rows_gpu(gpu, X, gamma, eps, in_place=False):
+    Xd = dev(X).view(torch.bfloat16)
+    Xh = Xd if in_place else torch.full_like(Xd, float("nan"))
+    gpu.rmsnorm_bf16(Xd, dev(gamma).view(torch.bfloat16), eps, Xh)
+    return host(Xh.view(torch.int16)).view(np.uint16)
+
+
+def _check_xhat(xh, X, gamma, eps, what):
+    """x_hat from the GPU (fp32 arithmetic, then RNE to bf16) against the
+    oracle's fp64 value: within half a bf16 ulp plus the fp32 error, and
+    equal to the oracle's bf16 except where the fp64 value sits within that
+    error of a rounding boundary."""
+    ref64 = oracle.rmsnorm_f64(X, gamma, eps)
+    ref = oracle.rmsnorm_bf16(X, gamma, eps)
+    got = oracle.bf16_to_f64(xh).reshape(ref64.shape)
+    err = np.abs(got - ref64)
+    assert np.all(err <= np.abs(ref64) * (2.0 ** -8 + 2.0 ** -20) + 1e-30), what
+    mismatch = np.mean(xh.reshape(ref.shape) != ref)
+    assert mismatch < 1e-3, f"{what}: {mismatch:.2e} of x_hat off the oracle's rounding"
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 2560), (33, 2560), (64, 9728), (5, 16384),
+                                 (2048, 2560)])
+def test_rmsnorm_rows(gpu, M, K):
+    g = np.random.default_rng([520, M, K])
+    X = qi.activations(g, M, K)
+    gamma = qi.f32_to_bf16_bits((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    announce(f"rmsnorm rows M={M} K={K}")
+    xh = _rmsnorm_rows_gpu(gpu, X, gamma, 1e-6)
+    _check_xhat(xh, X, gamma, 1e-6, f"rmsnorm rows M={M} K={K}")
+
+
+def test_rmsnorm_rows_in_place_and_edge_values(gpu):
+    """In place gives the same bits; a zero row with eps = 0 gives NaN (0/0,
+    as the oracle's definition), with eps > 0 zeros; scaling a row by 4
+    leaves x_hat unchanged at eps = 0."""
+    g = np.random.default_rng(521)
+    M, K = 6, 2560
+    X = qi.activations(g, M, K)
+    X[1] = 0
+    X[2] = qi.f32_to_bf16_bits((qi.bf16_bits_to_f32(X[3]) * 4.0).astype(np.float32))
+    gamma = qi.f32_to_bf16_bits(np.ones(K, np.float32))
+    announce("rmsnorm rows in place, zero row, scaled row")
+    a = _rmsnorm_rows_gpu(gpu, X, gamma, 1e-6)
+    b = _rmsnorm_rows_gpu(gpu, X, gamma, 1e-6, in_place=True)
+    assert np.array_equal(a, b)
+    assert np.all(a[1] == 0)
+    z = _rmsnorm_rows_gpu(gpu, X, gamma, 0.0)
+    assert np.array_equal(z[2], z[3])
+    assert np.all(np.isnan(oracle.bf16_to_f64(z[1])))
+
+
+def test_rmsnorm_rows_then_gemv_equals_fused(gpu):
+    """The row norm followed by jq4k_gemv gives jq4k_gemv_rmsnorm's output bit
+    for bit: the same x_hat, then the same GEMV."""
+    g = np.random.default_rng(522)
+    for N, K in ((2560, 2560), (1024, 9728)):
+        W = qi.weight_bytes(g, N, K)
+        X = qi.activations(g, 1, K)
+        gamma = qi.f32_to_bf16_bits((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+        announce(f"rmsnorm rows + gemv vs fused, N={N} K={K}")
+        xh = _rmsnorm_rows_gpu(gpu, X, gamma, 1e-6)
+        y1 = run_gemm(W, xh.reshape(1, K), N, K)
+        Y = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+        gpu.gemv_rmsnorm(dev(W), dev(X).view(torch.bfloat16), dev(gamma).view(torch.bfloat16),
+                         1e-6, Y)
+        assert np.array_equal(y1.view(np.uint32), host(Y).view(np.uint32))
+
+
+def test_rmsnorm_rows_then_gemm_prefill_m33(gpu):
+    """Prefill with the norm: row norm then the small-M matmul, against the
+    oracle's norm-then-matmul (reading of the norm's rounding as for M = 1)."""
+    g = np.random.default_rng(523)
+    N, K, M = 1000, 2560, 33
+    W = qi.weight_bytes(g, N, K)
+    X = qi.activations(g, M, K)
+    gamma = qi.f32_to_bf16_bits((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    announce("rmsnorm rows + gemm M=33")
+    xh = _rmsnorm_rows_gpu(gpu, X, gamma, 1e-6)
+    y = run_gemm(W, xh.reshape(M, K), N, K)
+    Yr, A, _ = oracle.gemm_rmsnorm(W, X, gamma, 1e-6, N, K)
+    parity(y, Yr, A, "rmsnorm rows + gemm M=33")
+
+
 # ---------------------------------------------------------------------------
 # FP16 <-> INT8 KV-cache convert (jq4k_kv_quant_i8, jq4k_kv_dequant_f16)
 
