@@ -134,7 +134,9 @@ int jq4k_gemv_batched(const jq4k_gemv_desc *problems, int count, hipStream_t str
  * M == 1 runs the decode GEMV when K <= JQ4K_GEMV_MAX_K; 2 <= M <= 64 the
  * small-M MFMA kernel (W dequantised in registers, whole K per workgroup);
  * larger M the dequantise-to-LDS bf16 MFMA kernels (K <= JQ4K_MFMA_MAX_K,
- * else JQ4K_EINVAL).  M == 0 or N == 0 returns 0 without launching.  Same
+ * else JQ4K_EINVAL): 128-row tiles, or the wave-specialised 256-row tile from
+ * M = 2048, and from M = 512 when the matmul still gives every compute unit
+ * two 256 x 128 tiles.  M == 0 or N == 0 returns 0 without launching.  Same
  * pointer and alignment rules as jq4k_gemv. */
 int jq4k_gemm(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
               int M, int N, int K, hipStream_t stream);
