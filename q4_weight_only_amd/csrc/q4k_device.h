@@ -127,17 +127,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+
+// fma(scale, (float)h, c) for a binary16 half h of a 32-bit word: one
+// v_fma_mix_f32, which widens h exactly (binary16 subnormals included: the
+// kernels run with denormals preserved) and rounds once.
+__device__ __forceinline__ float fma_half_lo(float scale, uint32_t h2, float c) {
+    return __builtin_fmaf(scale, static_cast<float>(__builtin_bit_cast(half2_t, h2)[0]), c);
+}
+__device__ __forceinline__ float fma_half_hi(float scale, uint32_t h2, float c) {
+    return __builtin_fmaf(scale, static_cast<float>(__builtin_bit_cast(half2_t, h2)[1]), c);
+}
+
 // bf16 weights of one qs dword, as two packed pairs per half:
 // lo2[0] = (w0, w1), lo2[1] = (w2, w3) of the even sub-block; hi2 likewise.
+// The same values as dequant_dword_f32 rounded to bf16, with no integer to
+// float conversion: a low nibble masked in place in a 16-bit half is the
+// binary16 subnormal q * 2^-24, a high nibble q * 2^-20, so with ds scaled by
+// 2^24 (2^20; exact, a power of two) fma(ds', h, -dm) is ds * q - dm rounded
+// once.  Per 8 weights: 1 shift, 4 masks, 8 v_fma_mix_f32, 4 bf16 packs.
+// `mask` is 0x0F0F0F0F at run time (see low_quants_rt).
 __device__ __forceinline__ void dequant_dword_bf16(uint32_t v, const QuarterScales& s,
                                                    uint32_t lo2[2], uint32_t hi2[2],
                                                    uint32_t mask) {
-    float lo[4], hi[4];
-    dequant_dword_f32(v, s, lo, hi, mask);
-    lo2[0] = pack_bf16x2(lo[0], lo[1]);
-    lo2[1] = pack_bf16x2(lo[2], lo[3]);
-    hi2[0] = pack_bf16x2(hi[0], hi[1]);
-    hi2[1] = pack_bf16x2(hi[2], hi[3]);
+    const uint32_t m_lo = mask & 0x000F000Fu;   // bits 0-3 of each half
+    const uint32_t m_hi = m_lo << 4;            // bits 4-7 of each half
+    const uint32_t v8 = v >> 8;
+    const uint32_t a02 = v & m_lo, a13 = v8 & m_lo;    // even sub-block, weights 0,2 / 1,3
+    const uint32_t b02 = v & m_hi, b13 = v8 & m_hi;    // odd sub-block
+    const float s0 = s.ds0 * 0x1p24f, s1 = s.ds1 * 0x1p20f;
+    lo2[0] = pack_bf16x2(fma_half_lo(s0, a02, -s.dm0), fma_half_lo(s0, a13, -s.dm0));
+    lo2[1] = pack_bf16x2(fma_half_hi(s0, a02, -s.dm0), fma_half_hi(s0, a13, -s.dm0));
+    hi2[0] = pack_bf16x2(fma_half_lo(s1, b02, -s.dm1), fma_half_lo(s1, b13, -s.dm1));
+    hi2[1] = pack_bf16x2(fma_half_hi(s1, b02, -s.dm1), fma_half_hi(s1, b13, -s.dm1));
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), fp32 (the SwiGLU epilogues),
