@@ -222,6 +222,28 @@ def test_mfma_identity_probe(gpu, path):
         assert np.array_equal(y, ref.T[k0:k0 + rows])
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_mfma_identity_probe_special_blocks(gpu, path):
+    """The identity probe on blocks whose d and dmin are subnormal, negative,
+    zero or the largest finite binary16 values: every matmul path's own
+    dequantisation (the binary16-subnormal form of the quants, widened by
+    v_fma_mix_f32) gives the oracle's bf16 weights bit for bit (+0 and -0
+    alike)."""
+    g = np.random.default_rng(119)
+    N, K = 48, 512
+    W = _special_blocks(g, N * K // 256).reshape(N, K // 256 * 144)
+    wb = oracle.dequant_bf16(W.reshape(-1, 144)).reshape(N, K)
+    ref = (wb.astype(np.uint32) << 16).view(np.float32)
+    rows = 64 if path == "skinny" else K
+    for k0 in range(0, K, rows):
+        X = np.zeros((rows, K), np.uint16)
+        X[np.arange(rows), k0 + np.arange(rows)] = 0x3F80
+        announce(f"{path} identity probe on special blocks, k {k0}..{k0 + rows - 1}")
+        y = run_gemm(W, X, N, K, path=_path(path))
+        assert np.all(np.isfinite(y))
+        assert np.array_equal(y, ref.T[k0:k0 + rows])
+
+
 @pytest.mark.parametrize("M", [2, 33, 300])
 def test_gemm_auto_and_determinism(gpu, M):
     g = np.random.default_rng([107, M])
