@@ -327,10 +327,24 @@ hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X
     size_t lds = 0;
     int total = 0;
     b.count = count;
-    for (int i = 0; i < count; ++i) {
+    // Problems with the longest rows first (largest K, stable): their
+    // workgroups stage the most x before their first weights, and started
+    // first they no longer form the tail (decode layer: 15.3 -> 14.9 us with
+    // the down projection, K = 9728, first).  Each problem's results do not
+    // depend on the order.
+    int ord[kGemvBatchMax];
+    for (int i = 0; i < count; ++i) ord[i] = i;
+    for (int i = 1; i < count; ++i)
+        for (int j = i; j > 0 && K[ord[j]] > K[ord[j - 1]]; --j) {
+            const int o = ord[j];
+            ord[j] = ord[j - 1];
+            ord[j - 1] = o;
+        }
+    for (int slot = 0; slot < count; ++slot) {
+        const int i = ord[slot];
         const int nb = K[i] / kQK;
-        b.p[i] = {W[i], reinterpret_cast<const uint4*>(X[i]), Y[i], N[i], nb, R[i]};
-        b.first[i] = total;
+        b.p[slot] = {W[i], reinterpret_cast<const uint4*>(X[i]), Y[i], N[i], nb, R[i]};
+        b.first[slot] = total;
         total += static_cast<int>((static_cast<long>(N[i]) + R[i] - 1) / R[i]);
         lds = gemv_lds_bytes(nb, R[i]) > lds ? gemv_lds_bytes(nb, R[i]) : lds;
     }
