@@ -58,7 +58,7 @@ constexpr int kGemvMaxRows = 1024;
 constexpr int kGemvSmallRowsPerCu = 64;  // below this many rows per CU: small-matrix rule
 // blocks of W per workgroup for large single GEMVs (measured best on the
 // 151936 x 2560 LM head) and inside batched launches (measured best on the
-// seven projections of a decode layer: 979 workgroups, all resident at once)
+// seven projections of a decode layer: 1002 workgroups, all resident at once)
 constexpr int kGemvLargeBlocksPerWg = 320;
 constexpr int kGemvBatchBlocksPerWg = 400;
 constexpr size_t kGemvLdsLimit = 64 * 1024;
