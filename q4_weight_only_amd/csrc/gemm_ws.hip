@@ -3,7 +3,7 @@
 // Y (M x N) = X (M x K) . W^T with W in Q4_K (genie-ai-runtime README, "At a
 // glance": "tensor-core MMQ Q4_K prefill"), for large M.  A workgroup of
 // eight waves computes a 256 x 128 tile of Y.  The dequantisation of W is
-// vector-ALU work of about three instructions per weight, done once per tile;
+// vector-ALU work of about two instructions per weight, done once per tile;
 // instead of interleaving it with the matrix instructions in one stream, the
 // workgroup splits the roles by wave:
 //   * waves 0..3 (consumers) read operand fragments from LDS and issue
