@@ -174,6 +174,14 @@ def test_gemv_batched_decode_layer(gpu):
         assert np.array_equal(got.view(np.uint32), single.view(np.uint32)), name
         Y, A = oracle.gemm(W, X, N, K)
         parity(got, Y, A, f"batched {name}")
+    # the launch queues the problems by K; the caller's order must not matter
+    order = np.random.default_rng(110).permutation(len(probs))
+    Yp = [torch.full((1, probs[i][1]), float("nan"), dtype=torch.float32, device="cuda:0")
+          for i in order]
+    announce("gemv batched, problems in another order")
+    gpu.gemv_batched([(Wd[i], Xd[i], y) for i, y in zip(order, Yp)])
+    for i, y in zip(order, Yp):
+        assert np.array_equal(host(y).view(np.uint32), host(Yb[i]).view(np.uint32)), probs[i][0]
 
 
 # ------------------------------------------------------------ M > 1 (MFMA)
