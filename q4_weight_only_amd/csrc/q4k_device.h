@@ -129,6 +129,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 
+// The bf16 dequantisation below reads quants as binary16 subnormals: a build
+// that flushes denormals would turn them into zeros.
+#if defined(__FAST_MATH__)
+#error "q4k kernels need denormals preserved; build without -ffast-math"
+#endif
+
 // fma(scale, (float)h, c) for a binary16 half h of a 32-bit word: one
 // v_fma_mix_f32, which widens h exactly (binary16 subnormals included: the
 // kernels run with denormals preserved) and rounds once.
