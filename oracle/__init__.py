@@ -6,7 +6,8 @@ imports, links or calls anything here, and this package shares no code with it.
 
 Contents
   * ctypes wrappers over ``q4k_oracle.c`` (fp16/bf16 scalars, field unpack,
-    fp32 dequant, bf16 of the fp32 weight, fp64 contraction with sum |w*x|);
+    fp32 dequant, bf16 of the fp32 weight, binary16 of the exact weight,
+    fp64 contraction with sum |w*x|);
   * ctypes wrappers over ``kv_oracle.c`` (the FP16 <-> INT8 KV-cache convert:
     per-vector absmax scale, round-half-even codes, fp16 dequantisation);
   * ``q4k_pack`` -- an independent bit-writer that packs fields into blocks,
@@ -53,6 +54,8 @@ def lib():
         L.oracle_dequant_f32.restype = None
         L.oracle_dequant_bf16.argtypes = [u8p, ctypes.c_long, u16p]
         L.oracle_dequant_bf16.restype = None
+        L.oracle_dequant_f16.argtypes = [u8p, ctypes.c_long, u16p]
+        L.oracle_dequant_f16.restype = None
         L.oracle_gemm.argtypes = [u8p, u16p, f64p, f64p, ctypes.c_long,
                                   ctypes.c_long, ctypes.c_long]
         L.oracle_gemm.restype = ctypes.c_int
@@ -124,6 +127,15 @@ def dequant_bf16(W) -> np.ndarray:
     W, nb = _blocks(W)
     w = np.zeros(nb * QK, np.uint16)
     lib().oracle_dequant_bf16(_ptr(W, ctypes.c_uint8), nb, _ptr(w, ctypes.c_uint16))
+    return w
+
+
+def dequant_f16(W) -> np.ndarray:
+    """binary16 (one round-to-nearest-even rounding of the exact weight) as
+    uint16 bits: the weights the decode GEMV multiplies."""
+    W, nb = _blocks(W)
+    w = np.zeros(nb * QK, np.uint16)
+    lib().oracle_dequant_f16(_ptr(W, ctypes.c_uint8), nb, _ptr(w, ctypes.c_uint16))
     return w
 
 
