@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--only", default="",
+                    help="comma-separated legs to time (decode,lm_head,...); prints them "
+                         "as one JSON object instead of the benchmark line")
     ap.add_argument("--profile", action="store_true",
                     help="a few eager launches of each kernel for rocprofv3, no JSON line")
     return ap.parse_args()
@@ -628,6 +631,20 @@ def main():
 
     if args.profile:
         profile_run(torch, jq4k)
+        return
+    if args.only:
+        legs = {"decode": lambda: decode_leg(torch, jq4k, args)[3:],
+                "lm_head": lambda: lm_head_leg(torch, jq4k, args),
+                "prefill": lambda: prefill_leg(torch, jq4k, args)[1:],
+                "m33": lambda: prefill_m33_leg(torch, jq4k, args),
+                "lm_head_m512": lambda: lm_head_m512_leg(torch, jq4k, args),
+                "swiglu": lambda: swiglu_leg(torch, jq4k, args),
+                "rmsnorm": lambda: rmsnorm_leg(torch, jq4k, args),
+                "kv": lambda: kv_convert_leg(torch, jq4k, args)}
+        out = {}
+        for name in args.only.split(","):
+            out[name] = legs[name]()
+        print(json.dumps(out, default=str), flush=True)
         return
     layer, layer_bytes, copies, secs, modes, per_proj = decode_leg(torch, jq4k, args)
     gbs = layer_bytes * args.steps / secs / 1e9

@@ -28,14 +28,30 @@
  *
  * Numerics.  Y is overwritten (never accumulated into).  Results are
  * deterministic: the same inputs on the same device give bit-identical Y.
- * Every element meets |y - y_exact| <= 2e-3 * sum_k |w*x| + 1e-5 where w is
- * the fp32 dequantised weight (see jq4k_dequant_f32).  The GEMM path for M > 1
- * contracts bfloat16 tiles of w (round-to-nearest-even of the fp32 weight,
- * exactly what jq4k_dequant_bf16 returns) on the matrix cores with fp32
- * accumulation; the M = 1 path works on the 4-bit codes directly with fp32
- * accumulation.  Inf/NaN in d or dmin propagate per IEEE.  The M = 1 kernel
- * forms sum (128+q)*x per 32-weight sub-block, so activations beyond about
- * 1e35 in magnitude can overflow there.
+ * The accuracy contract is |y - y_ref| <= 2e-3 * sum_k |w*x| + 1e-5 per
+ * element, y_ref the exact contraction of the fp32 dequantised weights (see
+ * jq4k_dequant_f32).
+ *   M = 1 (jq4k_gemv, jq4k_gemv_batched, jq4k_gemv_rmsnorm, jq4k_gemm_swiglu
+ *   at M = 1): every fp32 weight is rounded to binary16 (jq4k_dequant_f16:
+ *   exact below 2^-14, relative error <= 2^-11 above), x is staged as
+ *   binary16 times a power of two per block of 256 values (exact, except
+ *   values below 2^-28 of their block's largest magnitude, which move by less
+ *   than 2^-39 of it), the products are exact and are summed in fp32 (256
+ *   per block, then the K/256 block sums in order).  So
+ *   |y - y_ref| <= (2^-11 + (K/256 + 258) * 2^-24) * sum|w*x| plus that
+ *   small-x term: at most 5.1e-4 * sum|w*x| for K <= 16384, for every block,
+ *   including blocks whose weights are zero or cancel (d*sc*q = dmin*m).
+ *   Limit: a weight of magnitude 65520 or more (d*sc*15 or dmin*m; any block
+ *   with d, dmin <= 69 stays below) is +-Inf in binary16, and its row's output
+ *   is then not finite.
+ *   M > 1: the matrix-core kernels contract bfloat16 tiles of w
+ *   (round-to-nearest-even of the fp32 weight, exactly what
+ *   jq4k_dequant_bf16 returns) with fp32 accumulation.  bfloat16 keeps 8
+ *   significant bits (relative error up to 2^-8), so adversarial blocks whose
+ *   weights all sit near a bfloat16 rounding midpoint, against activations of
+ *   one sign, can exceed the 2e-3 term by up to about 2x; randomly drawn
+ *   Q4_K weights stay far inside it.
+ * Inf/NaN in d, dmin or x propagate per IEEE.
  *
  * Ownership and execution.  All pointers are device pointers owned by the
  * caller; the library allocates no memory and keeps no state beyond a cache
@@ -301,6 +317,10 @@ int jq4k_kv_dequant_f16(const int8_t *q, const float *scale, jq4k_f16 *v, long n
  *   jq4k_dequant_bf16:  w[256*nblocks], bfloat16 of that fp32 weight
  *                       (round-to-nearest-even), the values the MFMA path
  *                       multiplies; 4-byte aligned.
+ *   jq4k_dequant_f16:   w[256*nblocks], binary16 bit patterns of that fp32
+ *                       weight (round-to-nearest-even; +-Inf from 65520 up),
+ *                       the values the M = 1 kernel multiplies; 4-byte
+ *                       aligned.
  * W must be 16-byte aligned.  nblocks == 0 returns 0; nblocks < 0 or null
  * pointers give JQ4K_EINVAL. */
 int jq4k_unpack_fields(const block_q4_K *W, long nblocks, uint8_t *q,
@@ -309,6 +329,8 @@ int jq4k_dequant_f32(const block_q4_K *W, long nblocks, float *w,
                      hipStream_t stream);
 int jq4k_dequant_bf16(const block_q4_K *W, long nblocks, jq4k_bf16 *w,
                       hipStream_t stream);
+int jq4k_dequant_f16(const block_q4_K *W, long nblocks, jq4k_f16 *w,
+                     hipStream_t stream);
 
 /* Text for a return code (static storage). */
 const char *jq4k_strerror(int code);

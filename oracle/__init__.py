@@ -6,7 +6,7 @@ imports, links or calls anything here, and this package shares no code with it.
 
 Contents
   * ctypes wrappers over ``q4k_oracle.c`` (fp16/bf16 scalars, field unpack,
-    fp32 dequant, bf16 of the fp32 weight, binary16 of the exact weight,
+    fp32 dequant, bf16 and binary16 of the fp32 weight,
     fp64 contraction with sum |w*x|);
   * ctypes wrappers over ``kv_oracle.c`` (the FP16 <-> INT8 KV-cache convert:
     per-vector absmax scale, round-half-even codes, fp16 dequantisation);
@@ -131,8 +131,8 @@ def dequant_bf16(W) -> np.ndarray:
 
 
 def dequant_f16(W) -> np.ndarray:
-    """binary16 (one round-to-nearest-even rounding of the exact weight) as
-    uint16 bits: the weights the decode GEMV multiplies."""
+    """binary16 (round-to-nearest-even) of the fp32 weights as uint16 bits:
+    the weights the decode GEMV multiplies."""
     W, nb = _blocks(W)
     w = np.zeros(nb * QK, np.uint16)
     lib().oracle_dequant_f16(_ptr(W, ctypes.c_uint8), nb, _ptr(w, ctypes.c_uint16))

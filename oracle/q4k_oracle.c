@@ -181,14 +181,15 @@ void oracle_dequant_bf16(const uint8_t *blocks, long nblocks, uint16_t *w) {
     }
 }
 
-/* The weight of the decode GEMV, which forms weights in binary16: the exact
- * value d*sc*q - dmin*m rounded once to binary16, round-to-nearest-even
- * (reading of the GEMV's weights; the pages fix no precision for them).
- * With E the integer of dequant_one (value = E * 2^-24, |E| < 2^51), the
- * rounding follows the format definition: 11 significant bits; magnitudes
- * below 2^-14 are subnormal multiples of 2^-24, so every |E| < 2^11 is
- * exact (and its bit pattern is E itself); 65504 is the largest finite value
- * and magnitudes from 65520 up round to infinity. */
+/* The weight of the decode GEMV, which multiplies binary16 weights: the fp32
+ * weight of dequant_one rounded to binary16, round-to-nearest-even (reading
+ * of the GEMV's weights; the pages fix no precision for them, and the
+ * matrix-core path's bf16 tiles are likewise a rounding of the fp32 weight).
+ * The fp32 weight is E * 2^-24 for an integer E, |E| < 2^51; the rounding
+ * follows the binary16 definition: 11 significant bits; magnitudes below
+ * 2^-14 are subnormal multiples of 2^-24, so every |E| < 2^11 is exact (and
+ * its bit pattern is E itself); 65504 is the largest finite value and
+ * magnitudes from 65520 up round to infinity. */
 static uint16_t round_exact_to_half(int64_t E) {
     uint16_t sign = E < 0 ? 0x8000u : 0u;
     uint64_t a = E < 0 ? (uint64_t)(-E) : (uint64_t)E;
@@ -215,12 +216,13 @@ static uint16_t dequant_one_half(double d, double dmin, int sc, int q, int m) {
         if (isnan(v)) return 0x7e00u;
         return (uint16_t)((signbit(v) ? 0x8000u : 0u) | 0x7c00u);
     }
-    int64_t D = (int64_t)ldexp(d, 24);
-    int64_t DM = (int64_t)ldexp(dmin, 24);
-    return round_exact_to_half(D * sc * q - DM * m);
+    /* the fp32 weight is an integer multiple of 2^-24 below 2^51 * 2^-24 */
+    float w32 = dequant_one(d, dmin, sc, q, m);
+    return round_exact_to_half((int64_t)ldexp((double)w32, 24));
 }
 
-/* w[256 * nblocks] as binary16 bit patterns: the decode GEMV's weights. */
+/* w[256 * nblocks] as binary16 bit patterns of the fp32 weights: the decode
+ * GEMV's weights. */
 void oracle_dequant_f16(const uint8_t *blocks, long nblocks, uint16_t *w) {
 #pragma omp parallel for schedule(static)
     for (long b = 0; b < nblocks; ++b) {

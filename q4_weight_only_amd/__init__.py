@@ -95,6 +95,8 @@ def _load():
         L.jq4k_dequant_f32.restype = i
         L.jq4k_dequant_bf16.argtypes = [vp, l, vp, vp]
         L.jq4k_dequant_bf16.restype = i
+        L.jq4k_dequant_f16.argtypes = [vp, l, vp, vp]
+        L.jq4k_dequant_f16.restype = i
         L.jq4k_strerror.argtypes = [i]
         L.jq4k_strerror.restype = ctypes.c_char_p
         L.jq4k_version.argtypes = []
@@ -135,8 +137,33 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _on_device(**tensors):
+    """Every tensor must live in the memory of the current GPU: the kernels
+    take raw device pointers, and a host or other-device pointer would fault
+    the GPU instead of raising here."""
+    import torch
+    dev = None
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (got one on {t.device})")
+        if dev is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the current device is {dev}")
+
+
+def _dtype(name, t, *allowed):
+    if t.dtype not in allowed:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {allowed}")
+
+
 def _shapes(W, X, Y):
     import torch
+    _on_device(W=W, X=X, Y=Y)
     if X.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError("X must hold bfloat16 values (bf16 or raw 16-bit)")
     if W.dtype != torch.uint8 or Y.dtype != torch.float32:
@@ -213,6 +240,7 @@ def gemm_batched_ws(problems, workspace, stream=None):
     arr = gemm_descs(problems)
     ptr, nbytes = None, 0
     if workspace is not None:
+        _on_device(workspace=workspace)
         ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(_load().jq4k_gemm_batched_ws(ctypes.addressof(arr), len(problems), ptr, nbytes,
                                         _stream(stream)), "jq4k_gemm_batched_ws")
@@ -233,7 +261,10 @@ def gemm(W, X, Y, stream=None, path=PATH_AUTO):
 
 def gemv_rmsnorm(W, X, gamma, eps, Y, stream=None):
     """Y = W . bf16(rmsnorm(x) * gamma) at M = 1 (jq4k_gemv_rmsnorm)."""
+    import torch
     M, N, K = _shapes(W, X, Y)
+    _on_device(gamma=gamma)
+    _dtype("gamma", gamma, torch.bfloat16, torch.int16, torch.uint16)
     if M != 1 or gamma.numel() != K:
         raise ValueError("gemv_rmsnorm takes one token and K gamma values")
     _check(_load().jq4k_gemv_rmsnorm(W.data_ptr(), X.data_ptr(), gamma.data_ptr(), float(eps),
@@ -244,6 +275,10 @@ def gemv_rmsnorm(W, X, gamma, eps, Y, stream=None):
 def rmsnorm_bf16(X, gamma, eps, Xhat, stream=None):
     """Xhat = bf16(rmsnorm(X) * gamma) row by row (jq4k_rmsnorm_bf16); X and
     Xhat are M x K bf16 (Xhat may be X), gamma K bf16 values."""
+    import torch
+    _on_device(X=X, gamma=gamma, Xhat=Xhat)
+    for name, t in (("X", X), ("gamma", gamma), ("Xhat", Xhat)):
+        _dtype(name, t, torch.bfloat16, torch.int16, torch.uint16)
     if X.dim() != 2 or Xhat.shape != X.shape or gamma.numel() != X.shape[1]:
         raise ValueError("rmsnorm_bf16 takes X and Xhat of one M x K shape and K gamma values")
     M, K = X.shape
@@ -254,7 +289,10 @@ def rmsnorm_bf16(X, gamma, eps, Xhat, stream=None):
 
 def gemm_swiglu(Wg, Wu, X, H, stream=None):
     """H = silu(X . Wg^T) * (X . Wu^T) (jq4k_gemm_swiglu); Wg and Wu alike."""
+    import torch
     M, N, K = _shapes(Wg, X, H)
+    _on_device(Wu=Wu)
+    _dtype("Wu", Wu, torch.uint8)
     if Wu.shape != Wg.shape:
         raise ValueError("gate and up matrices differ in shape")
     _check(_load().jq4k_gemm_swiglu(Wg.data_ptr(), Wu.data_ptr(), X.data_ptr(), H.data_ptr(),
@@ -265,26 +303,43 @@ def gemm_swiglu(Wg, Wu, X, H, stream=None):
 def kv_quant_i8(v, q, scale, stream=None):
     """FP16 -> INT8 KV convert: v (nvec, dim) float16 or int16/uint16 bit
     patterns, q (nvec, dim) int8, scale (nvec,) float32, all device tensors."""
+    import torch
+    _on_device(v=v, q=q, scale=scale)
+    _dtype("v", v, torch.float16, torch.int16, torch.uint16)
+    _dtype("q", q, torch.int8)
+    _dtype("scale", scale, torch.float32)
     nvec, dim = v.shape
+    if q.shape != v.shape or scale.numel() != nvec:
+        raise ValueError("kv_quant_i8 takes v and q of one shape and one scale per vector")
     _check(_load().jq4k_kv_quant_i8(v.data_ptr(), q.data_ptr(), scale.data_ptr(), nvec, dim,
                                     _stream(stream)), "jq4k_kv_quant_i8")
 
 
 def kv_dequant_f16(q, scale, v, stream=None):
     """INT8 -> FP16 KV convert (the inverse mapping of kv_quant_i8's codes)."""
+    import torch
+    _on_device(q=q, scale=scale, v=v)
+    _dtype("v", v, torch.float16, torch.int16, torch.uint16)
+    _dtype("q", q, torch.int8)
+    _dtype("scale", scale, torch.float32)
     nvec, dim = q.shape
+    if v.shape != q.shape or scale.numel() != nvec:
+        raise ValueError("kv_dequant_f16 takes q and v of one shape and one scale per vector")
     _check(_load().jq4k_kv_dequant_f16(q.data_ptr(), scale.data_ptr(), v.data_ptr(), nvec, dim,
                                        _stream(stream)), "jq4k_kv_dequant_f16")
 
 
-def _nblocks(W):
+def _nblocks(W, **outs):
+    import torch
+    _on_device(W=W, **outs)
+    _dtype("W", W, torch.uint8)
     if W.numel() % BLOCK_BYTES:
         raise ValueError("W is not a whole number of 144-byte blocks")
     return W.numel() // BLOCK_BYTES
 
 
 def unpack_fields(W, q, sc, m, stream=None):
-    nb = _nblocks(W)
+    nb = _nblocks(W, q=q, sc=sc, m=m)
     if q.numel() != nb * QK or sc.numel() != nb * 8 or m.numel() != nb * 8:
         raise ValueError("output sizes disagree with W")
     _check(_load().jq4k_unpack_fields(W.data_ptr(), nb, q.data_ptr(), sc.data_ptr(),
@@ -292,7 +347,7 @@ def unpack_fields(W, q, sc, m, stream=None):
 
 
 def dequant_f32(W, w, stream=None):
-    nb = _nblocks(W)
+    nb = _nblocks(W, w=w)
     if w.numel() != nb * QK:
         raise ValueError("output size disagrees with W")
     _check(_load().jq4k_dequant_f32(W.data_ptr(), nb, w.data_ptr(), _stream(stream)),
@@ -300,8 +355,16 @@ def dequant_f32(W, w, stream=None):
 
 
 def dequant_bf16(W, w, stream=None):
-    nb = _nblocks(W)
+    nb = _nblocks(W, w=w)
     if w.numel() != nb * QK:
         raise ValueError("output size disagrees with W")
     _check(_load().jq4k_dequant_bf16(W.data_ptr(), nb, w.data_ptr(), _stream(stream)),
            "jq4k_dequant_bf16")
+
+
+def dequant_f16(W, w, stream=None):
+    nb = _nblocks(W, w=w)
+    if w.numel() != nb * QK:
+        raise ValueError("output size disagrees with W")
+    _check(_load().jq4k_dequant_f16(W.data_ptr(), nb, w.data_ptr(), _stream(stream)),
+           "jq4k_dequant_f16")

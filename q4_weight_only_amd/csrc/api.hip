@@ -46,6 +46,7 @@ hipError_t launch_unpack_fields(const uint8_t* W, long nblocks, uint8_t* q, uint
                                 uint8_t* m, hipStream_t stream);
 hipError_t launch_dequant_f32(const uint8_t* W, long nblocks, float* w, hipStream_t stream);
 hipError_t launch_dequant_bf16(const uint8_t* W, long nblocks, uint16_t* w, hipStream_t stream);
+hipError_t launch_dequant_f16(const uint8_t* W, long nblocks, uint16_t* w, hipStream_t stream);
 }  // namespace jq4k
 
 static_assert(JQ4K_GEMM_BATCH_MAX <= jq4k::kSchedMax, "one launch per grouped matmul");
@@ -431,6 +432,13 @@ int jq4k_dequant_bf16(const block_q4_K* W, long nblocks, jq4k_bf16* w, hipStream
     if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
     return static_cast<int>(
         jq4k::launch_dequant_bf16(reinterpret_cast<const uint8_t*>(W), nblocks, w, stream));
+}
+
+int jq4k_dequant_f16(const block_q4_K* W, long nblocks, jq4k_f16* w, hipStream_t stream) {
+    const int rc = check_export(W, nblocks, w, 4);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    return static_cast<int>(
+        jq4k::launch_dequant_f16(reinterpret_cast<const uint8_t*>(W), nblocks, w, stream));
 }
 
 int jq4k_kv_quant_i8(const jq4k_f16* v, int8_t* q, float* scale, long nvec, int dim,

@@ -8,28 +8,33 @@
 // consecutive blocks of W (nb = K/256) -- one contiguous span of memory.  The
 // span is cut into tasks of one quarter block each (header + 32 quant bytes
 // = 64 weights, sub-blocks 2c and 2c+1); 256 threads sweep the tasks in
-// rounds, so lanes 4j..4j+3 of a round take the four quarters of one block
-// and every round reads 64 consecutive blocks.  A thread's quarter c = t & 3
-// never changes.
+// rounds.  Lane l of wave w takes quarter c = l / 16 of block 16 w + l % 16
+// (plus 64 per round), so every round reads 64 consecutive blocks and a
+// lane's quarter never changes.
 //
-// Arithmetic per quarter.  With s = a sub-block, the kernel uses
-//   sum_{k in s} w_k x_k = d*sc_s * sum (q_k x_k) - dmin*m_s * X_s,
-//   X_s = sum_{k in s} x_k,
-// and forms sum q_k x_k as sum (128 + q_k) x_k - 128 X_s: a byte permute puts
-// each 4-bit code q under the bf16 exponent of 128 (0x43 in the high byte
-// gives the exact bf16 value 128 + q), and v_dot2_f32_bf16 multiplies two
-// such codes by two bf16 activations per instruction with fp32 accumulation.
-// X_s is computed once per workgroup, while x is staged in LDS.  Per 8 weights:
-// 3 mask/shift, 4 permutes, 4 dot2 -- no per-weight float conversion.
+// Arithmetic.  Each weight is formed in fp32, d*sc*q - dmin*m rounded once
+// (v_fma_mix_f32 on the quants read as binary16 subnormals), then rounded to
+// binary16, and x is staged as binary16 with a power-of-two scale per
+// block of 256 values (2^-s_kb, chosen from the block's largest exponent so
+// that no value overflows).  The products then go through the matrix cores:
+// v_mfma_f32_16x16x32_f16 with A = the x of 16 blocks (row m = block m of
+// the wave) and B = their weights (column n = block n), so that the diagonal
+// D[j][j] sums block j's 256 products over the eight instructions of a
+// round; the other 240 entries are not used.  The lanes of quarter
+// c = j / 4 hold D[j][j] (accumulator j % 4) and store it, times 2^s_kb, as
+// the block's partial.  No offset or factored form is involved, so the
+// rounding error is relative to sum |w * x|: at most 2^-11 per weight from
+// the binary16 rounding, plus fp32 accumulation over 256 products and nb
+// partials (the bound is stated with the header's numerics).
 //
-// Reduction.  The four lanes of a block are summed with two DPP quad
-// permutes; one value per block goes to LDS; after all rounds each row sums
+// Reduction.  One partial per block in LDS; after all rounds each row sums
 // its nb block values in order (deterministic, no atomics).
 //
-// LDS layout of x.  x is stored as 16-byte chunks, chunk g = 32 kb + 8 c + i
-// (i = 0..3 the even sub-block, 4..7 the odd one), in groups of 8 per
-// (block, quarter) at a stride of 9 chunks (x_group_base), which keeps the
-// reads free of bank conflicts and costs no address arithmetic per chunk.
+// LDS layout of x.  Chunk (kb, c, t) -- 16 bytes, the binary16 values
+// x[256 kb + 64 c + 4 t + 0..3] then x[256 kb + 64 c + 32 + 4 t + 0..3], the
+// A operand of instruction t for quarter c -- sits at 9 (c nb + kb) + t.  The
+// stride of 9 chunks per (quarter, block) keeps the reads free of bank
+// conflicts and costs no address arithmetic per chunk.
 #include "q4k_device.h"
 
 namespace jq4k {
@@ -37,46 +42,59 @@ namespace jq4k {
 constexpr int kGemvThreads = 256;
 constexpr int kGemvBatchMax = 16;  // problems per batched launch
 
+typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
+typedef __attribute__((ext_vector_type(4))) float float4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+
 size_t gemv_lds_bytes(int nb, int R);
 
-// x in LDS: the 8 chunks of (block kb, quarter c) -- chunk g = 32 kb + 8 c
-// + i of x, i = 0..3 the even sub-block, 4..7 the odd one -- sit at 9 (4 kb
-// + c) + i.  The stride of 9 chunks spreads the groups over the banks: the
-// 64 lanes of a round read one chunk index i of 64 consecutive groups, and
-// 9 m mod 16 takes every 16-byte slot exactly four times, the conflict-free
-// case of ds_read_b128.  A thread's 8 reads are one base address plus
-// immediate offsets.
+// x in LDS (see the layout above): the 16 lanes of one quarter c read chunk
+// t of 16 consecutive blocks (consecutive groups, wrapping at the end of a
+// row), and 9 m mod 16 gives 16 consecutive groups 16 different 16-byte
+// slots of the 64 banks, the conflict-free case of ds_read_b128.
 constexpr int kXGroupStride = 9;
-__device__ __forceinline__ int x_group_base(int kb, int c) { return (4 * kb + c) * kXGroupStride; }
-__device__ __forceinline__ int x_chunk_phys(int g) { return (g >> 3) * kXGroupStride + (g & 7); }
+__device__ __forceinline__ int x_group_base(int kb, int c, int nb) {
+    return (c * nb + kb) * kXGroupStride;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+// Largest biased exponent field (bits 7..14) among the 8 bf16 values of a
+// chunk; packed 16-bit maxima.
+__device__ __forceinline__ int max_exponent8(uint4 v) {
+    constexpr uint32_t kExp = 0x7F807F80u;
+    const u16x2_t a = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.x & kExp),
+                                                __builtin_bit_cast(u16x2_t, v.y & kExp));
+    const u16x2_t b = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.z & kExp),
+                                                __builtin_bit_cast(u16x2_t, v.w & kExp));
+    const u16x2_t m = __builtin_elementwise_max(a, b);
+    return static_cast<int>(max(static_cast<uint32_t>(m[0]), static_cast<uint32_t>(m[1])) >> 7);
 }
 
-// 128 + q as bf16 for bytes 0,1 (SEL01) or 2,3 (SEL23) of a quant word
-// whose bytes hold one code each: result lanes (128 + q_lo, 128 + q_hi).
-constexpr uint32_t kBf16Exp128 = 0x43434343u;
-constexpr uint32_t kSel01 = 0x04010400u;
-constexpr uint32_t kSel23 = 0x04030402u;
-
-__device__ __forceinline__ float quant_dot8(uint32_t q4, uint32_t xa, uint32_t xb, float acc) {
-    acc = dot2_bf16(__builtin_amdgcn_perm(kBf16Exp128, q4, kSel01), xa, acc);
-    acc = dot2_bf16(__builtin_amdgcn_perm(kBf16Exp128, q4, kSel23), xb, acc);
-    return acc;
+// Maximum over the 32 lanes of each half wave: row-local DPP steps (lanes
+// 0..15 of a row), then one swizzle across the half wave's two rows.
+__device__ __forceinline__ int half_wave_max(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));  // row_ror:4
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));  // row_ror:8
+    // ds_swizzle, bit-mask mode: lane ^ 16 within each group of 32
+    return max(v, __builtin_amdgcn_ds_swizzle(v, (0x10 << 10) | 0x1F));
 }
 
-__device__ __forceinline__ float quad_sum(float v) {
-    // quad_perm [1,0,3,2] then [2,3,0,1]
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                       0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                       0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-    return v;
+// The scale exponent of a block of x whose largest exponent field is e:
+// x * 2^-s stays below 2^15 in magnitude (binary16 overflows at 65520), and
+// 2^-s is a normal fp32 (s in [-126, 114]; e = 255 is Inf or NaN, which
+// propagate).  Values below 2^(s-14) become binary16 subnormals: they lose
+// at most 2^(s-25) = 2^(e-166), i.e. less than 2^-39 of the block's largest
+// magnitude.
+__device__ __forceinline__ int block_shift(int e) { return min(max(e - 141, -126), 114); }
+
+// Two bf16 values (one word) times 2^-s (exact in fp32: a power of two),
+// each rounded once to binary16.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float scale) {
+    return pack_f16x2(bf16_lo(w) * scale, bf16_hi(w) * scale);
 }
 
 struct QuarterLoad {
@@ -91,42 +109,33 @@ __device__ __forceinline__ QuarterLoad load_quarter(const uint8_t* blk, int c) {
     return r;
 }
 
-// Contribution of one quarter block to its row: 64 weights.
-__device__ __forceinline__ float quarter_dot(const QuarterLoad& ld, int c, const uint4* xs,
-                                             int kb, float2 xsum) {
-    const float d = half_bits_to_float(ld.hdr.x & 0xFFFFu);
-    const float dmin = half_bits_to_float(ld.hdr.x >> 16);
-    uint32_t scp, mp;
-    scale_min_pair(static_cast<uint32_t>(c), ld.hdr.y, ld.hdr.z, ld.hdr.w, &scp, &mp);
-
-    float acc0 = -128.f * xsum.x;  // -128 X_(2c)
-    float acc1 = -128.f * xsum.y;  // -128 X_(2c+1)
+// D[j][j] of the round's 16 x 16 product for this lane's block j = lane % 16
+// (meaningful in the lanes of quarter j / 4): 64 weights of quarter c times
+// the matching staged x, summed over the four quarters by the instruction.
+__device__ __forceinline__ float4_t quarter_mfma(const QuarterLoad& ld, int c, const uint4* xg) {
+    const QuarterScales s = quarter_scales(ld.hdr, static_cast<uint32_t>(c));
     const uint32_t qw[8] = {ld.qa.x, ld.qa.y, ld.qa.z, ld.qa.w,
                             ld.qb.x, ld.qb.y, ld.qb.z, ld.qb.w};
-    const uint4* xg = xs + x_group_base(kb, c);
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 xl = xg[i];
-        const uint4 xh = xg[4 + i];
-        const uint32_t v0 = qw[2 * i], v1 = qw[2 * i + 1];
-        acc0 = quant_dot8(low_quants(v0), xl.x, xl.y, acc0);
-        acc0 = quant_dot8(low_quants(v1), xl.z, xl.w, acc0);
-        acc1 = quant_dot8(high_quants(v0), xh.x, xh.y, acc1);
-        acc1 = quant_dot8(high_quants(v1), xh.z, xh.w, acc1);
+    for (int i = 0; i < 8; ++i) {
+        uint32_t h[4];
+        dequant_dword_f16(qw[i], s, h);
+        const uint4 xa = xg[i];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(half8_t, xa),
+            __builtin_bit_cast(half8_t, make_uint4(h[0], h[1], h[2], h[3])), acc, 0, 0, 0);
     }
-    const float sc0 = ubyte_to_float<0>(scp), sc1 = ubyte_to_float<1>(scp);
-    const float m0 = ubyte_to_float<0>(mp), m1 = ubyte_to_float<1>(mp);
-    const float qx = sc0 * acc0 + sc1 * acc1;
-    const float mx = m0 * xsum.x + m1 * xsum.y;
-    return d * qx - dmin * mx;
+    return acc;
 }
 
-// LDS: x chunks (nb*36 x 16 B), per-sub-block sums X_s (nb*8 floats, as a
-// float2 (even, odd) per (kb, quarter)), per-block partials (R*nb floats per
-// matrix).
-constexpr int kGemvDepth = 2;  // quarter tasks in flight per thread (2 measured best: 74 VGPRs, 6 waves per SIMD)
+// LDS: x chunks (nb*36 x 16 B), the scale exponent s_kb of every block (nb
+// ints, padded to 16 B), per-block partials (R*nb floats per matrix).
+constexpr int kGemvDepth = 3;  // quarter tasks in flight per thread (3 measured best)
 constexpr int kGemvMaxK = 16384;
 constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
+
+__host__ __device__ constexpr int gemv_shift_words(int nb) { return (nb + 3) & ~3; }
 
 // One workgroup's share of a GEMV: rows [tile * R, tile * R + R) of W.
 // kPair: the same rows of a second matrix W2 follow in the task list (the
@@ -143,15 +152,18 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
                                           const uint4* __restrict__ gamma = nullptr,
                                           float eps = 0.f) {
     uint4* xs = smem;
-    float2* xsum = reinterpret_cast<float2*>(xs + nb * 4 * kXGroupStride);
-    float* part = reinterpret_cast<float*>(xsum + nb * 4);
+    int* xsh = reinterpret_cast<int*>(xs + nb * 4 * kXGroupStride);
+    float* part = reinterpret_cast<float*>(xsh + gemv_shift_words(nb));
 
     const int t = threadIdx.x;
-    const int c = t & 3;
+    const int lane = t & 63;
+    const int c = lane >> 4, j = lane & 15;
+    const bool diag = c == (j >> 2);        // this lane stores block j's partial
+    const int sel = j & 3;                  // ... from accumulator j % 4
     const long row0 = tile * R;
     const int rows = static_cast<int>(min(static_cast<long>(R), N - row0));
     const int nblk = rows * nb;                       // blocks per matrix
-    const int ntask = (kPair ? 2 : 1) * nblk * 4;
+    const int nblk_all = (kPair ? 2 : 1) * nblk;
     const uint8_t* Wt = W + row0 * nb * kBlockBytes;
     const uint8_t* Wt2 = kPair ? W2 + row0 * nb * kBlockBytes : nullptr;
     // block b of the task list: W's span, then (kPair) W2's
@@ -159,7 +171,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
         if (kPair && b >= nblk) return Wt2 + static_cast<long>(b - nblk) * kBlockBytes;
         return Wt + static_cast<long>(b) * kBlockBytes;
     };
-    const int b0 = t >> 2;  // this thread's first block; +64 per round
+    const int b0 = 16 * (t >> 6) + j;  // this lane's first block; +64 per round
 
     // Memory requests in the order they are needed (vmcnt retires in order):
     // x first, then the first kGemvDepth rounds of weights, so that staging
@@ -171,16 +183,15 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     // chunk or block: with loads under branches the compiler's count of
     // loads in flight turns pessimistic at the joins and it waits for all
     // of them, which undoes the prefetch.
-    const int nround = (ntask + kGemvThreads - 1) / kGemvThreads;   // same for every thread
-    const int nblk_all = ntask >> 2;
+    const int nround = (nblk_all + 63) / 64;   // same for every thread
     auto round_block = [&](int round) { return min(b0 + 64 * round, nblk_all - 1); };
 #pragma unroll
-    for (int j = 0; j < kGemvMaxXChunksPerThread; ++j) {
-        // j beyond the chunks of the largest K: no load at all (compile-time)
-        if (j * kGemvThreads < nxc) {
-            const int g = min(t + j * kGemvThreads, nxc - 1);
-            xv[j] = X[g];
-            if constexpr (kNorm) gv[j] = gamma[g];
+    for (int q = 0; q < kGemvMaxXChunksPerThread; ++q) {
+        // q beyond the chunks of the largest K: no load at all (compile-time)
+        if (q * kGemvThreads < nxc) {
+            const int g = min(t + q * kGemvThreads, nxc - 1);
+            xv[q] = X[g];
+            if constexpr (kNorm) gv[q] = gamma[g];
         }
     }
     QuarterLoad ld[kGemvDepth];
@@ -190,9 +201,9 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     if constexpr (kNorm) {
         float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < kGemvMaxXChunksPerThread; ++j)
-            if (t + j * kGemvThreads < nxc) {
-                const uint4 v = xv[j];
+        for (int q = 0; q < kGemvMaxXChunksPerThread; ++q)
+            if (t + q * kGemvThreads < nxc) {
+                const uint4 v = xv[q];
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -206,48 +217,64 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
         const float total = (wave_ss[0] + wave_ss[1]) + (wave_ss[2] + wave_ss[3]);
         const float r = rsqrtf(total / static_cast<float>(nb * kQK) + eps);
 #pragma unroll
-        for (int j = 0; j < kGemvMaxXChunksPerThread; ++j)
-            if (t + j * kGemvThreads < nxc) {
-                const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
-                const uint32_t q[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+        for (int q = 0; q < kGemvMaxXChunksPerThread; ++q)
+            if (t + q * kGemvThreads < nxc) {
+                const uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+                const uint32_t gm[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
                 uint32_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    o[e] = pack_bf16x2(bf16_lo(w[e]) * r * bf16_lo(q[e]),
-                                       bf16_hi(w[e]) * r * bf16_hi(q[e]));
-                xv[j] = make_uint4(o[0], o[1], o[2], o[3]);
+                    o[e] = pack_bf16x2(bf16_lo(w[e]) * r * bf16_lo(gm[e]),
+                                       bf16_hi(w[e]) * r * bf16_hi(gm[e]));
+                xv[q] = make_uint4(o[0], o[1], o[2], o[3]);
             }
     }
 
-    // Stage x; each quad of lanes holds one half sub-block (4 chunks of 8),
-    // so two DPP steps give X_s for every sub-block.
+    // Stage x as binary16.  Chunk g (x[8g .. 8g+7]) belongs to block
+    // kb = g / 32, quarter c = (g / 8) % 4, and is piece gq = g % 8 of the
+    // quarter: pieces 0..3 are even-sub-block values (bytes 0..7 of chunks
+    // t = 2 gq, 2 gq + 1), pieces 4..7 odd ones (bytes 8..15 of chunks
+    // t = 2 (gq - 4), + 1).  The 32 chunks of a block sit in 32 consecutive
+    // lanes (half a wave), which reduce the block's largest exponent among
+    // themselves; a half wave past the end of x holds repeats and stores
+    // nothing.
 #pragma unroll
-    for (int j = 0; j < kGemvMaxXChunksPerThread; ++j) {
-        const int g = t + j * kGemvThreads;
-        if (g < nxc) {
-            const uint4 v = xv[j];
-            xs[x_chunk_phys(g)] = v;
-            float sum = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
-                        ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
-            sum = quad_sum(sum);
-            if ((g & 3) == 0) reinterpret_cast<float*>(xsum)[g >> 2] = sum;
+    for (int q = 0; q < kGemvMaxXChunksPerThread; ++q) {
+        if (q * kGemvThreads < nxc) {
+            const int g = t + q * kGemvThreads;
+            const uint4 v = xv[q];
+            const int e = half_wave_max(max_exponent8(v));
+            const int sh = block_shift(e);
+            const float scale = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sh) << 23);
+            const uint32_t h0 = bf16x2_to_f16x2(v.x, scale), h1 = bf16x2_to_f16x2(v.y, scale);
+            const uint32_t h2 = bf16x2_to_f16x2(v.z, scale), h3 = bf16x2_to_f16x2(v.w, scale);
+            if (g < nxc) {
+                const int kb = g >> 5, gq = g & 7;
+                const int t0 = 2 * (gq & 3);
+                uint2* dst = reinterpret_cast<uint2*>(xs + x_group_base(kb, (g >> 3) & 3, nb) + t0) +
+                             (gq >> 2);
+                dst[0] = make_uint2(h0, h1);
+                dst[2] = make_uint2(h2, h3);
+                if ((g & 31) == 0) xsh[kb] = sh;
+            }
         }
     }
     __syncthreads();
 
     // A round past the thread's last task (the last round of a span whose
-    // task count is not a multiple of 256) computes on a repeated block and
-    // stores nothing; the four lanes of a block agree, so the quad sum sees
-    // only its own block.  The loop runs whole groups of kGemvDepth rounds
-    // without a branch; the remaining rounds follow it, without prefetch.
+    // block count is not a multiple of 64) computes on a repeated block and
+    // stores nothing; the four lanes of a block agree, so the instruction's
+    // sum over quarters sees only its own block.  The loop runs whole groups
+    // of kGemvDepth rounds without a branch; the remaining rounds follow it,
+    // without prefetch.
     const int kb_step = 64 % nb;
     int kb = b0 % nb;
     auto task = [&](int round, QuarterLoad& l, bool prefetch) {
         const int b = b0 + 64 * round;
-        const float2 xsm = xsum[kb * 4 + c];
-        float p = quarter_dot(l, c, xs, kb, xsm);
-        p = quad_sum(p);
-        if (c == 0 && b < nblk_all) part[b] = p;
+        const float4_t acc = quarter_mfma(l, c, xs + x_group_base(kb, c, nb));
+        float p = sel == 0 ? acc[0] : sel == 1 ? acc[1] : sel == 2 ? acc[2] : acc[3];
+        p = __builtin_amdgcn_ldexpf(p, xsh[kb]);
+        if (diag && b < nblk_all) part[b] = p;
         if (prefetch) l = load_quarter(blk_ptr(round_block(round + kGemvDepth)), c);
         kb += kb_step;
         if (kb >= nb) kb -= nb;
@@ -263,10 +290,10 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     __syncthreads();
     for (int r = t; r < rows; r += kGemvThreads) {
         float s = 0.f;
-        for (int j = 0; j < nb; ++j) s += part[r * nb + j];
+        for (int i = 0; i < nb; ++i) s += part[r * nb + i];
         if constexpr (kPair) {
             float u = 0.f;
-            for (int j = 0; j < nb; ++j) u += part[nblk + r * nb + j];
+            for (int i = 0; i < nb; ++i) u += part[nblk + r * nb + i];
             s = silu(s) * u;
         }
         Y[row0 + r] = s;
@@ -354,8 +381,8 @@ hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X
 }
 
 size_t gemv_lds_bytes(int nb, int R) {
-    return static_cast<size_t>(nb) * 4 * kXGroupStride * 16 + static_cast<size_t>(nb) * 4 * 8 +
-           static_cast<size_t>(R) * nb * 4;
+    return static_cast<size_t>(nb) * 4 * kXGroupStride * 16 +
+           static_cast<size_t>(gemv_shift_words(nb)) * 4 + static_cast<size_t>(R) * nb * 4;
 }
 
 hipError_t launch_gemv_rmsnorm(const uint8_t* W, const uint16_t* X, const uint16_t* gamma,

@@ -310,3 +310,43 @@ def test_kv_convert_argument_checks(L):
         assert call(V, Q + 4, S, 4, 128) == jq4k.EALIGN
         assert call(V, Q, S + 2, 4, 128) == jq4k.EALIGN
         assert call(V, Q, S, 1 << 62, 512) == jq4k.EINVAL
+
+
+def test_binding_rejects_host_tensors_before_any_launch():
+    """Host (CPU) tensors reach no kernel: every wrapper raises ValueError
+    from its checks, before the C call (the kernels would take a host
+    pointer as a device address).  No GPU is needed or touched."""
+    torch = pytest.importorskip("torch")
+    W = torch.zeros((8, 144), dtype=torch.uint8)
+    X = torch.zeros((1, 256), dtype=torch.bfloat16)
+    Y = torch.zeros((1, 8), dtype=torch.float32)
+    g = torch.zeros(256, dtype=torch.bfloat16)
+    cases = [
+        ("gemv", lambda: jq4k.gemv(W, X, Y)),
+        ("gemm", lambda: jq4k.gemm(W, X, Y)),
+        ("gemm path", lambda: jq4k.gemm(W, X, Y, path=jq4k.PATH_SKINNY)),
+        ("gemv_batched", lambda: jq4k.gemv_batched([(W, X, Y)])),
+        ("gemm_batched", lambda: jq4k.gemm_batched([(W, X, Y)])),
+        ("gemm_batched_ws", lambda: jq4k.gemm_batched_ws([(W, X, Y)], None)),
+        ("gemv_rmsnorm", lambda: jq4k.gemv_rmsnorm(W, X, g, 1e-6, Y)),
+        ("rmsnorm_bf16", lambda: jq4k.rmsnorm_bf16(X, g, 1e-6, X.clone())),
+        ("gemm_swiglu", lambda: jq4k.gemm_swiglu(W, W.clone(), X, Y)),
+        ("kv_quant_i8", lambda: jq4k.kv_quant_i8(torch.zeros((2, 8), dtype=torch.float16),
+                                                 torch.zeros((2, 8), dtype=torch.int8),
+                                                 torch.zeros(2))),
+        ("kv_dequant_f16", lambda: jq4k.kv_dequant_f16(torch.zeros((2, 8), dtype=torch.int8),
+                                                       torch.zeros(2),
+                                                       torch.zeros((2, 8), dtype=torch.float16))),
+        ("unpack_fields", lambda: jq4k.unpack_fields(W, torch.zeros(8 * 256, dtype=torch.uint8),
+                                                     torch.zeros(64, dtype=torch.uint8),
+                                                     torch.zeros(64, dtype=torch.uint8))),
+        ("dequant_f32", lambda: jq4k.dequant_f32(W, torch.zeros(8 * 256))),
+        ("dequant_bf16", lambda: jq4k.dequant_bf16(W, torch.zeros(8 * 256, dtype=torch.int16))),
+        ("dequant_f16", lambda: jq4k.dequant_f16(W, torch.zeros(8 * 256, dtype=torch.int16))),
+    ]
+    for name, call in cases:
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call()
+    # a non-contiguous view is refused too (checked first)
+    with pytest.raises(ValueError, match="contiguous"):
+        jq4k.gemv(W.t(), X, Y)

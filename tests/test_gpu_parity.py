@@ -97,6 +97,24 @@ def test_dequant_bf16_bit_exact(gpu):
     _assert_same_weights(got, ref, (got & 0x7FFF) == 0, (ref & 0x7FFF) == 0, W, "dequant_bf16")
 
 
+def test_dequant_f16_bit_exact(gpu):
+    """The decode GEMV's binary16 weights (jq4k_dequant_f16 runs its device
+    routine): one rounding of the exact weight, bit for bit, on blocks with
+    special d/dmin (subnormal, negative, zero, up to 65504: some weights
+    overflow to infinity), workload blocks and the golden blocks."""
+    g = np.random.default_rng(120)
+    W = np.concatenate([_special_blocks(g, 2000), qi.weight_bytes(g, 64, 2560).reshape(-1, 144)]
+                       + [b["bytes"][None] for b in golden_blocks.load()])
+    nb = W.shape[0]
+    announce(f"dequant_f16 nblocks={nb}")
+    w = torch.zeros(nb * 256, dtype=torch.int16, device="cuda:0")
+    gpu.dequant_f16(dev(W), w)
+    got = host(w).view(np.uint16)
+    ref = oracle.dequant_f16(W)
+    assert np.any((ref & 0x7FFF) == 0x7C00)       # overflowing weights are covered
+    _assert_same_weights(got, ref, (got & 0x7FFF) == 0, (ref & 0x7FFF) == 0, W, "dequant_f16")
+
+
 # ------------------------------------------------------------ M = 1
 
 def test_gemv_single_2560x2560(gpu):
@@ -128,17 +146,155 @@ def test_gemv_decode_layer(gpu):
 
 
 def test_gemv_one_hot_isolates_weights(gpu):
-    """x = e_k gives y = column k of the fp32 weights, exactly."""
+    """x = e_k gives y = column k of the binary16 weights the GEMV forms
+    (jq4k_dequant_f16), exactly: pins the kernel's mapping of k to block,
+    quarter, nibble and matrix-core operand position."""
     g = np.random.default_rng(104)
     N, K = 40, 512
     W = qi.weight_bytes(g, N, K)
-    w = oracle.dequant_f32(W).reshape(N, K)
+    w = oracle.dequant_f16(W).view(np.float16).astype(np.float32).reshape(N, K)
     for k in (0, 31, 32, 63, 64, 255, 256, 300, 511):
         X = np.zeros((1, K), np.uint16)
         X[0, k] = 0x3F80
         announce(f"gemv one-hot k={k}")
         y = run_gemm(W, X, N, K, path="gemv")
         assert np.array_equal(y[0], w[:, k]), k
+
+
+def _zero_weight_matrix(g, N, K, d, kind):
+    """N x K blocks that mix exactly-zero weights with ordinary ones, built by
+    the oracle-side encoder.  kind 'zero': q = 0 and m = 0 with sc = 63 and
+    dmin = d (a valid Q4_K block whose weights are all 0); 'cancel': in every
+    sub-block q is a constant c and m = c*sc with dmin = d, so d*sc*q - dmin*m
+    = 0 although both terms are large.  Rows 0..N/2 are entirely such blocks;
+    in the other rows 7 of every block's 8 sub-blocks are, and one is random
+    (the workload's d, sc, m, q)."""
+    nb = N * (K // 256)
+    dbits = pk.half_bits(np.full(nb, d))
+    sc = np.full((nb, 8), 63)
+    m = np.zeros((nb, 8), np.int64)
+    q = np.zeros((nb, 8, 32), np.int64)
+    if kind == "cancel":
+        c = g.integers(1, 4, (nb, 8))
+        sc = g.integers(1, 64, (nb, 8)) // c
+        sc[sc == 0] = 1
+        m = sc * c
+        q[:] = c[:, :, None]
+    rows_zero = N // 2
+    live = np.arange(nb) >= rows_zero * (K // 256)
+    s_live = g.integers(0, 8, nb)
+    idx = np.flatnonzero(live)
+    sc[idx, s_live[idx]] = g.integers(0, 64, idx.size)
+    m[idx, s_live[idx]] = g.integers(0, 64, idx.size)
+    q[idx, s_live[idx]] = g.integers(0, 16, (idx.size, 32))
+    return pk.pack_blocks(dbits, dbits, sc, m, q.reshape(nb, 256)).reshape(N, -1), rows_zero
+
+
+@pytest.mark.parametrize("kind", ["zero", "cancel"])
+@pytest.mark.parametrize("d", [2e-3, 1e-2, 1.0])
+@pytest.mark.parametrize("K", [2560, 9728])
+def test_gemv_zero_weight_rows(gpu, kind, d, K):
+    """Rows whose weights are exactly zero (and rows mostly so) with dense
+    N(0,1) activations, through every M = 1 entry point: jq4k_gemv,
+    jq4k_gemv_batched, jq4k_gemv_rmsnorm and jq4k_gemm_swiglu.  The oracle
+    gives y = 0 and sum|w*x| = 0 there, so the bound leaves 1e-5; the kernel's
+    binary16 weights are exactly 0, so y is exactly 0."""
+    g = np.random.default_rng([140, K, int(d * 1e4), kind == "cancel"])
+    N = 300
+    W, rows_zero = _zero_weight_matrix(g, N, K, d, kind)
+    X = qi.activations(g, 1, K)
+    assert np.all(oracle.dequant_f32(W).reshape(N, K)[:rows_zero] == 0)
+    Y, A = oracle.gemm(W, X, N, K)
+    announce(f"gemv zero-weight rows kind={kind} d={d} K={K}")
+    y = run_gemm(W, X, N, K, path="gemv")
+    parity(y, Y, A, f"gemv zero rows {kind} d={d} K={K}")
+    assert np.all(y[0, :rows_zero] == 0)
+    # the grouped launch, with an ordinary problem beside it
+    Wr = qi.weight_bytes(g, 77, 2560)
+    Xr = qi.activations(g, 1, 2560)
+    Yb = [torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda:0"),
+          torch.full((1, 77), float("nan"), dtype=torch.float32, device="cuda:0")]
+    gpu.gemv_batched([(dev(W), dev(X).view(torch.bfloat16), Yb[0]),
+                      (dev(Wr), dev(Xr).view(torch.bfloat16), Yb[1])])
+    parity(host(Yb[0]), Y, A, f"gemv batched zero rows {kind} d={d} K={K}")
+    # with the RMSNorm prologue
+    gamma = qi.f32_to_bf16_bits((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    Yn = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    gpu.gemv_rmsnorm(dev(W), dev(X).view(torch.bfloat16), dev(gamma).view(torch.bfloat16),
+                     1e-6, Yn)
+    Yr, Ar, _ = oracle.gemm_rmsnorm(W, X, gamma, 1e-6, N, K)
+    yn = host(Yn)
+    parity(yn, Yr, Ar, f"gemv rmsnorm zero rows {kind} d={d} K={K}")
+    assert np.all(yn[0, :rows_zero] == 0)
+    # SwiGLU with the zero-weight matrix as gate and as up
+    Wo = qi.weight_bytes(g, N, K)
+    _swiglu_check(gpu, W, Wo, X, N, K, f"zero-weight gate {kind} d={d}")
+    _swiglu_check(gpu, Wo, W, X, N, K, f"zero-weight up {kind} d={d}")
+
+
+def test_gemv_large_and_special_scales(gpu):
+    """Blocks with d, dmin of both signs from binary16 subnormals up to 69
+    (the largest weights, 69*63*15 = 65205, stay finite in binary16), and the
+    golden blocks: every output within the bound."""
+    g = np.random.default_rng(141)
+    N, K = 200, 2560
+    nb = N * K // 256
+    W = g.integers(0, 256, (nb, 144), dtype=np.uint8)
+    hdr = g.integers(0, 0x5450, (nb, 2)).astype(np.uint16)
+    hdr |= (g.integers(0, 2, (nb, 2)) << 15).astype(np.uint16)
+    W[:, 0:4] = hdr.view(np.uint8).reshape(nb, 4)
+    W = W.reshape(N, -1)
+    X = qi.activations(g, 1, K)
+    announce("gemv large and special scales")
+    y = run_gemm(W, X, N, K, path="gemv")
+    Y, A = oracle.gemm(W, X, N, K)
+    parity(y, Y, A, "gemv special scales")
+
+
+def test_gemv_overflowing_weight_gives_non_finite_row(gpu):
+    """A weight of 65520 or more in magnitude is +-Inf in binary16 (the
+    GEMV's documented limit): its row's output is not finite; the other rows
+    are unaffected and within the bound."""
+    g = np.random.default_rng(142)
+    N, K = 64, 512
+    W = qi.weight_bytes(g, N, K)
+    big = pk.pack_blocks(pk.half_bits(np.array([65504.0])), pk.half_bits(np.array([0.0])),
+                         np.full((1, 8), 63), np.zeros((1, 8), np.int64),
+                         np.full((1, 256), 15))
+    W[5, 0:144] = big[0]
+    X = qi.activations(g, 1, K)
+    announce("gemv overflowing weight")
+    y = run_gemm(W, X, N, K, path="gemv")
+    assert not np.isfinite(y[0, 5])
+    keep = np.arange(N) != 5
+    Y, A = oracle.gemm(W, X, N, K)
+    parity(y[:, keep], Y[:, keep], A[:, keep], "gemv rows beside an overflowing one")
+
+
+def test_gemv_activation_range(gpu):
+    """Activations beyond binary16's range and across many binades inside one
+    block of 256 (x is staged as binary16 with a power-of-two scale per
+    block), and an all-zero x: every output within the bound."""
+    g = np.random.default_rng(143)
+    N, K = 300, 2560
+    W = qi.weight_bytes(g, N, K)
+    z = g.standard_normal(K)
+    cases = {
+        "huge": z * 1e30,
+        "tiny": z * 1e-30,
+        "beyond_f16": z * 7e4,
+        "binades": z * np.exp2(g.integers(-40, 40, K)),
+        "mixed_blocks": z * np.repeat(np.exp2(g.integers(-60, 60, K // 256)), 256),
+        "zero": np.zeros(K),
+    }
+    for name, xv in cases.items():
+        X = qi.f32_to_bf16_bits(xv.astype(np.float32))[None]
+        announce(f"gemv activation range {name}")
+        y = run_gemm(W, X, N, K, path="gemv")
+        Y, A = oracle.gemm(W, X, N, K)
+        parity(y, Y, A, f"gemv activations {name}")
+        if name == "zero":
+            assert np.all(y == 0)
 
 
 def test_gemv_closed_form_constant_blocks(gpu):
