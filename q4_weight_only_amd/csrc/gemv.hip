@@ -159,7 +159,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     const int lane = t & 63;
     const int c = lane >> 4, j = lane & 15;
     const bool diag = c == (j >> 2);        // this lane stores block j's partial
-    const int sel = j & 3;                  // ... from accumulator j % 4
+    const bool sel1 = (j & 1) != 0, sel2 = (j & 2) != 0;   // ... from accumulator j % 4
     const long row0 = tile * R;
     const int rows = static_cast<int>(min(static_cast<long>(R), N - row0));
     const int nblk = rows * nb;                       // blocks per matrix
@@ -272,8 +272,9 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     auto task = [&](int round, QuarterLoad& l, bool prefetch) {
         const int b = b0 + 64 * round;
         const float4_t acc = quarter_mfma(l, c, xs + x_group_base(kb, c, nb));
-        float p = sel == 0 ? acc[0] : sel == 1 ? acc[1] : sel == 2 ? acc[2] : acc[3];
-        p = __builtin_amdgcn_ldexpf(p, xsh[kb]);
+        const float p01 = sel1 ? acc[1] : acc[0];
+        const float p23 = sel1 ? acc[3] : acc[2];
+        const float p = __builtin_amdgcn_ldexpf(sel2 ? p23 : p01, xsh[kb]);
         if (diag && b < nblk_all) part[b] = p;
         if (prefetch) l = load_quarter(blk_ptr(round_block(round + kGemvDepth)), c);
         kb += kb_step;
