@@ -97,6 +97,8 @@ typedef uint16_t jq4k_f16;  /* IEEE binary16 bit pattern */
                          /* K not a positive multiple of 256, M != 1 for */
                          /* the GEMV, K above the GEMV limit, bad path   */
 #define JQ4K_EALIGN (-2) /* W or X not 16-byte aligned, Y not 4-byte    */
+#define JQ4K_ESCRATCH (-3) /* jq4k_gemm_batched_noalloc: the problems   */
+                           /* need more than JQ4K_SCRATCH_BYTES          */
 
 /* Largest K the M = 1 kernel accepts (it keeps x in LDS). */
 #define JQ4K_GEMV_MAX_K 16384
@@ -206,6 +208,24 @@ int jq4k_gemm_batched(const jq4k_gemm_desc *problems, int count, hipStream_t str
  * JQ4K_EALIGN if it is not 256-byte aligned; nothing is launched then. */
 int jq4k_gemm_batched_ws(const jq4k_gemm_desc *problems, int count, void *workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the static device buffer jq4k_gemm_batched_noalloc uses as its
+ * split-K workspace (one per GPU, held until the process ends). */
+#define JQ4K_SCRATCH_BYTES (8u << 20)
+
+/* jq4k_gemm_batched_ws without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The split K workspace is a static
+ * device array of JQ4K_SCRATCH_BYTES per GPU; nothing is allocated (no
+ * hipMalloc, no allocating library call).  The first call on a device looks
+ * up that device's copy and clears it once on `stream`.  Same problems,
+ * results and errors as jq4k_gemm_batched_ws (bit-identical outputs), plus
+ * JQ4K_ESCRATCH, with nothing launched, when jq4k_gemm_workspace_size would
+ * exceed JQ4K_SCRATCH_BYTES for these problems (a Qwen3-4B layer at M <= 64
+ * needs 1.3 MB, its down projection alone 6.6 MB).  Every call on one GPU
+ * shares that GPU's buffer: calls that may overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. */
+int jq4k_gemm_batched_noalloc(const jq4k_gemm_desc *problems, int count, hipStream_t stream);
 
 /* Workspace bytes jq4k_gemm_batched_ws needs for these problems (0 when no
  * problem splits K; the size depends on the shapes and on the number of

@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libjq4k.so")
 HEADER = os.path.join(HERE, "..", "include", "jq4k.h")
 
-OK, EINVAL, EALIGN = 0, -1, -2
+OK, EINVAL, EALIGN, ESCRATCH = 0, -1, -2, -3
+SCRATCH_BYTES = 8 << 20
 (PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_T64, PATH_MFMA_T128, PATH_MFMA_T256, PATH_SKINNY,
  PATH_MFMA_BIG) = range(8)
 GEMV_MAX_K = 16384
@@ -75,6 +76,8 @@ def _load():
         L.jq4k_gemm_batched.restype = i
         L.jq4k_gemm_batched_ws.argtypes = [vp, i, vp, ctypes.c_size_t, vp]
         L.jq4k_gemm_batched_ws.restype = i
+        L.jq4k_gemm_batched_noalloc.argtypes = [vp, i, vp]
+        L.jq4k_gemm_batched_noalloc.restype = i
         L.jq4k_gemm_workspace_size.argtypes = [vp, i, ctypes.POINTER(ctypes.c_size_t)]
         L.jq4k_gemm_workspace_size.restype = i
         L.jq4k_kv_quant_i8.argtypes = [vp, vp, vp, l, i, vp]
@@ -244,6 +247,14 @@ def gemm_batched_ws(problems, workspace, stream=None):
         ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(_load().jq4k_gemm_batched_ws(ctypes.addressof(arr), len(problems), ptr, nbytes,
                                         _stream(stream)), "jq4k_gemm_batched_ws")
+
+
+def gemm_batched_noalloc(problems, stream=None):
+    """jq4k_gemm_batched_ws with the library's static per-GPU scratch buffer
+    as the workspace (allocates nothing; calls on one GPU must not overlap)."""
+    arr = gemm_descs(problems)
+    _check(_load().jq4k_gemm_batched_noalloc(ctypes.addressof(arr), len(problems),
+                                             _stream(stream)), "jq4k_gemm_batched_noalloc")
 
 
 def gemm(W, X, Y, stream=None, path=PATH_AUTO):

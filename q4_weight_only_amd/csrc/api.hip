@@ -2,6 +2,7 @@
 // Every check runs before the first HIP call, so rejected calls launch
 // nothing and can be exercised without a GPU.
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "jq4k.h"
@@ -50,6 +51,11 @@ hipError_t launch_dequant_f16(const uint8_t* W, long nblocks, uint16_t* w, hipSt
 }  // namespace jq4k
 
 static_assert(JQ4K_GEMM_BATCH_MAX <= jq4k::kSchedMax, "one launch per grouped matmul");
+
+// The split-K workspace of the allocation-free grouped matmul
+// (jq4k_gemm_batched_noalloc, below): one copy per GPU.
+static_assert(JQ4K_SCRATCH_BYTES % 256 == 0, "whole 256-byte lines");
+static __device__ __align__(256) uint8_t scratch[JQ4K_SCRATCH_BYTES];
 
 namespace {
 
@@ -254,6 +260,55 @@ int check_export(const void* W, long nblocks, const void* out, uintptr_t out_ali
     return 0;
 }
 
+// ---- the allocation-free grouped matmul (jq4k_gemm_batched_noalloc) ----
+// Its split-K workspace is this static device array: every GPU the library
+// runs on holds one copy, at its own address, until the process ends.  Host
+// code never uses the name as an address (on the host it is only a stand-in):
+// hipGetSymbolAddress gives each device's address once, with that device
+// current, and the kernels get that pointer.
+__global__ void scratch_clear_kernel(uint4* p, long n) {
+    for (long i = blockIdx.x * static_cast<long>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<long>(gridDim.x) * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    int rc = 0;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's scratch address, set up on the first call there: the
+// symbol's address, then one clear of the whole array on `stream` (the
+// split-K counters must start at zero; every call leaves them at zero).
+int device_scratch(hipStream_t stream, void** out) {
+    int dev = 0;
+    const hipError_t ge = hipGetDevice(&dev);
+    if (ge != hipSuccess) return static_cast<int>(ge);
+    if (dev < 0 || dev >= kMaxDevices) return JQ4K_EINVAL;
+    ScratchSlot& s = g_scratch[dev];
+    std::call_once(s.once, [&] {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            s.rc = e != hipSuccess ? static_cast<int>(e) : static_cast<int>(hipErrorInvalidSymbol);
+            return;
+        }
+        hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, stream,
+                           static_cast<uint4*>(p), static_cast<long>(JQ4K_SCRATCH_BYTES / 16));
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            s.rc = static_cast<int>(e);
+            return;
+        }
+        s.ptr = p;
+    });
+    if (s.rc != 0) return s.rc;
+    *out = s.ptr;
+    return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,6 +393,22 @@ int jq4k_gemm_batched_ws(const jq4k_gemm_desc* problems, int count, void* worksp
     if (jq4k::gemm_launch_size(a.M, a.N, a.live, a.tile, splits) > 0x7FFFFFFFL)
         return JQ4K_EINVAL;
     return launch_batch(a, splits, workspace, stream);
+}
+
+int jq4k_gemm_batched_noalloc(const jq4k_gemm_desc* problems, int count, hipStream_t stream) {
+    GemmBatchArgs a;
+    const int rc = collect_gemm_batch(problems, count, a);
+    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
+    int splits[JQ4K_GEMM_BATCH_MAX];
+    const long need = splitk_for(a, splits);
+    if (need == 0) return launch_batch(a, nullptr, nullptr, stream);
+    if (static_cast<unsigned long>(need) > JQ4K_SCRATCH_BYTES) return JQ4K_ESCRATCH;
+    if (jq4k::gemm_launch_size(a.M, a.N, a.live, a.tile, splits) > 0x7FFFFFFFL)
+        return JQ4K_EINVAL;
+    void* ws = nullptr;
+    const int src = device_scratch(stream, &ws);
+    if (src != 0) return src;
+    return launch_batch(a, splits, ws, stream);
 }
 
 int jq4k_gemv_rmsnorm(const block_q4_K* W, const jq4k_bf16* X, const jq4k_bf16* gamma,
@@ -460,6 +531,7 @@ const char* jq4k_strerror(int code) {
         case JQ4K_OK: return "success";
         case JQ4K_EINVAL: return "invalid argument";
         case JQ4K_EALIGN: return "misaligned pointer";
+        case JQ4K_ESCRATCH: return "problems need more than the static scratch buffer";
         default:
             if (code > 0) return hipGetErrorString(static_cast<hipError_t>(code));
             return "unknown error";

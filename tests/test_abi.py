@@ -350,3 +350,18 @@ def test_binding_rejects_host_tensors_before_any_launch():
     # a non-contiguous view is refused too (checked first)
     with pytest.raises(ValueError, match="contiguous"):
         jq4k.gemv(W.t(), X, Y)
+
+
+def test_noalloc_argument_checks(L):
+    """jq4k_gemm_batched_noalloc rejects what jq4k_gemm_batched_ws rejects,
+    and problems needing more than the static buffer, before any launch."""
+    assert L.jq4k_gemm_batched_noalloc(None, 0, None) == 0
+    assert L.jq4k_gemm_batched_noalloc(None, 1, None) == jq4k.EINVAL
+    assert L.jq4k_gemm_batched_noalloc(None, -1, None) == jq4k.EINVAL
+    arr = _gemm_descs((16, 16, 16, 33, 8, 100))
+    assert L.jq4k_gemm_batched_noalloc(ctypes.addressof(arr), 1, None) == jq4k.EINVAL
+    arr = _gemm_descs((17, 16, 16, 33, 8, 256))
+    assert L.jq4k_gemm_batched_noalloc(ctypes.addressof(arr), 1, None) == jq4k.EALIGN
+    big = _gemm_descs(*[(16, 16, 16, 64, 2560, 9728)] * 4)
+    assert L.jq4k_gemm_batched_noalloc(ctypes.addressof(big), 4, None) == jq4k.ESCRATCH
+    assert L.jq4k_strerror(jq4k.ESCRATCH).decode().startswith("problems need more")
