@@ -4,12 +4,25 @@
       kernel-trace statistics (rocprofv3 --kernel-trace --stats, CSV output)
       per kernel and per (kernel, grid size), as markdown.
 
+  python profile_summary.py legs TRACE_DIR FETCH_DIR WRITE_DIR OUT.json --cmd "COMMANDS"
+      per-leg kernel-trace averages and HBM bytes of a `bench.py --profile` run
+      (one run with --kernel-trace, one with --pmc FETCH_SIZE, one with --pmc
+      WRITE_SIZE).  The legs are told apart by the marker launches that
+      profile run makes (the probe-read kernel with 1000 + leg index
+      workgroups); the counters are scaled by what they read for the run's
+      512 MiB device copy.  The file records a hash of the kernel sources;
+      bench.py reports these figures only while the kernels are unchanged.
+
   python profile_summary.py traffic FETCH_DIR WRITE_DIR OUT.json --cmd "COMMAND"
       mean HBM bytes per dispatch from two counter runs (--pmc FETCH_SIZE, then
       --pmc WRITE_SIZE).  The counters are scaled by what they read for the
       512 MiB device copy that `bench.py --profile` runs first (a plain copy
       of known size).  The file records a hash of the kernel sources; bench.py
       reports the traffic only while the kernels are unchanged.
+
+  python profile_summary.py sq OUT.md DIR... --cmd "COMMAND" ... --title TITLE
+      mean SQ counter values per leg and kernel of `bench.py --profile`
+      counter runs.
 
 Reads rocprofv3 CSV output only; runs nothing on the GPU.
 """
@@ -114,6 +127,114 @@ def traffic(fetch_dir, write_dir, out, cmd):
     print(f"wrote {out}")
 
 
+MARKER_KERNEL = "probe_read_kernel"
+MARKER_BASE = 1000
+PROFILE_LEGS = ["copy_512MiB", "single", "decode", "lm_head", "m33", "prefill", "lm_head_m512"]
+
+
+def _segments(rows, key, wg_of, name_of):
+    """Split dispatch rows (sorted by `key`) at the marker launches; returns
+    {leg: [rows]}."""
+    legs = collections.defaultdict(list)
+    cur = None
+    for r in sorted(rows, key=key):
+        name = name_of(r)
+        wg = wg_of(r)
+        if MARKER_KERNEL in name and MARKER_BASE <= wg < MARKER_BASE + len(PROFILE_LEGS):
+            cur = PROFILE_LEGS[wg - MARKER_BASE]
+            continue
+        if cur is not None:
+            legs[cur].append(r)
+    return legs
+
+
+def legs_summary(trace_dir, fetch_dir, write_dir, out, cmd):
+    trace = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))))
+    tl = _segments(trace, key=lambda r: int(r["Start_Timestamp"]),
+                   wg_of=lambda r: int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]),
+                   name_of=lambda r: r["Kernel_Name"])
+
+    def counters(d):
+        rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+        return _segments(rows, key=lambda r: int(r["Dispatch_Id"]),
+                         wg_of=lambda r: int(r["Grid_Size"]) // int(r["Workgroup_Size"]),
+                         name_of=lambda r: r["Kernel_Name"])
+    fl, wl = counters(fetch_dir), counters(write_dir)
+
+    def scale(seg):
+        # the 512 MiB copies (other copies in the segment are the next leg's
+        # weight rotation, a few MB each)
+        vals = [float(r["Counter_Value"]) for r in seg.get("copy_512MiB", [])
+                if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1e5]
+        if not vals:
+            raise SystemExit("no 512 MiB copy in the counter run")
+        return COPY_BYTES / (statistics.median(vals) * 1024)   # counters: KiB per dispatch
+    fs, ws = scale(fl), scale(wl)
+    legs = {}
+    for leg in PROFILE_LEGS[1:]:
+        per = collections.defaultdict(list)
+        for r in tl.get(leg, []):
+            per[short_name(r["Kernel_Name"])].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        fetch = collections.defaultdict(list)
+        for r in fl.get(leg, []):
+            fetch[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]) * 1024 * fs)
+        write = collections.defaultdict(list)
+        for r in wl.get(leg, []):
+            write[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]) * 1024 * ws)
+        legs[leg] = {}
+        for k, v in per.items():
+            if "jq4k" not in k:
+                continue
+            legs[leg][k] = {"calls": len(v), "avg_us": round(statistics.mean(v), 3),
+                            "median_us": round(statistics.median(v), 3),
+                            "fetch_bytes": round(statistics.mean(fetch[k])) if fetch.get(k) else None,
+                            "write_bytes": round(statistics.mean(write[k])) if write.get(k) else None}
+    doc = {"command": cmd, "copy_reference_bytes": COPY_BYTES,
+           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+           "kernel_sources_sha256": kernel_source_hash(), "legs": legs}
+    with open(out, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    print(f"wrote {out}")
+
+
+def sq_summary(dirs, out, cmds, title):
+    """Mean value per dispatch of every counter in the counter runs `dirs`
+    (each a `bench.py --profile` run), per leg and jq4k kernel, as
+    markdown."""
+    table = collections.defaultdict(dict)   # (leg, kernel) -> counter -> mean
+    names = []
+    for d in dirs:
+        rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+        segs = _segments(rows, key=lambda r: int(r["Dispatch_Id"]),
+                         wg_of=lambda r: int(r["Grid_Size"]) // int(r["Workgroup_Size"]),
+                         name_of=lambda r: r["Kernel_Name"])
+        for leg, seg in segs.items():
+            per = collections.defaultdict(list)
+            for r in seg:
+                k = short_name(r["Kernel_Name"])
+                if "jq4k" in k:
+                    per[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+            for (k, c), v in per.items():
+                table[(leg, k)][c] = statistics.mean(v)
+                if c not in names:
+                    names.append(c)
+    cols = [key for key in sorted(table, key=lambda kv: PROFILE_LEGS.index(kv[0]))]
+    lines = [f"# rocprofv3 counters: {title}", "", "Commands (from the repository root):", "",
+             "```", *cmds, "```", "",
+             "Mean counter value per dispatch, in millions, per leg of `bench.py --profile` "
+             "(weights rotated over >= 1 GiB of copies, as the benchmark runs them).", "",
+             "| counter | " + " | ".join(f"{leg}: `{k.replace('jq4k::', '')}`" for leg, k in cols)
+             + " |", "|---|" + "---:|" * len(cols)]
+    for c in names:
+        lines.append(f"| {c} | " + " | ".join(
+            f"{table[key].get(c, float('nan')) / 1e6:.2f}" for key in cols) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -126,9 +247,25 @@ def main():
     c.add_argument("write_dir")
     c.add_argument("out")
     c.add_argument("--cmd", required=True)
+    g = sub.add_parser("legs")
+    g.add_argument("trace_dir")
+    g.add_argument("fetch_dir")
+    g.add_argument("write_dir")
+    g.add_argument("out")
+    g.add_argument("--cmd", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("out")
+    q.add_argument("dirs", nargs="+")
+    q.add_argument("--cmd", action="append", required=True)
+    q.add_argument("--title", required=True)
     a = ap.parse_args()
+    if a.what == "sq":
+        sq_summary(a.dirs, a.out, a.cmd, a.title)
+        return
     if a.what == "trace":
         trace_summary(a.dir, a.out, a.cmd)
+    elif a.what == "legs":
+        legs_summary(a.trace_dir, a.fetch_dir, a.write_dir, a.out, a.cmd)
     else:
         traffic(a.fetch_dir, a.write_dir, a.out, a.cmd)
 

@@ -11,6 +11,7 @@ The C entry points (include/jq4k.h) are also exposed with the same names and
 raw integer pointers in ``jq4k.raw``.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -100,6 +101,10 @@ def _load():
         L.jq4k_dequant_bf16.restype = i
         L.jq4k_dequant_f16.argtypes = [vp, l, vp, vp]
         L.jq4k_dequant_f16.restype = i
+        L.jq4k_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i, vp]
+        L.jq4k_probe_read.restype = i
+        L.jq4k_probe_mfma.argtypes = [l, vp, i, vp]
+        L.jq4k_probe_mfma.restype = i
         L.jq4k_strerror.argtypes = [i]
         L.jq4k_strerror.restype = ctypes.c_char_p
         L.jq4k_version.argtypes = []
@@ -114,10 +119,13 @@ def raw():
 
 
 def declared_symbols():
-    """Function names that include/jq4k.h declares."""
-    with open(HEADER) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(jq4k_\w+)\s*\(", text, re.M)))
+    """Function names that the headers under include/ declare."""
+    names = set()
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
+        with open(path) as f:
+            text = f.read()
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(jq4k_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def strerror(code: int) -> str:

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libjq4k.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "gemv.hip", "gemm.hip", "gemm_ws.hip", "gemm_big.hip", "gemm_skinny.hip",
-           "kv_convert.hip", "rmsnorm.hip", "exports.hip"]
+           "kv_convert.hip", "rmsnorm.hip", "exports.hip", "probes.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
