@@ -616,6 +616,21 @@ def ceilings_leg(torch, jq4k, args, traces):
     out["mfma_bf16_loop"] = {"workgroups": mwgs, "us": round(t * 1e6, 1),
                              "TFLOP_s": round(fl / t / 1e12, 1),
                              "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    # the int8-activation MMQ variant's inner loop (MFMA + per-sub-block
+    # rescale) from registers: an upper bound on its rate
+    qwgs = 2 * cus
+
+    def mq(i):
+        check(jq4k, L.jq4k_probe_mmq(iters, sink.data_ptr(), qwgs, stream_ptr(torch)))
+    t = timed(torch, mq, 5, 1, False) / 5
+    ops = iters * 2.0 * 64 * 64 * 32 * qwgs * 4
+    out["mmq_i8_inner_loop"] = {
+        "workgroups": qwgs, "us": round(t * 1e6, 1), "TOPS": round(ops / t / 1e12, 1),
+        "frac_of_int8_peak": round(ops / t / 1e12 / 5000.0, 4),
+        "frac_of_bf16_peak": round(ops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "note": "16 v_mfma_i32_16x16x32_i8 per sub-block of a 64x64 wave tile plus the fp32 "
+                "rescale of every int32 sum, operands in registers; compare with the bf16 "
+                "path's full kernel (prefill.value)"}
     del buf
     return out
 

@@ -31,6 +31,16 @@ int jq4k_probe_read(const void *p, size_t bytes, uint32_t *sink, int workgroups,
  * argument, or the launch's hipError_t. */
 int jq4k_probe_mfma(long iters, float *sink, int workgroups, hipStream_t stream);
 
+/* The inner loop of an int8-activation Q4_K matmul, from registers: per
+ * sub-block of 32 k, the sixteen v_mfma_i32_16x16x32_i8 of a wave's 64 x 64
+ * output tile (2 * 64 * 64 * 32 ops) and the fp32 rescale of each int32 sum
+ * by the sub-block's weight scale and min and the activation block's scale,
+ * `iters` sub-blocks, `workgroups` workgroups of four waves.  No loads, no
+ * code unpacking, no activation quantisation: an upper bound on the rate
+ * such a kernel reaches.  sink: device, one float per thread.  Returns 0,
+ * -1 for a bad argument, or the launch's hipError_t. */
+int jq4k_probe_mmq(long iters, float *sink, int workgroups, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

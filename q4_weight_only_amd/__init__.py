@@ -105,6 +105,8 @@ def _load():
         L.jq4k_probe_read.restype = i
         L.jq4k_probe_mfma.argtypes = [l, vp, i, vp]
         L.jq4k_probe_mfma.restype = i
+        L.jq4k_probe_mmq.argtypes = [l, vp, i, vp]
+        L.jq4k_probe_mmq.restype = i
         L.jq4k_strerror.argtypes = [i]
         L.jq4k_strerror.restype = ctypes.c_char_p
         L.jq4k_version.argtypes = []

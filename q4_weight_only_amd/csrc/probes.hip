@@ -62,6 +62,63 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(long iters,
     sink[blockIdx.x * kProbeThreads + t] = s;
 }
 
+typedef __attribute__((ext_vector_type(4))) int int4_p;
+typedef __attribute__((ext_vector_type(4))) float float4_p;
+
+// The inner loop of an int8-activation Q4_K matmul (activations quantised to
+// int8 per 32 values with one fp32 scale each, weights as their 4-bit codes):
+// a wave owns a 64 x 64 output tile in fp32; for every sub-block of 32 k it
+// issues the 16 v_mfma_i32_16x16x32_i8 of the tile (exact int32 sums over
+// the sub-block) and rescales each int32 sum into the fp32 tile,
+//   y += (d sc)_n (dx_m S) - (dmin m)_n (dx sx)_m,
+// as the sub-block's scales differ per row of W and per activation block.
+// Operands come from registers (no loads, no code unpacking, no activation
+// quantisation): an upper bound on such a kernel's rate on this chip.
+__global__ __launch_bounds__(kProbeThreads) void probe_mmq_kernel(long iters,
+                                                                  float* __restrict__ sink) {
+    const uint32_t t = threadIdx.x;
+    const long a = 0x0102030405060708L ^ t, b = 0x0807060504030201L + t;
+    float4_p y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = float4_p{0.f, 0.f, 0.f, 0.f};
+    float ds[4], dm[4], dx[4][4], dxs[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ds[i] = 1e-3f * (i + 1 + (t & 3));
+        dm[i] = 2e-3f * (i + 1);
+        for (int r = 0; r < 4; ++r) {
+            dx[i][r] = 1e-2f * (r + 1 + i);
+            dxs[i][r] = 3e-2f * (r + i);
+        }
+    }
+    for (long it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const int4_p s = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                    a + mi, b + ni, int4_p{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float f = static_cast<float>(s[r]);
+                    y[mi * 4 + ni][r] = __builtin_fmaf(ds[ni], dx[mi][r] * f,
+                                                       __builtin_fmaf(-dm[ni], dxs[mi][r],
+                                                                      y[mi * 4 + ni][r]));
+                }
+            }
+        // next sub-block: other scales
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ds[i] += 1e-7f;
+            dx[i][0] += 1e-7f;
+        }
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += y[i][0] + y[i][1] + y[i][2] + y[i][3];
+    sink[blockIdx.x * kProbeThreads + t] = acc;
+}
+
 }  // namespace jq4k
 
 extern "C" {
@@ -81,6 +138,13 @@ int jq4k_probe_read(const void* p, size_t bytes, uint32_t* sink, int workgroups,
 int jq4k_probe_mfma(long iters, float* sink, int workgroups, hipStream_t stream) {
     if (sink == nullptr || workgroups <= 0 || iters < 0) return -1;
     hipLaunchKernelGGL(jq4k::probe_mfma_kernel, dim3(workgroups), dim3(jq4k::kProbeThreads), 0,
+                       stream, iters, sink);
+    return static_cast<int>(hipGetLastError());
+}
+
+int jq4k_probe_mmq(long iters, float* sink, int workgroups, hipStream_t stream) {
+    if (sink == nullptr || workgroups <= 0 || iters < 0) return -1;
+    hipLaunchKernelGGL(jq4k::probe_mmq_kernel, dim3(workgroups), dim3(jq4k::kProbeThreads), 0,
                        stream, iters, sink);
     return static_cast<int>(hipGetLastError());
 }
