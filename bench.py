@@ -75,6 +75,15 @@ def parse():
     return ap.parse_args()
 
 
+def graph_ok(args, graph):
+    """Whether a leg replays its launches from a HIP graph (the default).
+    The M = 1 LM head is timed eagerly: its graph replays measured ~8 us per
+    launch longer than eager launches and than its kernel trace (45.6 us),
+    while launch overhead at that length is negligible.  The matrix-core
+    legs measure the same either way."""
+    return graph and not args.eager
+
+
 def timed(torch, fn, steps, warmup, use_graph):
     """Run fn(i) for warm-up, then time `steps` calls; returns seconds."""
     stream = torch.cuda.current_stream()
@@ -276,9 +285,10 @@ def lm_head_leg(torch, jq4k, args, traces):
         check(jq4k, L.jq4k_gemv(Wd[i % copies].data_ptr(), Xd.data_ptr(), Yd.data_ptr(), 1, N, K,
                                 stream_ptr(torch)))
     steps = max(10, args.steps // 10)
-    t = timed(torch, one, steps, 3, not args.eager) / steps
+    t = timed(torch, one, steps, 3, graph_ok(args, False)) / steps
     return {"workload": "Qwen3-4B-shaped LM head as Q4_K, N=151936 x K=2560, M=1, seed 4",
             "N": N, "K": K, "weight_bytes": int(W.nbytes), "rotation_copies": copies,
+            "launch": "eager" if not graph_ok(args, False) else "hip-graph",
             "us": round(t * 1e6, 2), "GB_s": round(W.nbytes / t / 1e9, 1),
             "roofline": roofline("hbm", int(W.nbytes), t, GEMV_KERNEL, "lm_head", traces,
                                  "bytes_per_launch")}
@@ -326,7 +336,7 @@ def prefill_leg(torch, jq4k, args, traces):
             check(jq4k, L.jq4k_gemm(Wc[p].data_ptr(), Xs[p].data_ptr(), Ys[p].data_ptr(), M, N,
                                     K, s))
 
-    graph = not args.eager
+    graph = graph_ok(args, True)
     steps = args.prefill_steps
     secs = timed(torch, step_batched, steps, 2, graph)
     modes = {}
@@ -421,7 +431,7 @@ def lm_head_m512_leg(torch, jq4k, args, traces):
         check(jq4k, L.jq4k_gemm(Wd[i % copies].data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K,
                                 stream_ptr(torch)))
     steps = max(5, args.prefill_steps)
-    t = timed(torch, one, steps, 2, not args.eager) / steps
+    t = timed(torch, one, steps, 2, graph_ok(args, True)) / steps
     flops = 2.0 * M * N * K
     return {"workload": "Qwen3-4B-shaped LM head as Q4_K, N=151936 x K=2560, M=512, seed 4",
             "N": N, "K": K, "M": M, "rotation_copies": copies, "us": round(t * 1e6, 1),
@@ -476,8 +486,8 @@ def swiglu_leg(torch, jq4k, args, traces):
         def grouped(i):
             check(jq4k, grouped_fn(ctypes.addressof(descs[i % copies]), 2, stream_ptr(torch)))
         steps = args.steps if M == 1 else args.prefill_steps
-        tf = timed(torch, fused, steps, 3, not args.eager) / steps
-        tg = timed(torch, grouped, steps, 3, not args.eager) / steps
+        tf = timed(torch, fused, steps, 3, graph_ok(args, True)) / steps
+        tg = timed(torch, grouped, steps, 3, graph_ok(args, True)) / steps
         if M == 1:
             out["m1"] = {"N": N, "K": K, "weight_bytes": wbytes, "fused_us": round(tf * 1e6, 2),
                          "fused_GB_s": round(wbytes / tf / 1e9, 1),
@@ -872,7 +882,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": dec["workload"] + "; one jq4k_gemv_batched launch per step (the seven "
@@ -880,6 +890,8 @@ def main():
             "weight_bytes_per_step": dec["weight_bytes_per_step"],
             "rotation_copies": dec["rotation_copies"],
             "launch": "eager" if args.eager else "hip-graph",
+            "arithmetic": "bf16 activations staged as binary16 (exact), 4-bit codes as "
+                          "binary16 on the matrix cores, fp32 sums, per-row certified bound",
             "device": torch.cuda.get_device_name(0),
         },
         "roofline": dec["roofline"],

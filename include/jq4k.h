@@ -32,18 +32,20 @@
  * element, y_ref the exact contraction of the fp32 dequantised weights (see
  * jq4k_dequant_f32).
  *   M = 1 (jq4k_gemv, jq4k_gemv_batched, jq4k_gemv_rmsnorm, jq4k_gemm_swiglu
- *   at M = 1): every fp32 weight is rounded to binary16 (jq4k_dequant_f16:
- *   exact below 2^-14, relative error <= 2^-11 above), x is staged as
- *   binary16 times a power of two per block of 256 values (exact, except
- *   values below 2^-28 of their block's largest magnitude, which move by less
- *   than 2^-39 of it), the products are exact and are summed in fp32 (256
- *   per block, then the K/256 block sums in order).  So
- *   |y - y_ref| <= (2^-11 + (K/256 + 258) * 2^-24) * sum|w*x| plus that
- *   small-x term: at most 5.1e-4 * sum|w*x| for K <= 16384, for every block,
- *   including blocks whose weights are zero or cancel (d*sc*q = dmin*m).
- *   Limit: a weight of magnitude 65520 or more (d*sc*15 or dmin*m; any block
- *   with d, dmin <= 69 stays below) is +-Inf in binary16, and its row's output
- *   is then not finite.
+ *   at M = 1): every output meets the contract.  The kernel sums each
+ *   sub-block in factored form, d*sc * sum(q x) - dmin*m * sum(x), with
+ *   exact products (x staged as binary16 times a power of two per block of
+ *   256) and fp32 sums, and bounds each row's rounding error from the same
+ *   data: at most (192 + K/256) * 2^-24 * sum over sub-blocks of
+ *   (15 |d sc| + |dmin m|) * sum |x|.  A row whose bound does not certify
+ *   2e-3 * sum|w*x| + 1e-5 against a lower bound of sum|w*x| (weights near
+ *   zero against large scales, e.g. d*sc*q = dmin*m) is recomputed in the
+ *   same launch from the fp32 weights with fp64 sums, as are all rows when
+ *   an activation is not exact in its staged binary16 (a value below 2^-31
+ *   of its block's largest magnitude, Inf, NaN).  The bound assumes the
+ *   matrix cores add exact binary16 products in fp32 with at most 2^-23
+ *   relative error per addition.  Rows of randomly drawn Q4_K blocks
+ *   certify with a margin of about 8 and are never recomputed.
  *   M > 1: the matrix-core kernels contract bfloat16 tiles of w
  *   (round-to-nearest-even of the fp32 weight, exactly what
  *   jq4k_dequant_bf16 returns) with fp32 accumulation.  bfloat16 keeps 8
@@ -337,10 +339,6 @@ int jq4k_kv_dequant_f16(const int8_t *q, const float *scale, jq4k_f16 *v, long n
  *   jq4k_dequant_bf16:  w[256*nblocks], bfloat16 of that fp32 weight
  *                       (round-to-nearest-even), the values the MFMA path
  *                       multiplies; 4-byte aligned.
- *   jq4k_dequant_f16:   w[256*nblocks], binary16 bit patterns of that fp32
- *                       weight (round-to-nearest-even; +-Inf from 65520 up),
- *                       the values the M = 1 kernel multiplies; 4-byte
- *                       aligned.
  * W must be 16-byte aligned.  nblocks == 0 returns 0; nblocks < 0 or null
  * pointers give JQ4K_EINVAL. */
 int jq4k_unpack_fields(const block_q4_K *W, long nblocks, uint8_t *q,
@@ -349,8 +347,6 @@ int jq4k_dequant_f32(const block_q4_K *W, long nblocks, float *w,
                      hipStream_t stream);
 int jq4k_dequant_bf16(const block_q4_K *W, long nblocks, jq4k_bf16 *w,
                       hipStream_t stream);
-int jq4k_dequant_f16(const block_q4_K *W, long nblocks, jq4k_f16 *w,
-                     hipStream_t stream);
 
 /* Text for a return code (static storage). */
 const char *jq4k_strerror(int code);

@@ -54,8 +54,6 @@ def lib():
         L.oracle_dequant_f32.restype = None
         L.oracle_dequant_bf16.argtypes = [u8p, ctypes.c_long, u16p]
         L.oracle_dequant_bf16.restype = None
-        L.oracle_dequant_f16.argtypes = [u8p, ctypes.c_long, u16p]
-        L.oracle_dequant_f16.restype = None
         L.oracle_gemm.argtypes = [u8p, u16p, f64p, f64p, ctypes.c_long,
                                   ctypes.c_long, ctypes.c_long]
         L.oracle_gemm.restype = ctypes.c_int
@@ -127,15 +125,6 @@ def dequant_bf16(W) -> np.ndarray:
     W, nb = _blocks(W)
     w = np.zeros(nb * QK, np.uint16)
     lib().oracle_dequant_bf16(_ptr(W, ctypes.c_uint8), nb, _ptr(w, ctypes.c_uint16))
-    return w
-
-
-def dequant_f16(W) -> np.ndarray:
-    """binary16 (round-to-nearest-even) of the fp32 weights as uint16 bits:
-    the weights the decode GEMV multiplies."""
-    W, nb = _blocks(W)
-    w = np.zeros(nb * QK, np.uint16)
-    lib().oracle_dequant_f16(_ptr(W, ctypes.c_uint8), nb, _ptr(w, ctypes.c_uint16))
     return w
 
 

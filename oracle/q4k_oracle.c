@@ -181,62 +181,6 @@ void oracle_dequant_bf16(const uint8_t *blocks, long nblocks, uint16_t *w) {
     }
 }
 
-/* The weight of the decode GEMV, which multiplies binary16 weights: the fp32
- * weight of dequant_one rounded to binary16, round-to-nearest-even (reading
- * of the GEMV's weights; the pages fix no precision for them, and the
- * matrix-core path's bf16 tiles are likewise a rounding of the fp32 weight).
- * The fp32 weight is E * 2^-24 for an integer E, |E| < 2^51; the rounding
- * follows the binary16 definition: 11 significant bits; magnitudes below
- * 2^-14 are subnormal multiples of 2^-24, so every |E| < 2^11 is exact (and
- * its bit pattern is E itself); 65504 is the largest finite value and
- * magnitudes from 65520 up round to infinity. */
-static uint16_t round_exact_to_half(int64_t E) {
-    uint16_t sign = E < 0 ? 0x8000u : 0u;
-    uint64_t a = E < 0 ? (uint64_t)(-E) : (uint64_t)E;
-    if (a < 2048) return (uint16_t)(sign | a);
-    int n = 0;
-    for (uint64_t t = a; t; t >>= 1) ++n;           /* bit length, >= 12 */
-    int shift = n - 11;
-    uint64_t keep = a >> shift;                      /* 1024 .. 2047 */
-    uint64_t rem = a & ((1ull << shift) - 1);
-    uint64_t half = 1ull << (shift - 1);
-    if (rem > half || (rem == half && (keep & 1))) ++keep;
-    if (keep == 2048) {                              /* carried into a new binade */
-        keep = 1024;
-        ++shift;
-    }
-    int biased = shift + 1;                          /* value = keep * 2^(shift-24) */
-    if (biased >= 31) return (uint16_t)(sign | 0x7c00u);
-    return (uint16_t)(sign | (biased << 10) | (keep - 1024));
-}
-
-static uint16_t dequant_one_half(double d, double dmin, int sc, int q, int m) {
-    if (!isfinite(d) || !isfinite(dmin)) {
-        double v = d * sc * q - dmin * m;
-        if (isnan(v)) return 0x7e00u;
-        return (uint16_t)((signbit(v) ? 0x8000u : 0u) | 0x7c00u);
-    }
-    /* the fp32 weight is an integer multiple of 2^-24 below 2^51 * 2^-24 */
-    float w32 = dequant_one(d, dmin, sc, q, m);
-    return round_exact_to_half((int64_t)ldexp((double)w32, 24));
-}
-
-/* w[256 * nblocks] as binary16 bit patterns of the fp32 weights: the decode
- * GEMV's weights. */
-void oracle_dequant_f16(const uint8_t *blocks, long nblocks, uint16_t *w) {
-#pragma omp parallel for schedule(static)
-    for (long b = 0; b < nblocks; ++b) {
-        const uint8_t *blk = blocks + b * BLOCK_BYTES;
-        double d = oracle_half_to_double(load_u16le(blk));
-        double dmin = oracle_half_to_double(load_u16le(blk + 2));
-        for (int i = 0; i < QK; ++i) {
-            int sc, m;
-            unpack_scale_min(blk + 4, i / 32, &sc, &m);
-            w[b * QK + i] = dequant_one_half(d, dmin, sc, quant_at(blk + 16, i), m);
-        }
-    }
-}
-
 /* ------------------------------------------------------------ contraction */
 
 /* Y[m][n] = sum_k w32[n][k] * x[m][k]   and   A[m][n] = sum_k |w32 * x|,

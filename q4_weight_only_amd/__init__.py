@@ -99,8 +99,6 @@ def _load():
         L.jq4k_dequant_f32.restype = i
         L.jq4k_dequant_bf16.argtypes = [vp, l, vp, vp]
         L.jq4k_dequant_bf16.restype = i
-        L.jq4k_dequant_f16.argtypes = [vp, l, vp, vp]
-        L.jq4k_dequant_f16.restype = i
         L.jq4k_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i, vp]
         L.jq4k_probe_read.restype = i
         L.jq4k_probe_mfma.argtypes = [l, vp, i, vp]
@@ -382,10 +380,3 @@ def dequant_bf16(W, w, stream=None):
     _check(_load().jq4k_dequant_bf16(W.data_ptr(), nb, w.data_ptr(), _stream(stream)),
            "jq4k_dequant_bf16")
 
-
-def dequant_f16(W, w, stream=None):
-    nb = _nblocks(W, w=w)
-    if w.numel() != nb * QK:
-        raise ValueError("output size disagrees with W")
-    _check(_load().jq4k_dequant_f16(W.data_ptr(), nb, w.data_ptr(), _stream(stream)),
-           "jq4k_dequant_f16")

@@ -12,7 +12,7 @@
 namespace jq4k {
 hipError_t launch_gemv(const uint8_t* W, const uint16_t* X, float* Y, int N, int K, int R,
                        hipStream_t stream);
-size_t gemv_lds_bytes(int nb, int R);
+size_t gemv_lds_bytes(int nb, int R, int mats);
 hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X,
                                float* const* Y, const int* N, const int* K, const int* R,
                                int count, hipStream_t stream);
@@ -47,7 +47,6 @@ hipError_t launch_unpack_fields(const uint8_t* W, long nblocks, uint8_t* q, uint
                                 uint8_t* m, hipStream_t stream);
 hipError_t launch_dequant_f32(const uint8_t* W, long nblocks, float* w, hipStream_t stream);
 hipError_t launch_dequant_bf16(const uint8_t* W, long nblocks, uint16_t* w, hipStream_t stream);
-hipError_t launch_dequant_f16(const uint8_t* W, long nblocks, uint16_t* w, hipStream_t stream);
 }  // namespace jq4k
 
 static_assert(JQ4K_GEMM_BATCH_MAX <= jq4k::kSchedMax, "one launch per grouped matmul");
@@ -66,9 +65,11 @@ constexpr int kGemvSmallRowsPerCu = 64;  // below this many rows per CU: small-m
 // blocks of W per workgroup for large single GEMVs (measured best on the
 // 151936 x 2560 LM head) and inside batched launches (measured best on the
 // seven projections of a decode layer: 1002 workgroups, all resident at once)
-constexpr int kGemvLargeBlocksPerWg = 320;
-constexpr int kGemvBatchBlocksPerWg = 400;
-constexpr size_t kGemvLdsLimit = 64 * 1024;
+constexpr int kGemvLargeBlocksPerWg = 480;
+constexpr int kGemvBatchBlocksPerWg = 512;
+// x staged as binary16 with its magnitudes takes 1088 B of LDS per 256
+// values (74 KB at the largest K); rows add 2 KB per group of 16
+constexpr size_t kGemvLdsLimit = 96 * 1024;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -97,22 +98,20 @@ int check_matmul(const void* W, const void* X, const void* Y, int M, int N, int 
     return 0;
 }
 
-// Rows per workgroup of the GEMV.  Small matrices take few rows per
-// workgroup so that every compute unit has loads in flight (about two
-// workgroups per compute unit); large ones take about kGemvLargeBlocksPerWg
-// blocks of W per workgroup (measured best on the 151936 x 2560 LM head).
-// Bounded by the LDS budget.
+// Rows per workgroup of the GEMV, in whole matrix-core tiles of 16 rows.
+// Matrices of up to kGemvSmallRowsPerCu rows per compute unit take one tile
+// of rows per workgroup (the most workgroups); larger ones about
+// kGemvLargeBlocksPerWg blocks of W per workgroup (measured best on the
+// 151936 x 2560 LM head: 48 rows, against 32, 64 and 128).  Bounded by the
+// LDS budget.
 int gemv_rows_per_block(int N, int K) {
     const int nb = K / jq4k::kQK;
     const long cus = cu_count();
-    long R;
-    if (N <= kGemvSmallRowsPerCu * cus)
-        R = (N + 2 * cus - 1) / (2 * cus);
-    else
-        R = (kGemvLargeBlocksPerWg + nb - 1) / nb;
-    if (R < 1) R = 1;
+    long R = 16;
+    if (N > kGemvSmallRowsPerCu * cus) R = ((kGemvLargeBlocksPerWg / nb + 8) / 16) * 16;
+    if (R < 16) R = 16;
     if (R > kGemvMaxRows) R = kGemvMaxRows;
-    while (R > 1 && jq4k::gemv_lds_bytes(nb, static_cast<int>(R)) > kGemvLdsLimit) --R;
+    while (R > 16 && jq4k::gemv_lds_bytes(nb, static_cast<int>(R), 1) > kGemvLdsLimit) R -= 16;
     return static_cast<int>(R);
 }
 
@@ -125,17 +124,17 @@ int run_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K, in
 }
 
 // Rows per workgroup inside a batched launch: the whole batch fills the GPU,
-// so each workgroup takes at most kGemvBatchBlocksPerWg blocks of W whatever
-// the row length (rounded down: the long rows' workgroups also stage the
-// most x; with the decode layer's down projection, K = 9728, at 10 rows =
-// 380 blocks instead of 11 rows = 418 the layer measured ~2% faster, 6 of 7
-// interleaved pairs on three boxes).
+// so each workgroup takes about kGemvBatchBlocksPerWg blocks of W whatever
+// the row length, in whole tiles of 16 rows (the decode layer: 48 rows at
+// K = 2560, 32 at 4096, 16 at 9728, 776 workgroups, all resident at once;
+// 384 and 768 blocks measured slower).
 int gemv_batch_rows(int N, int K) {
     const int nb = K / jq4k::kQK;
-    int R = kGemvBatchBlocksPerWg / nb;
+    // whole matrix-core tiles of 16 rows, the nearest multiple to the target
+    int R = (kGemvBatchBlocksPerWg / nb + 8) & ~15;
+    if (R < 16) R = 16;
     if (R > N) R = N;
-    if (R < 1) R = 1;
-    while (R > 1 && jq4k::gemv_lds_bytes(nb, R) > kGemvLdsLimit) --R;
+    while (R > 16 && jq4k::gemv_lds_bytes(nb, R, 1) > kGemvLdsLimit) R -= 16;
     return R;
 }
 
@@ -327,7 +326,7 @@ int jq4k_gemv_rows(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int
     const int rc = check_matmul(W, X, Y, 1, N, K);
     if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
     if (rows_per_block > 0 &&
-        jq4k::gemv_lds_bytes(K / jq4k::kQK, rows_per_block) > kGemvLdsLimit)
+        jq4k::gemv_lds_bytes(K / jq4k::kQK, rows_per_block, 1) > kGemvLdsLimit)
         return JQ4K_EINVAL;
     return run_gemv(W, X, Y, N, K, rows_per_block, stream);
 }
@@ -442,13 +441,13 @@ int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16
     const uint8_t* wg = reinterpret_cast<const uint8_t*>(Wg);
     const uint8_t* wu = reinterpret_cast<const uint8_t*>(Wu);
     if (M == 1 && K <= JQ4K_GEMV_MAX_K) {
-        // R rows of each matrix per workgroup: half a grouped launch's span,
-        // so a workgroup streams about as many blocks as one of a grouped
-        // launch (measured 8.4-8.6 us on the 9728 x 2560 pair, against 9.5 us
-        // with half the single GEMV's rows); both sets of partials fit
+        // R rows of each matrix per workgroup, whole tiles of 16: about as
+        // many blocks of the two matrices together as a workgroup of a
+        // grouped launch streams
         const int nb = K / jq4k::kQK;
-        int R = (gemv_batch_rows(N, K) + 1) / 2;
-        while (R > 1 && jq4k::gemv_lds_bytes(nb, 2 * R) > kGemvLdsLimit) --R;
+        int R = ((kGemvBatchBlocksPerWg / 2 / nb + 8) / 16) * 16;
+        if (R < 16) R = 16;
+        while (R > 16 && jq4k::gemv_lds_bytes(nb, R, 2) > kGemvLdsLimit) R -= 16;
         return static_cast<int>(jq4k::launch_gemv_swiglu(wg, wu, X, H, N, K, R, stream));
     }
     if (K > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
@@ -503,13 +502,6 @@ int jq4k_dequant_bf16(const block_q4_K* W, long nblocks, jq4k_bf16* w, hipStream
     if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
     return static_cast<int>(
         jq4k::launch_dequant_bf16(reinterpret_cast<const uint8_t*>(W), nblocks, w, stream));
-}
-
-int jq4k_dequant_f16(const block_q4_K* W, long nblocks, jq4k_f16* w, hipStream_t stream) {
-    const int rc = check_export(W, nblocks, w, 4);
-    if (rc != 0) return rc == kQuickReturn ? JQ4K_OK : rc;
-    return static_cast<int>(
-        jq4k::launch_dequant_f16(reinterpret_cast<const uint8_t*>(W), nblocks, w, stream));
 }
 
 int jq4k_kv_quant_i8(const jq4k_f16* v, int8_t* q, float* scale, long nvec, int dim,

@@ -1,7 +1,7 @@
 // exports.hip -- field unpack and dequantisation of whole blocks, for tests.
 //
 // These run the same device routines the matmul kernels run (scale_min_pair,
-// low_quants / high_quants, quarter_scales, dequant_dword_f32/_bf16/_f16), one
+// low_quants / high_quants, quarter_scales, dequant_dword_f32/_bf16), one
 // workgroup of 64 threads per block: threads 0..31 take one quant dword each
 // (quarter c = t / 8, byte offset p = 4 (t % 8)), threads 32..35 the scale
 // and min pair of quarter t - 32.
@@ -12,7 +12,7 @@ namespace jq4k {
 constexpr int kExportThreads = 64;
 constexpr unsigned kExportMaxGrid = 65536;
 
-enum class ExportKind { kFields, kF32, kBf16, kF16 };
+enum class ExportKind { kFields, kF32, kBf16 };
 
 template <ExportKind kind>
 __global__ __launch_bounds__(kExportThreads) void q4k_export_kernel(
@@ -44,14 +44,6 @@ __global__ __launch_bounds__(kExportThreads) void q4k_export_kernel(
                     wf[lo0 + i] = lo[i];
                     wf[hi0 + i] = hi[i];
                 }
-            } else if constexpr (kind == ExportKind::kF16) {
-                const QuarterScales s = quarter_scales(hdr, static_cast<uint32_t>(c));
-                uint32_t h[4];
-                dequant_dword_f16(v, s, h);
-                wh[lo0 / 2] = h[0];
-                wh[lo0 / 2 + 1] = h[1];
-                wh[hi0 / 2] = h[2];
-                wh[hi0 / 2 + 1] = h[3];
             } else {
                 const QuarterScales s = quarter_scales(hdr, static_cast<uint32_t>(c));
                 uint32_t lo2[2], hi2[2];
@@ -96,13 +88,6 @@ hipError_t launch_dequant_f32(const uint8_t* W, long nblocks, float* w, hipStrea
 
 hipError_t launch_dequant_bf16(const uint8_t* W, long nblocks, uint16_t* w, hipStream_t stream) {
     hipLaunchKernelGGL(q4k_export_kernel<ExportKind::kBf16>, dim3(export_grid(nblocks)),
-                       dim3(kExportThreads), 0, stream, W, nblocks, nullptr, nullptr, nullptr,
-                       nullptr, reinterpret_cast<uint32_t*>(w), kNibbleMask);
-    return hipGetLastError();
-}
-
-hipError_t launch_dequant_f16(const uint8_t* W, long nblocks, uint16_t* w, hipStream_t stream) {
-    hipLaunchKernelGGL(q4k_export_kernel<ExportKind::kF16>, dim3(export_grid(nblocks)),
                        dim3(kExportThreads), 0, stream, W, nblocks, nullptr, nullptr, nullptr,
                        nullptr, reinterpret_cast<uint32_t*>(w), kNibbleMask);
     return hipGetLastError();

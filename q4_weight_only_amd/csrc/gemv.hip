@@ -1,76 +1,110 @@
 // gemv.hip -- the M = 1 (decode) Q4_K GEMV for gfx950.
 //
-// y[n] = sum_k w[n][k] x[k], weights dequantised in registers and never
-// materialised (genie-ai-runtime README, "At a glance": INT4 dequant-fused
-// GEMV).  HBM-bound: each weight byte is read once (0.5625 B per weight).
+// y[n] = sum_k w[n][k] x[k], w = d*sc_s*q - dmin*m_s (genie-ai-runtime
+// README, "At a glance": INT4 dequant-fused GEMV).  HBM-bound: every byte of
+// W is read once (0.5625 B per weight); no weight is ever formed.
 //
-// Work decomposition.  A workgroup owns R consecutive rows, i.e. R*nb
-// consecutive blocks of W (nb = K/256) -- one contiguous span of memory.  The
-// span is cut into tasks of one quarter block each (header + 32 quant bytes
-// = 64 weights, sub-blocks 2c and 2c+1); 256 threads sweep the tasks in
-// rounds.  Lane l of wave w takes quarter c = l / 16 of block 16 w + l % 16
-// (plus 64 per round), so every round reads 64 consecutive blocks and a
-// lane's quarter never changes.
+// Arithmetic: the factored form on the matrix cores, certified per row.
+// Sub-block s of a block adds ds_s * S1_s - dm_s * S0_s to its row, with
+// ds = d*sc and dm = dmin*m (exact in fp32: at most 11 + 6 significant
+// bits), S1 = sum q x over the sub-block's 32 weights and S0 = sum x.  The
+// 4-bit codes go into v_mfma_f32_16x16x32_f16 as they sit in the block: a
+// nibble masked in place in a 16-bit half reads as the binary16 subnormal
+// q * 2^-24 (low nibble) or q * 2^-20 (high nibble), exactly.  x is staged
+// as binary16 times 2^-sh per block of 256 values (sh from the block's
+// largest exponent), so every product q * x is exact and the matrix cores
+// sum them in fp32.
 //
-// Arithmetic.  Each weight is formed in fp32, d*sc*q - dmin*m rounded once
-// (v_fma_mix_f32 on the quants read as binary16 subnormals), then rounded to
-// binary16, and x is staged as binary16 with a power-of-two scale per
-// block of 256 values (2^-s_kb, chosen from the block's largest exponent so
-// that no value overflows).  The products then go through the matrix cores:
-// v_mfma_f32_16x16x32_f16 with A = the x of 16 blocks (row m = block m of
-// the wave) and B = their weights (column n = block n), so that the diagonal
-// D[j][j] sums block j's 256 products over the eight instructions of a
-// round; the other 240 entries are not used.  The lanes of quarter
-// c = j / 4 hold D[j][j] (accumulator j % 4) and store it, times 2^s_kb, as
-// the block's partial.  No offset or factored form is involved, so the
-// rounding error is relative to sum |w * x|: at most 2^-11 per weight from
-// the binary16 rounding, plus fp32 accumulation over 256 products and nb
-// partials (the bound is stated with the header's numerics).
+// The factored form loses accuracy where ds*S1 and dm*S0 cancel (weights
+// near zero against large scales), so every row also carries a bound on its
+// own rounding error and a lower bound on sum |w x|, and a row whose bound
+// does not certify the accuracy contract is recomputed exactly (below).
+// Rows of randomly drawn blocks certify with a margin of about 8.
 //
-// Reduction.  One partial per block in LDS; after all rounds each row sums
-// its nb block values in order (deterministic, no atomics).
+// Matrix-core tile: 16 rows of W at one block column kb.  B column n is
+// block (row n, kb); lane 16c + n holds 8 codes of its quarter c (the
+// quarter's code bytes pair sub-blocks 2c and 2c+1).  Row m < 8 of A is
+// sub-block m of x: lane 16c + m supplies its values where sub-block m is
+// the one k-group c covers in the instruction (2c for the instructions on
+// low nibbles, 2c+1 for high) and zeros otherwise; rows 8..15 are zero.
+// Eight instructions per tile (4 code pairs x low/high nibbles) leave
+// D[s][n] = S1_s of block n (scaled) in lane 16 (s / 4) + n, accumulator
+// s % 4: lanes 0..31 ("S lanes") hold sub-blocks 0..3 / 4..7 of block n.
 //
-// LDS layout of x.  Chunk (kb, c, t) -- 16 bytes, the binary16 values
-// x[256 kb + 64 c + 4 t + 0..3] then x[256 kb + 64 c + 32 + 4 t + 0..3], the
-// A operand of instruction t for quarter c -- sits at 9 (c nb + kb) + t.  The
-// stride of 9 chunks per (quarter, block) keeps the reads free of bank
-// conflicts and costs no address arithmetic per chunk.
+// Per tile, every S lane combines its four sub-blocks: a = dm S0,
+// r = ds D - a, and sums r (the output) and |r| (L: sum over sub-blocks of
+// |sum w x| <= sum |w x|).  Lanes 32..63 ("T lanes", D = 0) sum the error
+// scale B = sum over sub-blocks of (15 |ds| + |dm|) T0 with T0 = sum |x|,
+// which bounds sum (|ds| q + |dm|) |x| and with it every rounding error.
+// S0 and T0 are staged with x.  Each tile's sums are scaled by 2^sh_kb.
+//
+// Certificate.  With u = 2^-24, every rounding error of the row is at most
+// E = (192 + nb) u B: the matrix cores' fp32 sums (at most 2u per addition
+// of 32 exact products: 64u, taken twice), the staged S0 and T0 (9
+// additions), the combine (3 roundings) and the row's sums (fewer than
+// 8 + nb additions deep).  The row is accepted when
+//     E <= 1.9e-3 * max(L - 2E, |y| - E) + 0.99e-5,
+// the slack to 2e-3 and 1e-5 covering w against the fp32 weight (u |w|) and
+// the rounding of E itself.  Otherwise -- and for every row when some x is
+// not exact in its staged binary16 (values below 2^-31 of their block's
+// largest magnitude, Inf, NaN) -- one wave recomputes the row: each fp32
+// weight (d*sc*q - dmin*m rounded once) times x, summed in fp64, rounded
+// once to fp32.
+//
+// Work decomposition.  A workgroup owns R consecutive rows (ceil(R/16)
+// groups of 16) of each of its matrices.  Its tiles (group g, column kb) are
+// numbered g*nb + kb and wave w takes tiles w, w+4, w+8, ..., so the four
+// waves sweep the same 16 rows at neighbouring columns; three tiles per lane
+// are in flight.  Within a group a wave's tiles share kb mod 4 (its
+// "class"); each lane sums its tiles of the group in order and leaves the
+// sums in LDS under (row, class), and each row adds its four classes in
+// order: deterministic, and the same bits whatever R or the launch (no
+// atomics on values).
+//
+// LDS layout of the staged x, per block kb (40 chunks of 16 B): chunk
+// 5 s + p holds the binary16 x of sub-block s, values 8p + {0,2,1,3,4,6,5,7}
+// (the order of the codes as masked from two consecutive code dwords: bytes
+// 0, 2, 1, 3 of each); the stride of 5 puts the four sub-blocks an
+// instruction reads on different banks.
 #include "q4k_device.h"
 
 namespace jq4k {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvBatchMax = 16;  // problems per batched launch
+constexpr int kGemvDepth = 3;      // tiles in flight per lane
+constexpr int kGemvMaxK = 16384;
+constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
+constexpr int kSubChunks = 5;   // LDS chunk stride of a sub-block's 4 chunks of x
+constexpr int kXaChunks = 40;   // LDS chunks per block of x (8 sub-blocks)
 
 typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
 typedef __attribute__((ext_vector_type(4))) float float4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 
-size_t gemv_lds_bytes(int nb, int R);
+__host__ __device__ constexpr int gemv_shift_words(int nb) { return (nb + 3) & ~3; }
+__host__ __device__ constexpr int gemv_groups(int R) { return (R + 15) >> 4; }
 
-// x in LDS (see the layout above): the 16 lanes of one quarter c read chunk
-// t of 16 consecutive blocks (consecutive groups, wrapping at the end of a
-// row), and 9 m mod 16 gives 16 consecutive groups 16 different 16-byte
-// slots of the 64 banks, the conflict-free case of ds_read_b128.
-constexpr int kXGroupStride = 9;
-__device__ __forceinline__ int x_group_base(int kb, int c, int nb) {
-    return (c * nb + kb) * kXGroupStride;
+// LDS of a workgroup with R rows of each of `mats` matrices (bytes):
+//   staged x              nb * 40 chunks
+//   zeros                 4 chunks (the A values of inactive lanes)
+//   S0[8], T0[8]          per block, 16 floats
+//   sh                    per block, one int (padded to 16 B)
+//   row partials          mats * 16 ceil(R/16) rows x 4 classes x 4 lane slots x 2 floats
+//   row results           mats * R floats
+//   recompute list        1 + mats * R ints (count, then rows)
+__host__ __device__ constexpr size_t gemv_lds_layout(int nb, int R, int mats) {
+    return static_cast<size_t>(nb) * kXaChunks * 16 + 64 + static_cast<size_t>(nb) * 64 +
+           static_cast<size_t>(gemv_shift_words(nb)) * 4 +
+           static_cast<size_t>(mats) * gemv_groups(R) * 16 * 16 * 8 +
+           static_cast<size_t>(mats) * R * 4 + (1 + static_cast<size_t>(mats) * R) * 4;
 }
+
+size_t gemv_lds_bytes(int nb, int R, int mats) { return gemv_lds_layout(nb, R, mats); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
-
-// Largest biased exponent field (bits 7..14) among the 8 bf16 values of a
-// chunk; packed 16-bit maxima.
-__device__ __forceinline__ int max_exponent8(uint4 v) {
-    constexpr uint32_t kExp = 0x7F807F80u;
-    const u16x2_t a = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.x & kExp),
-                                                __builtin_bit_cast(u16x2_t, v.y & kExp));
-    const u16x2_t b = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.z & kExp),
-                                                __builtin_bit_cast(u16x2_t, v.w & kExp));
-    const u16x2_t m = __builtin_elementwise_max(a, b);
-    return static_cast<int>(max(static_cast<uint32_t>(m[0]), static_cast<uint32_t>(m[1])) >> 7);
-}
 
 // Maximum over the 32 lanes of each half wave: row-local DPP steps (lanes
 // 0..15 of a row), then one swizzle across the half wave's two rows.
@@ -83,62 +117,80 @@ __device__ __forceinline__ int half_wave_max(int v) {
     return max(v, __builtin_amdgcn_ds_swizzle(v, (0x10 << 10) | 0x1F));
 }
 
-// The scale exponent of a block of x whose largest exponent field is e:
-// x * 2^-s stays below 2^15 in magnitude (binary16 overflows at 65520), and
-// 2^-s is a normal fp32 (s in [-126, 114]; e = 255 is Inf or NaN, which
-// propagate).  Values below 2^(s-14) become binary16 subnormals: they lose
-// at most 2^(s-25) = 2^(e-166), i.e. less than 2^-39 of the block's largest
-// magnitude.
-__device__ __forceinline__ int block_shift(int e) { return min(max(e - 141, -126), 114); }
-
-// Two bf16 values (one word) times 2^-s (exact in fp32: a power of two),
-// each rounded once to binary16.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float scale) {
-    return pack_f16x2(bf16_lo(w) * scale, bf16_hi(w) * scale);
+// Sum over the four lanes of a quad, the same bits in all four: each lane
+// adds its partner's value, then the other pair's sum (fp32 addition
+// commutes, so the four results agree).
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    return v;
 }
 
-struct QuarterLoad {
-    uint4 hdr, qa, qb;
+// The scale exponent of a block of x whose largest exponent field is e:
+// x * 2^-sh stays below 2^15 in magnitude (binary16 overflows at 65520),
+// and 2^-sh is a normal fp32 (sh in [-126, 114]; e = 255 is Inf or NaN).
+__device__ __forceinline__ int block_shift(int e) { return min(max(e - 141, -126), 114); }
+__device__ __forceinline__ float pow2f(int e) {
+    return __builtin_bit_cast(float, static_cast<uint32_t>(127 + e) << 23);
+}
+
+struct TileLoad {
+    uint4 hdr, qa, qb;   // header; code dwords 0..3 and 4..7 of the lane's quarter
 };
 
-__device__ __forceinline__ QuarterLoad load_quarter(const uint8_t* blk, int c) {
-    QuarterLoad r;
-    r.hdr = load16(blk);
-    r.qa = load16(blk + 16 + 32 * c);
-    r.qb = load16(blk + 32 + 32 * c);
-    return r;
-}
-
-// D[j][j] of the round's 16 x 16 product for this lane's block j = lane % 16
-// (meaningful in the lanes of quarter j / 4): 64 weights of quarter c times
-// the matching staged x, summed over the four quarters by the instruction.
-__device__ __forceinline__ float4_t quarter_mfma(const QuarterLoad& ld, int c, const uint4* xg) {
-    const QuarterScales s = quarter_scales(ld.hdr, static_cast<uint32_t>(c));
-    const uint32_t qw[8] = {ld.qa.x, ld.qa.y, ld.qa.z, ld.qa.w,
-                            ld.qb.x, ld.qb.y, ld.qb.z, ld.qb.w};
-    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+// One row recomputed by one wave, lane l taking sub-block l / 8, weights
+// 4 (l % 8) .. + 3 of every block: each fp32 weight (one rounding of
+// d*sc*q - dmin*m) times x, summed in fp64 (the products of a 24-bit weight
+// and an 8-bit activation are exact there), the lanes' sums combined in a
+// fixed butterfly and rounded once to fp32.  kNorm: x is the normalised
+// activation, recomputed exactly as it was staged.
+template <bool kNorm>
+__device__ float exact_row(const uint8_t* rowp, int nb, const uint4* __restrict__ X,
+                           const uint4* __restrict__ gamma, float rnorm, int lane) {
+    const int s = lane >> 3, i0 = 4 * (lane & 7);
+    const uint16_t* Xh = reinterpret_cast<const uint16_t*>(X);
+    const uint16_t* Gh = reinterpret_cast<const uint16_t*>(gamma);
+    double acc = 0.0;
+    for (int kb = 0; kb < nb; ++kb) {
+        const uint8_t* blk = rowp + static_cast<long>(kb) * kBlockBytes;
+        const uint4 hdr = load16(blk);
+        const uint32_t qd = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * (s >> 1) + i0);
+        const uint2 xw = *reinterpret_cast<const uint2*>(Xh + kQK * kb + 32 * s + i0);
+        float xs[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y)};
+        if constexpr (kNorm) {
+            const uint2 gw = *reinterpret_cast<const uint2*>(Gh + kQK * kb + 32 * s + i0);
+            const uint32_t o0 = pack_bf16x2(xs[0] * rnorm * bf16_lo(gw.x),
+                                            xs[1] * rnorm * bf16_hi(gw.x));
+            const uint32_t o1 = pack_bf16x2(xs[2] * rnorm * bf16_lo(gw.y),
+                                            xs[3] * rnorm * bf16_hi(gw.y));
+            xs[0] = bf16_lo(o0);
+            xs[1] = bf16_hi(o0);
+            xs[2] = bf16_lo(o1);
+            xs[3] = bf16_hi(o1);
+        }
+        const float d = half_bits_to_float(hdr.x & 0xFFFFu);
+        const float dmin = half_bits_to_float(hdr.x >> 16);
+        uint32_t scp, mp;
+        scale_min_pair(static_cast<uint32_t>(s >> 1), hdr.y, hdr.z, hdr.w, &scp, &mp);
+        const uint32_t odd = static_cast<uint32_t>(s & 1);
+        const float ds = d * static_cast<float>((scp >> (8 * odd)) & 0xFFu);
+        const float dm = dmin * static_cast<float>((mp >> (8 * odd)) & 0xFFu);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t h[4];
-        dequant_dword_f16(qw[i], s, h);
-        const uint4 xa = xg[i];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            __builtin_bit_cast(half8_t, xa),
-            __builtin_bit_cast(half8_t, make_uint4(h[0], h[1], h[2], h[3])), acc, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t q = (qd >> (8 * e + 4 * odd)) & 0xFu;
+            const float w = __builtin_fmaf(ds, static_cast<float>(q), -dm);
+            acc = __builtin_fma(static_cast<double>(w), static_cast<double>(xs[e]), acc);
+        }
     }
-    return acc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    return static_cast<float>(acc);
 }
-
-// LDS: x chunks (nb*36 x 16 B), the scale exponent s_kb of every block (nb
-// ints, padded to 16 B), per-block partials (R*nb floats per matrix).
-constexpr int kGemvDepth = 3;  // quarter tasks in flight per thread (3 measured best)
-constexpr int kGemvMaxK = 16384;
-constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
-
-__host__ __device__ constexpr int gemv_shift_words(int nb) { return (nb + 3) & ~3; }
 
 // One workgroup's share of a GEMV: rows [tile * R, tile * R + R) of W.
-// kPair: the same rows of a second matrix W2 follow in the task list (the
+// kPair: the same rows of a second matrix W2 follow in the tile list (the
 // gate and up projections of an MLP), and the row's output is
 // silu(gate) * up (SwiGLU) instead of the dot product.
 // kNorm: x is RMS-normalised while it is staged, x_hat = bf16(x / sqrt(
@@ -151,40 +203,50 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
                                           int N, int nb, int R, long tile, uint4* smem,
                                           const uint4* __restrict__ gamma = nullptr,
                                           float eps = 0.f) {
-    uint4* xs = smem;
-    int* xsh = reinterpret_cast<int*>(xs + nb * 4 * kXGroupStride);
-    float* part = reinterpret_cast<float*>(xsh + gemv_shift_words(nb));
-
+    constexpr int kMats = kPair ? 2 : 1;
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int c = lane >> 4, j = lane & 15;
-    const bool diag = c == (j >> 2);        // this lane stores block j's partial
-    const bool sel1 = (j & 1) != 0, sel2 = (j & 2) != 0;   // ... from accumulator j % 4
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const long row0 = tile * R;
     const int rows = static_cast<int>(min(static_cast<long>(R), N - row0));
-    const int nblk = rows * nb;                       // blocks per matrix
-    const int nblk_all = (kPair ? 2 : 1) * nblk;
-    const uint8_t* Wt = W + row0 * nb * kBlockBytes;
-    const uint8_t* Wt2 = kPair ? W2 + row0 * nb * kBlockBytes : nullptr;
-    // block b of the task list: W's span, then (kPair) W2's
-    auto blk_ptr = [&](int b) {
-        if (kPair && b >= nblk) return Wt2 + static_cast<long>(b - nblk) * kBlockBytes;
-        return Wt + static_cast<long>(b) * kBlockBytes;
-    };
-    const int b0 = 16 * (t >> 6) + j;  // this lane's first block; +64 per round
+    const int G = gemv_groups(rows);            // row groups per matrix here
+    const int Gt = kMats * G;
+    const int Gl = gemv_groups(R);              // ... in a full workgroup (LDS carve)
 
-    // Memory requests in the order they are needed (vmcnt retires in order):
-    // x first, then the first kGemvDepth rounds of weights, so that staging
-    // x waits only for x and each round waits only for its own weights.
+    uint4* xa = smem;
+    uint4* zero4 = xa + nb * kXaChunks;
+    float* zs = reinterpret_cast<float*>(zero4 + 4);
+    int* xsh = reinterpret_cast<int*>(zs + nb * 16);
+    float2* part = reinterpret_cast<float2*>(xsh + gemv_shift_words(nb));
+    float* yrow = reinterpret_cast<float*>(part + kMats * Gl * 16 * 16);
+    int* flist = reinterpret_cast<int*>(yrow + kMats * R);
+
+    // Lane roles.  As an A/B lane: k-group c, row / column m of the tile.
+    const int c = lane >> 4, m = lane & 15;
+    const bool act_lo = m == 2 * c, act_hi = m == 2 * c + 1;   // rows 8..15: never
+    const int zero_chunk = nb * kXaChunks;
+    const int alo_base = act_lo ? kSubChunks * m : zero_chunk;
+    const int ahi_base = act_hi ? kSubChunks * m : zero_chunk;
+    const int alo_stride = act_lo ? kXaChunks : 0;
+    const int ahi_stride = act_hi ? kXaChunks : 0;
+    // As a D lane: S (lanes 0..31: D = S1) or T (32..63: D = 0), sub-blocks
+    // 4 half + 0..3 of block (row m, kb)
+    const bool laneT = lane >= 32;
+    const bool half = ((lane >> 4) & 1) != 0;
+    const int zoff = (laneT ? 8 : 0) + (half ? 4 : 0);
+    // scale bytes of sub-blocks 4 half + 0..3 (Q4_K packing): half 0 the low
+    // six bits of scales[i] and scales[4+i]; half 1 the nibbles of
+    // scales[8+i] plus bits 6..7 of scales[i] and scales[4+i] as bits 4..5.
+    // One branch-free formula with lane-constant masks.
+    const uint32_t low_mask = half ? 0x0F0F0F0Fu : 0x3F3F3F3Fu;
+    const uint32_t top_mask = half ? 0x30303030u : 0u;
+    const int qoff = 16 + 32 * c;
+
+    // x first, then the first tiles of weights (vmcnt retires in order), so
+    // that staging x waits only for x.
     const int nxc = nb * 32;  // 16-byte chunks of x, at most 2048 (K <= 16384)
     uint4 xv[kGemvMaxXChunksPerThread];
     uint4 gv[kNorm ? kGemvMaxXChunksPerThread : 1];
-    // Every load below is unconditional, past the end a repeat of the last
-    // chunk or block: with loads under branches the compiler's count of
-    // loads in flight turns pessimistic at the joins and it waits for all
-    // of them, which undoes the prefetch.
-    const int nround = (nblk_all + 63) / 64;   // same for every thread
-    auto round_block = [&](int round) { return min(b0 + 64 * round, nblk_all - 1); };
 #pragma unroll
     for (int q = 0; q < kGemvMaxXChunksPerThread; ++q) {
         // q beyond the chunks of the largest K: no load at all (compile-time)
@@ -194,10 +256,58 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
             if constexpr (kNorm) gv[q] = gamma[g];
         }
     }
-    QuarterLoad ld[kGemvDepth];
-#pragma unroll
-    for (int u = 0; u < kGemvDepth; ++u) ld[u] = load_quarter(blk_ptr(round_block(u)), c);
 
+    // This wave's tiles: w, w + 4, ... of the Gt * nb.  Loads past the last
+    // tile repeat it (every load below is unconditional: with loads under
+    // branches the compiler's count of loads in flight turns pessimistic at
+    // the joins and it waits for all of them, which undoes the prefetch).
+    const int ntiles = Gt * nb;
+    const int mine = ntiles > wave ? (ntiles - wave + 3) >> 2 : 0;
+    auto group_row = [&](int g) {
+        const bool second = kPair && g >= G;
+        const int gg = second ? g - G : g;
+        const long r = row0 + min(16 * gg + m, rows - 1);
+        return (second ? W2 : W) + r * nb * kBlockBytes + qoff;
+    };
+    int pi = 0, pg = 0, pkb = wave;
+    while (pkb >= nb) {
+        pkb -= nb;
+        ++pg;
+    }
+    const uint8_t* prow = group_row(pg);
+    auto issue = [&](TileLoad& l) {
+        const uint8_t* p = prow + pkb * kBlockBytes;
+        l.qa = load16(p);
+        l.qb = load16(p + 16);
+        l.hdr = load16(p - qoff);
+        if (pi + 1 < mine) {
+            ++pi;
+            pkb += 4;
+            const int g0 = pg;
+            while (pkb >= nb) {
+                pkb -= nb;
+                ++pg;
+            }
+            if (pg != g0) prow = group_row(pg);
+        }
+    };
+    // Two tiles go out before x is staged, the third after: a smaller first
+    // burst of weight loads lets x (queued behind it) arrive sooner
+    // (measured: 2 best of 0..3 on the decode layer and the LM head).
+    constexpr int kEarly = 2;
+    TileLoad ld[kGemvDepth];
+    if (mine > 0) {
+#pragma unroll
+        for (int u = 0; u < kEarly; ++u) issue(ld[u]);
+    }
+
+    // LDS that is read before it is written: the zeros, the partials (a
+    // class without blocks, when nb < 4, stays zero) and the list's count.
+    if (t < 4) zero4[t] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = t; i < Gt * 16 * 16; i += kGemvThreads) part[i] = make_float2(0.f, 0.f);
+    if (t == 0) flist[0] = 0;
+
+    float rnorm = 0.f;
     if constexpr (kNorm) {
         float ss = 0.f;
 #pragma unroll
@@ -215,7 +325,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
         if ((t & 63) == 0) wave_ss[t >> 6] = ss;
         __syncthreads();
         const float total = (wave_ss[0] + wave_ss[1]) + (wave_ss[2] + wave_ss[3]);
-        const float r = rsqrtf(total / static_cast<float>(nb * kQK) + eps);
+        rnorm = rsqrtf(total / static_cast<float>(nb * kQK) + eps);
 #pragma unroll
         for (int q = 0; q < kGemvMaxXChunksPerThread; ++q)
             if (t + q * kGemvThreads < nxc) {
@@ -224,80 +334,220 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
                 uint32_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    o[e] = pack_bf16x2(bf16_lo(w[e]) * r * bf16_lo(gm[e]),
-                                       bf16_hi(w[e]) * r * bf16_hi(gm[e]));
+                    o[e] = pack_bf16x2(bf16_lo(w[e]) * rnorm * bf16_lo(gm[e]),
+                                       bf16_hi(w[e]) * rnorm * bf16_hi(gm[e]));
                 xv[q] = make_uint4(o[0], o[1], o[2], o[3]);
             }
     }
 
-    // Stage x as binary16.  Chunk g (x[8g .. 8g+7]) belongs to block
-    // kb = g / 32, quarter c = (g / 8) % 4, and is piece gq = g % 8 of the
-    // quarter: pieces 0..3 are even-sub-block values (bytes 0..7 of chunks
-    // t = 2 gq, 2 gq + 1), pieces 4..7 odd ones (bytes 8..15 of chunks
-    // t = 2 (gq - 4), + 1).  The 32 chunks of a block sit in 32 consecutive
-    // lanes (half a wave), which reduce the block's largest exponent among
-    // themselves; a half wave past the end of x holds repeats and stores
-    // nothing.
+    // Stage x.  Chunk g (x[8g .. 8g+7]) is piece p = g % 4 of sub-block
+    // s = (g / 4) % 8 of block kb = g / 32.  The 32 chunks of a block sit in
+    // 32 consecutive lanes (half a wave), which reduce the block's largest
+    // magnitude among themselves, and the 4 chunks of a sub-block in a quad,
+    // which sums its S0 and T0; a half wave past the end of x holds repeats
+    // and stores nothing.  A bf16 value is exact in the staged binary16 when
+    // its exponent field is at least the block's largest minus 31 (its last
+    // significant bit then lands at or above 2^-24 after the scaling), or
+    // when it is zero; smaller non-zero values (and Inf, NaN) set `inexact`.
+    int inexact = 0;
 #pragma unroll
     for (int q = 0; q < kGemvMaxXChunksPerThread; ++q) {
         if (q * kGemvThreads < nxc) {
             const int g = t + q * kGemvThreads;
             const uint4 v = xv[q];
-            const int e = half_wave_max(max_exponent8(v));
+            const uint4 mag = make_uint4(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu,
+                                         v.w & 0x7FFF7FFFu);
+            const u16x2_t mx = __builtin_elementwise_max(
+                __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, mag.x),
+                                          __builtin_bit_cast(u16x2_t, mag.y)),
+                __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, mag.z),
+                                          __builtin_bit_cast(u16x2_t, mag.w)));
+            // magnitude bits minus one: zero wraps to the largest value
+            const u16x2_t one = {1, 1};
+            const u16x2_t mn = __builtin_elementwise_min(
+                __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, mag.x) - one,
+                                          __builtin_bit_cast(u16x2_t, mag.y) - one),
+                __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, mag.z) - one,
+                                          __builtin_bit_cast(u16x2_t, mag.w) - one));
+            const int e = half_wave_max(
+                static_cast<int>(max(static_cast<uint32_t>(mx[0]), static_cast<uint32_t>(mx[1])) >> 7));
+            const int low = static_cast<int>(min(static_cast<uint32_t>(mn[0]), static_cast<uint32_t>(mn[1])));
+            const int bad = (e == 255) | (low < ((e - 31) << 7) - 1);
             const int sh = block_shift(e);
-            const float scale = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sh) << 23);
-            const uint32_t h0 = bf16x2_to_f16x2(v.x, scale), h1 = bf16x2_to_f16x2(v.y, scale);
-            const uint32_t h2 = bf16x2_to_f16x2(v.z, scale), h3 = bf16x2_to_f16x2(v.w, scale);
+            const float scale = pow2f(-sh);
+            const float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+            float f[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = x[i] * scale;
+            const uint32_t h0 = pack_f16x2(f[0], f[2]), h1 = pack_f16x2(f[1], f[3]);
+            const uint32_t h2 = pack_f16x2(f[4], f[6]), h3 = pack_f16x2(f[5], f[7]);
+            const half2_t ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+            float s0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, h0), ones, 0.f, false);
+            s0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, h1), ones, s0, false);
+            s0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, h2), ones, s0, false);
+            s0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, h3), ones, s0, false);
+            float t0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, h0 & 0x7FFF7FFFu), ones,
+                                              0.f, false);
+            t0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, h1 & 0x7FFF7FFFu), ones, t0,
+                                        false);
+            t0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, h2 & 0x7FFF7FFFu), ones, t0,
+                                        false);
+            t0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, h3 & 0x7FFF7FFFu), ones, t0,
+                                        false);
+            s0 = quad_sum(s0);
+            t0 = quad_sum(t0);
             if (g < nxc) {
-                const int kb = g >> 5, gq = g & 7;
-                const int t0 = 2 * (gq & 3);
-                uint2* dst = reinterpret_cast<uint2*>(xs + x_group_base(kb, (g >> 3) & 3, nb) + t0) +
-                             (gq >> 2);
-                dst[0] = make_uint2(h0, h1);
-                dst[2] = make_uint2(h2, h3);
+                inexact |= bad;
+                const int kb = g >> 5, s = (g >> 2) & 7, p = g & 3;
+                xa[kb * kXaChunks + kSubChunks * s + p] = make_uint4(h0, h1, h2, h3);
+                if (p == 0) {
+                    zs[kb * 16 + s] = s0;
+                    zs[kb * 16 + 8 + s] = t0;
+                }
                 if ((g & 31) == 0) xsh[kb] = sh;
             }
         }
     }
+    const bool x_inexact = __syncthreads_or(inexact) != 0;
+    if (mine > 0) {
+#pragma unroll
+        for (int u = kEarly; u < kGemvDepth; ++u) issue(ld[u]);
+    }
+
+    // The tiles.  The lane's running sums over the tiles of its group, all
+    // of one class kb mod 4 (each (group, class) belongs to one wave):
+    //   S lanes   v1 = sum r (the output), v2 = sum |r| (L)
+    //   T lanes   v2 = sum |dm| T0, v3 = sum 15 |d sc| T0 (v2 + v3 = B)
+    // each tile's sums scaled by 2^sh_kb.  They go to slot lane / 16 of
+    // (row, class) in `part` when the wave moves to the next group, so a
+    // row's sums do not depend on R or on which wave ran which tile.
+    int cg = 0, ckb = wave;
+    while (ckb >= nb) {
+        ckb -= nb;
+        ++cg;
+    }
+    const int slot = lane >> 4;
+    float v1 = 0.f, v2 = 0.f, v3 = 0.f;
+    auto flush = [&](int g, int kb) {
+        part[((g * 16 + m) * 4 + (kb & 3)) * 4 + slot] = make_float2(v1, laneT ? v2 + v3 : v2);
+        v1 = 0.f;
+        v2 = 0.f;
+        v3 = 0.f;
+    };
+    auto compute = [&](const TileLoad& l) {
+        const uint4* alo = xa + alo_base + __umul24(ckb, alo_stride);
+        const uint4* ahi = xa + ahi_base + __umul24(ckb, ahi_stride);
+        const uint32_t qw[8] = {l.qa.x, l.qa.y, l.qa.z, l.qa.w, l.qb.x, l.qb.y, l.qb.z, l.qb.w};
+        float4_t dlo = {0.f, 0.f, 0.f, 0.f}, dhi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t v0 = qw[2 * p], u1 = qw[2 * p + 1];
+            const uint32_t s0 = v0 >> 8, s1 = u1 >> 8;
+            const uint4 blo = make_uint4(v0 & 0x000F000Fu, s0 & 0x000F000Fu,
+                                         u1 & 0x000F000Fu, s1 & 0x000F000Fu);
+            const uint4 bhi = make_uint4(v0 & 0x00F000F0u, s0 & 0x00F000F0u,
+                                         u1 & 0x00F000F0u, s1 & 0x00F000F0u);
+            dlo = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, alo[p]),
+                                                         __builtin_bit_cast(half8_t, blo), dlo,
+                                                         0, 0, 0);
+            dhi = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ahi[p]),
+                                                         __builtin_bit_cast(half8_t, bhi), dhi,
+                                                         0, 0, 0);
+        }
+        // sub-blocks 4 half + i: even ones from the low-nibble instructions
+        // (codes q 2^-24), odd ones from the high-nibble ones (q 2^-20)
+        const float D[4] = {dlo[0], dhi[1], dlo[2], dhi[3]};
+        const uint4 h = l.hdr;
+        const float d = half_bits_to_float(h.x & 0xFFFFu);
+        const float dmin = half_bits_to_float(h.x >> 16);
+        const float dE = d * 0x1p24f, dO = d * 0x1p20f, d15 = fabsf(d) * 15.0f;
+        const uint32_t sc_src = half ? h.w : h.y;
+        const uint32_t m_src = half ? h.w >> 4 : h.z;
+        const uint32_t scb = (sc_src & low_mask) | ((h.y >> 2) & top_mask);
+        const uint32_t mb = (m_src & low_mask) | ((h.z >> 2) & top_mask);
+        const float4_t Z = *reinterpret_cast<const float4_t*>(zs + ckb * 16 + zoff);
+        const float sc[4] = {ubyte_to_float<0>(scb), ubyte_to_float<1>(scb),
+                             ubyte_to_float<2>(scb), ubyte_to_float<3>(scb)};
+        const float mm[4] = {ubyte_to_float<0>(mb), ubyte_to_float<1>(mb),
+                             ubyte_to_float<2>(mb), ubyte_to_float<3>(mb)};
+        float r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ds = ((i & 1) ? dO : dE) * sc[i];
+            const float a = (dmin * mm[i]) * Z[i];
+            r[i] = __builtin_fmaf(ds, D[i], -a);
+        }
+        const float zsc = ((sc[0] * Z[0] + sc[1] * Z[1]) + (sc[2] * Z[2] + sc[3] * Z[3]));
+        const int sh = xsh[ckb];
+        v1 += __builtin_amdgcn_ldexpf((r[0] + r[1]) + (r[2] + r[3]), sh);
+        v2 += __builtin_amdgcn_ldexpf((fabsf(r[0]) + fabsf(r[1])) + (fabsf(r[2]) + fabsf(r[3])),
+                                      sh);
+        v3 += __builtin_amdgcn_ldexpf(d15 * zsc, sh);
+        // next tile of this wave
+        const int kb0 = ckb;
+        ckb += 4;
+        const int g0 = cg;
+        while (ckb >= nb) {
+            ckb -= nb;
+            ++cg;
+        }
+        if (cg != g0) flush(g0, kb0);
+    };
+    if (mine > 0) {
+        int i = 0;
+        for (; i + kGemvDepth <= mine; i += kGemvDepth) {
+#pragma unroll
+            for (int u = 0; u < kGemvDepth; ++u) {
+                compute(ld[u]);
+                issue(ld[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u + 1 < kGemvDepth; ++u)
+            if (i + u < mine) compute(ld[u]);
+        // the last group, unless its last tile ended it (then cg >= Gt and
+        // the group was flushed in compute)
+        if (cg < Gt) flush(cg, ckb);
+    }
     __syncthreads();
 
-    // A round past the thread's last task (the last round of a span whose
-    // block count is not a multiple of 64) computes on a repeated block and
-    // stores nothing; the four lanes of a block agree, so the instruction's
-    // sum over quarters sees only its own block.  The loop runs whole groups
-    // of kGemvDepth rounds without a branch; the remaining rounds follow it,
-    // without prefetch.
-    const int kb_step = 64 % nb;
-    int kb = b0 % nb;
-    auto task = [&](int round, QuarterLoad& l, bool prefetch) {
-        const int b = b0 + 64 * round;
-        const float4_t acc = quarter_mfma(l, c, xs + x_group_base(kb, c, nb));
-        const float p01 = sel1 ? acc[1] : acc[0];
-        const float p23 = sel1 ? acc[3] : acc[2];
-        const float p = __builtin_amdgcn_ldexpf(sel2 ? p23 : p01, xsh[kb]);
-        if (diag && b < nblk_all) part[b] = p;
-        if (prefetch) l = load_quarter(blk_ptr(round_block(round + kGemvDepth)), c);
-        kb += kb_step;
-        if (kb >= nb) kb -= nb;
-    };
-    int r0 = 0;
-    for (; r0 + kGemvDepth <= nround; r0 += kGemvDepth) {
+    // Rows: the classes' sums in a fixed order, the certificate, and the list
+    // of rows to recompute (the list's order does not matter: a row's
+    // recomputation is the same whichever wave runs it).
+    const float kE = (192.0f + static_cast<float>(nb)) * 0x1p-24f;
+    for (int q = t; q < kMats * rows; q += kGemvThreads) {
+        const int mat = (kPair && q >= rows) ? 1 : 0;
+        const int qq = q - mat * rows;
+        const float2* pr = part + (mat * G * 16 + qq) * 16;
+        float y = 0.f, L = 0.f, B = 0.f;
 #pragma unroll
-        for (int u = 0; u < kGemvDepth; ++u) task(r0 + u, ld[u], true);
-    }
-#pragma unroll
-    for (int u = 0; u + 1 < kGemvDepth; ++u)
-        if (r0 + u < nround) task(r0 + u, ld[u], false);
-    __syncthreads();
-    for (int r = t; r < rows; r += kGemvThreads) {
-        float s = 0.f;
-        for (int i = 0; i < nb; ++i) s += part[r * nb + i];
-        if constexpr (kPair) {
-            float u = 0.f;
-            for (int i = 0; i < nb; ++i) u += part[nblk + r * nb + i];
-            s = silu(s) * u;
+        for (int k = 0; k < 4; ++k) {
+            y += pr[4 * k].x + pr[4 * k + 1].x;
+            L += pr[4 * k].y + pr[4 * k + 1].y;
+            B += pr[4 * k + 2].y + pr[4 * k + 3].y;
         }
-        Y[row0 + r] = s;
+        const float E = kE * B;
+        const float lb = fmaxf(L - 2.0f * E, fabsf(y) - E);
+        yrow[q] = y;
+        if (x_inexact || !(E <= 1.9e-3f * lb + 0.99e-5f)) flist[1 + atomicAdd(flist, 1)] = q;
+    }
+    __syncthreads();
+    const int nredo = flist[0];
+    for (int e = wave; e < nredo; e += 4) {
+        const int q = flist[1 + e];
+        const int mat = (kPair && q >= rows) ? 1 : 0;
+        const int qq = q - mat * rows;
+        const uint8_t* rp = (mat ? W2 : W) + (row0 + qq) * nb * kBlockBytes;
+        const float y = exact_row<kNorm>(rp, nb, X, gamma, rnorm, lane);
+        if (lane == 0) yrow[q] = y;
+    }
+    __syncthreads();
+    for (int q = t; q < rows; q += kGemvThreads) {
+        if constexpr (kPair)
+            Y[row0 + q] = silu(yrow[q]) * yrow[rows + q];
+        else
+            Y[row0 + q] = yrow[q];
     }
 }
 
@@ -357,8 +607,7 @@ hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X
     b.count = count;
     // Problems with the longest rows first (largest K, stable): their
     // workgroups stage the most x before their first weights, and started
-    // first they no longer form the tail (decode layer: 15.3 -> 14.9 us with
-    // the down projection, K = 9728, first).  Each problem's results do not
+    // first they do not form the tail.  Each problem's results do not
     // depend on the order.
     int ord[kGemvBatchMax];
     for (int i = 0; i < count; ++i) ord[i] = i;
@@ -374,16 +623,12 @@ hipError_t launch_gemv_batched(const uint8_t* const* W, const uint16_t* const* X
         b.p[slot] = {W[i], reinterpret_cast<const uint4*>(X[i]), Y[i], N[i], nb, R[i]};
         b.first[slot] = total;
         total += static_cast<int>((static_cast<long>(N[i]) + R[i] - 1) / R[i]);
-        lds = gemv_lds_bytes(nb, R[i]) > lds ? gemv_lds_bytes(nb, R[i]) : lds;
+        const size_t need = gemv_lds_bytes(nb, R[i], 1);
+        lds = need > lds ? need : lds;
     }
     b.first[count] = total;
     hipLaunchKernelGGL(q4k_gemv_batched_kernel, dim3(total), dim3(kGemvThreads), lds, stream, b);
     return hipGetLastError();
-}
-
-size_t gemv_lds_bytes(int nb, int R) {
-    return static_cast<size_t>(nb) * 4 * kXGroupStride * 16 +
-           static_cast<size_t>(gemv_shift_words(nb)) * 4 + static_cast<size_t>(R) * nb * 4;
 }
 
 hipError_t launch_gemv_rmsnorm(const uint8_t* W, const uint16_t* X, const uint16_t* gamma,
@@ -391,19 +636,18 @@ hipError_t launch_gemv_rmsnorm(const uint8_t* W, const uint16_t* X, const uint16
     const int nb = K / kQK;
     const unsigned grid = static_cast<unsigned>((static_cast<long>(N) + R - 1) / R);
     hipLaunchKernelGGL(q4k_gemv_rmsnorm_kernel, dim3(grid), dim3(kGemvThreads),
-                       gemv_lds_bytes(nb, R), stream, W, reinterpret_cast<const uint4*>(X),
+                       gemv_lds_bytes(nb, R, 1), stream, W, reinterpret_cast<const uint4*>(X),
                        reinterpret_cast<const uint4*>(gamma), eps, Y, N, nb, R);
     return hipGetLastError();
 }
 
-// R rows of each matrix per workgroup; the partials of both sit in LDS
-// (gemv_lds_bytes(nb, 2 R)).
+// R rows of each matrix per workgroup.
 hipError_t launch_gemv_swiglu(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
                               int N, int K, int R, hipStream_t stream) {
     const int nb = K / kQK;
     const unsigned grid = static_cast<unsigned>((static_cast<long>(N) + R - 1) / R);
     hipLaunchKernelGGL(q4k_gemv_swiglu_kernel, dim3(grid), dim3(kGemvThreads),
-                       gemv_lds_bytes(nb, 2 * R), stream, Wg, Wu,
+                       gemv_lds_bytes(nb, R, 2), stream, Wg, Wu,
                        reinterpret_cast<const uint4*>(X), H, N, nb, R);
     return hipGetLastError();
 }
@@ -412,8 +656,9 @@ hipError_t launch_gemv(const uint8_t* W, const uint16_t* X, float* Y, int N, int
                        hipStream_t stream) {
     const int nb = K / kQK;
     const unsigned grid = static_cast<unsigned>((static_cast<long>(N) + R - 1) / R);
-    hipLaunchKernelGGL(q4k_gemv_kernel, dim3(grid), dim3(kGemvThreads), gemv_lds_bytes(nb, R),
-                       stream, W, reinterpret_cast<const uint4*>(X), Y, N, nb, R);
+    hipLaunchKernelGGL(q4k_gemv_kernel, dim3(grid), dim3(kGemvThreads),
+                       gemv_lds_bytes(nb, R, 1), stream, W, reinterpret_cast<const uint4*>(X), Y,
+                       N, nb, R);
     return hipGetLastError();
 }
 

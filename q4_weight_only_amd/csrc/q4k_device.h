@@ -168,7 +168,7 @@ __device__ __forceinline__ void dequant_dword_bf16(uint32_t v, const QuarterScal
     hi2[1] = pack_bf16x2(fma_half_hi(s1, b02, -s.dm1), fma_half_hi(s1, b13, -s.dm1));
 }
 
-// ---- binary16 weights and activations (the M = 1 GEMV) ----------------
+// ---- binary16 activations (the M = 1 GEMV) ----------------------------
 
 // Two fp32 -> packed binary16 pair, round-to-nearest-even
 // (v_cvt_pk_f16_f32).  Written as the instruction so that the compiler
@@ -178,29 +178,6 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     uint32_t r;
     asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
     return r;
-}
-
-// binary16 weights of one qs dword (bytes p..p+3 of quarter c): the fp32
-// weight of dequant_dword_f32 (d*sc*q - dmin*m rounded once, formed by
-// v_fma_mix_f32 on the quants read as binary16 subnormals, see
-// dequant_dword_bf16) rounded to binary16, as four packed pairs:
-//   h[0] = (w_lo0, w_lo1), h[1] = (w_lo2, w_lo3)   even sub-block, 64c + p + 0..3
-//   h[2] = (w_hi0, w_hi1), h[3] = (w_hi2, w_hi3)   odd sub-block, 64c + 32 + p + 0..3
-// Per 8 weights: 1 shift, 4 masks, 8 v_fma_mix_f32, 4 v_cvt_pk_f16_f32.
-// Every exact weight is a multiple of 2^-24 (d and dmin are binary16), so
-// weights below 2^-14 in magnitude are exact binary16 subnormals; larger
-// ones carry a relative error of at most 2^-11 from the binary16 rounding;
-// from 65520 up they round to infinity.
-__device__ __forceinline__ void dequant_dword_f16(uint32_t v, const QuarterScales& s,
-                                                  uint32_t h[4]) {
-    const uint32_t v8 = v >> 8;
-    const uint32_t a02 = v & 0x000F000Fu, a13 = v8 & 0x000F000Fu;   // q0,q2 / q1,q3 (even)
-    const uint32_t b02 = v & 0x00F000F0u, b13 = v8 & 0x00F000F0u;   // the same (odd)
-    const float s0 = s.ds0 * 0x1p24f, s1 = s.ds1 * 0x1p20f;
-    h[0] = pack_f16x2(fma_half_lo(s0, a02, -s.dm0), fma_half_lo(s0, a13, -s.dm0));
-    h[1] = pack_f16x2(fma_half_hi(s0, a02, -s.dm0), fma_half_hi(s0, a13, -s.dm0));
-    h[2] = pack_f16x2(fma_half_lo(s1, b02, -s.dm1), fma_half_lo(s1, b13, -s.dm1));
-    h[3] = pack_f16x2(fma_half_hi(s1, b02, -s.dm1), fma_half_hi(s1, b13, -s.dm1));
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), fp32 (the SwiGLU epilogues),

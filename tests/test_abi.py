@@ -342,7 +342,6 @@ def test_binding_rejects_host_tensors_before_any_launch():
                                                      torch.zeros(64, dtype=torch.uint8))),
         ("dequant_f32", lambda: jq4k.dequant_f32(W, torch.zeros(8 * 256))),
         ("dequant_bf16", lambda: jq4k.dequant_bf16(W, torch.zeros(8 * 256, dtype=torch.int16))),
-        ("dequant_f16", lambda: jq4k.dequant_f16(W, torch.zeros(8 * 256, dtype=torch.int16))),
     ]
     for name, call in cases:
         with pytest.raises(ValueError, match="GPU tensor"):

@@ -190,78 +190,6 @@ def test_dequant_is_the_correct_rounding_of_the_exact_value():
             assert _is_rne(exact, w[b, i]), (b, i, exact, w[b, i])
 
 
-def _is_rne16(exact: Fraction, h: np.float16) -> bool:
-    """h is binary16's round-to-nearest-even of the exact value: the nearest
-    of h and its two neighbours, the even significand on a tie; magnitudes
-    from 65520 (the midpoint above 65504) up round to infinity."""
-    if abs(exact) >= 65520:
-        return bool(np.isinf(h)) and (h > 0) == (exact > 0)
-    if not np.isfinite(h):
-        return False
-    lo = np.nextafter(h, np.float16(-np.inf))
-    hi = np.nextafter(h, np.float16(np.inf))
-    e = abs(exact - Fraction(float(h)))
-    near = [abs(exact - Fraction(float(v))) for v in (lo, hi) if np.isfinite(v)]
-    if any(e > n for n in near):
-        return False
-    if any(e == n for n in near):
-        return int(np.array([h]).view(np.uint16)[0]) % 2 == 0
-    return True
-
-
-def test_dequant_f16_is_the_correct_rounding_of_the_fp32_weight():
-    """The decode GEMV's binary16 weights: binary16's round-to-nearest-even
-    of the fp32 weight, over arbitrary finite d and dmin of both signs and
-    every exponent (so subnormal, tie, overflow and huge values all occur),
-    checked against the exact rational value of the fp32 weight."""
-    g = np.random.default_rng(24)
-    nb = 96
-    d = g.integers(0, 0x7C00, nb).astype(np.uint16) | (g.integers(0, 2, nb) << 15).astype(np.uint16)
-    dmin = g.integers(0, 0x7C00, nb).astype(np.uint16) | (g.integers(0, 2, nb) << 15).astype(np.uint16)
-    sc = g.integers(0, 64, (nb, 8))
-    m = g.integers(0, 64, (nb, 8))
-    q = g.integers(0, 16, (nb, 256))
-    blocks = pk.pack_blocks(d, dmin, sc, m, q)
-    w = oracle.dequant_f16(blocks).view(np.float16).reshape(nb, 256)
-    w32 = oracle.dequant_f32(blocks).reshape(nb, 256)
-    seen_inf = seen_sub = 0
-    for b in range(nb):
-        for i in g.integers(0, 256, 32):
-            exact = Fraction(float(w32[b, i]))
-            assert _is_rne16(exact, w[b, i]), (b, i, exact, w[b, i])
-            seen_inf += bool(np.isinf(w[b, i]))
-            seen_sub += 0 < abs(exact) < Fraction(1, 2 ** 14)
-    assert seen_inf and seen_sub
-
-
-def test_dequant_f16_matches_numpy_conversion_of_the_fp32_weight():
-    """numpy's correctly rounded float32 -> float16 conversion of the oracle's
-    fp32 weights gives its binary16 bits, for every weight of random blocks
-    (workload-like and arbitrary d, dmin); weights below 2^-14 (the binary16
-    subnormal range) are the exact weight, which is a multiple of 2^-24."""
-    g = np.random.default_rng(25)
-    for kind in ("workload", "arbitrary"):
-        nb = 400
-        if kind == "workload":
-            d, dmin, sc, m, q = random_fields(g, nb)
-        else:
-            d = g.integers(0, 0x5800, nb).astype(np.uint16) | (g.integers(0, 2, nb) << 15).astype(np.uint16)
-            dmin = g.integers(0, 0x5800, nb).astype(np.uint16) | (g.integers(0, 2, nb) << 15).astype(np.uint16)
-            sc, m, q = g.integers(0, 64, (nb, 8)), g.integers(0, 64, (nb, 8)), g.integers(0, 16, (nb, 256))
-        blocks = pk.pack_blocks(d, dmin, sc, m, q)
-        got = oracle.dequant_f16(blocks).reshape(nb, 256)
-        ref = oracle.dequant_f32(blocks).astype(np.float16).view(np.uint16).reshape(nb, 256)
-        same = (got == ref) | (((got & 0x7FFF) == 0) & ((ref & 0x7FFF) == 0))
-        assert same.all(), kind
-        D = np.rint(np.ldexp(pk.half_value(d), 24)).astype(np.int64)
-        DM = np.rint(np.ldexp(pk.half_value(dmin), 24)).astype(np.int64)
-        E = (D[:, None] * np.repeat(sc, 32, axis=1) * q - DM[:, None] * np.repeat(m, 32, axis=1))
-        exact = np.ldexp(E.astype(np.float64), -24)
-        tiny = np.abs(exact) < 2.0 ** -14
-        assert tiny.any()
-        assert np.array_equal(got.view(np.float16)[tiny].astype(np.float64), exact[tiny])
-
-
 def test_dequant_bf16_is_torch_rounding_of_dequant_f32():
     g = np.random.default_rng(22)
     blocks = qi.weight_bytes(g, 40, 2560)
