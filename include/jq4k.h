@@ -156,8 +156,10 @@ int jq4k_gemv_batched(const jq4k_gemv_desc *problems, int count, hipStream_t str
  * larger M the dequantise-to-LDS bf16 MFMA kernels (K <= JQ4K_MFMA_MAX_K,
  * else JQ4K_EINVAL): 128-row tiles, or the wave-specialised 256-row tile from
  * M = 2048, and from M = 512 when the matmul still gives every compute unit
- * two 256 x 128 tiles.  M == 0 or N == 0 returns 0 without launching.  Same
- * pointer and alignment rules as jq4k_gemv. */
+ * two 256 x 128 tiles; a 256-row launch whose 256 x 256 output tiles give
+ * every compute unit at least three runs the register-W kernel
+ * (JQ4K_PATH_MFMA_RW) instead.  M == 0 or N == 0 returns 0 without
+ * launching.  Same pointer and alignment rules as jq4k_gemv. */
 int jq4k_gemm(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
               int M, int N, int K, hipStream_t stream);
 
@@ -178,8 +180,10 @@ typedef struct {
  * prefill; one launch for projections that do not depend on each other, such
  * as q, k and v, or gate and up, so that their tiles fill the GPU together).
  * The tile (64, 128 or 256 rows of M) follows the largest M of the batch:
- * 64 up to M = 64, 256 from M = 512, else 128; every problem meets the same
- * bounds as jq4k_gemm.  Problems
+ * 64 up to M = 64, 256 from M = 512, else 128; a 256-row batch whose
+ * 256 x 256 output tiles give every compute unit at least three runs the
+ * register-W kernel.  Every problem meets the same bounds as jq4k_gemm.
+ * Problems
  * with M == 0 or N == 0 are skipped.  `problems` is a host array read before
  * the call returns (passed to the kernel by value; nothing is allocated).
  * Outputs must not overlap any input.  Errors: JQ4K_EINVAL for count < 0,
@@ -293,6 +297,8 @@ int jq4k_gemm_swiglu(const block_q4_K *Wg, const block_q4_K *Wu, const jq4k_bf16
                               /* W dequantised in registers, X in LDS     */
 #define JQ4K_PATH_MFMA_BIG 7  /* MFMA kernel, 256 x 256 tiles, four waves */
                               /* that each load, dequantise and multiply  */
+#define JQ4K_PATH_MFMA_RW 8   /* MFMA kernel, 256 x 256 tiles, four waves */
+                              /* that dequantise W into operand registers */
 
 /* jq4k_gemm with an explicit kernel path; JQ4K_EINVAL for an unknown path,
  * JQ4K_PATH_GEMV with M != 1 or JQ4K_PATH_SKINNY with M > 64.  Results meet

@@ -22,7 +22,7 @@ HEADER = os.path.join(HERE, "..", "include", "jq4k.h")
 OK, EINVAL, EALIGN, ESCRATCH = 0, -1, -2, -3
 SCRATCH_BYTES = 8 << 20
 (PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_T64, PATH_MFMA_T128, PATH_MFMA_T256, PATH_SKINNY,
- PATH_MFMA_BIG) = range(8)
+ PATH_MFMA_BIG, PATH_MFMA_RW) = range(9)
 GEMV_MAX_K = 16384
 MFMA_MAX_K = 4194304
 BLOCK_BYTES = 144

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libjq4k.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "gemv.hip", "gemm.hip", "gemm_ws.hip", "gemm_big.hip", "gemm_skinny.hip",
+SOURCES = ["api.hip", "gemv.hip", "gemm.hip", "gemm_ws.hip", "gemm_big.hip", "gemm_rw.hip", "gemm_skinny.hip",
            "kv_convert.hip", "rmsnorm.hip", "exports.hip", "probes.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,9 +25,16 @@ CFLAGS = [
 ]
 
 
+# Per-source flags.  gemm_rw.hip orders its matrix, vector and LDS
+# instructions with scheduling-group barriers; the post-register-allocation
+# scheduler would reorder them again (runs of 16 matrix instructions, then
+# dozens of vector ones with the matrix cores idle), so it is off there.
+EXTRA_FLAGS = {"gemm_rw.hip": ["-mllvm", "--disable-post-ra"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

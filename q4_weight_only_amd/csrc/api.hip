@@ -22,6 +22,7 @@ hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, f
 long gemm_launch_size(const int* M, const int* N, int count, int tile,
                       const int* splits = nullptr);
 constexpr int kTileBig = 512;   // tile code of the 256 x 256 kernel (gemm_big.hip)
+constexpr int kTileRw = 1024;   // tile code of the register-W 256 x 256 kernel (gemm_rw.hip)
 long gemm_splitk_plan(const int* M, const int* N, const int* K, int count, long min_items,
                       int* splits);
 hipError_t launch_gemm_skinny(const uint8_t* const* W, const uint16_t* const* X,
@@ -148,6 +149,21 @@ int mfma_tile_for(int M, bool grouped) {
     return M >= (grouped ? 512 : 2048) ? 256 : 128;
 }
 
+// A launch of 256-row tiles moves to the register-W kernel (gemm_rw.hip,
+// one workgroup per CU) once its 256 x 256 output tiles give every CU at
+// least kRwTilesPerCu of them: below that the tail of the one-per-CU kernel
+// costs more than it saves (Qwen3-4B at M = 2048: the seven-projection layer,
+// 3.75 tiles per CU, 422 vs 466 us; gate alone, 1.2 per CU, 147 vs 134 us;
+// the LM head at M = 512, 4.6 per CU, 399 vs 475 us).
+constexpr long kRwTilesPerCu = 3;
+
+bool rw_pays(const int* M, const int* N, int count) {
+    long tiles = 0;
+    for (int i = 0; i < count; ++i)
+        tiles += static_cast<long>((M[i] + 255) / 256) * ((N[i] + 255) / 256);
+    return tiles >= kRwTilesPerCu * cu_count();
+}
+
 int run_mfma(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K, int tile,
              hipStream_t stream) {
     if (K > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
@@ -178,6 +194,7 @@ int run_mfma_auto(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int 
     if (tile == 128 && M >= 512 &&
         static_cast<long>((M + 255) / 256) * ((N + 127) / 128) >= 2L * cu_count())
         tile = 256;
+    if (tile == 256 && rw_pays(&M, &N, 1)) tile = jq4k::kTileRw;
     return run_mfma(W, X, Y, M, N, K, tile, stream);
 }
 
@@ -213,6 +230,7 @@ int collect_gemm_batch(const jq4k_gemm_desc* problems, int count, GemmBatchArgs&
     for (int i = 0; i < a.live; ++i)
         if (a.K[i] > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
     a.tile = mfma_tile_for(a.max_m, true);
+    if (a.tile == 256 && rw_pays(a.M, a.N, a.live)) a.tile = jq4k::kTileRw;
     if (jq4k::gemm_launch_size(a.M, a.N, a.live, a.tile) > 0x7FFFFFFFL) return JQ4K_EINVAL;
     return 0;
 }
@@ -457,7 +475,7 @@ int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16
 
 int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int N, int K,
                    int path, hipStream_t stream) {
-    if (path < JQ4K_PATH_AUTO || path > JQ4K_PATH_MFMA_BIG) return JQ4K_EINVAL;
+    if (path < JQ4K_PATH_AUTO || path > JQ4K_PATH_MFMA_RW) return JQ4K_EINVAL;
     if (path == JQ4K_PATH_GEMV && (M != 1 || K > JQ4K_GEMV_MAX_K)) return JQ4K_EINVAL;
     if (path == JQ4K_PATH_SKINNY && M > 64) return JQ4K_EINVAL;
     const int rc = check_matmul(W, X, Y, M, N, K);
@@ -470,6 +488,7 @@ int jq4k_gemm_path(const block_q4_K* W, const jq4k_bf16* X, float* Y, int M, int
         case JQ4K_PATH_MFMA_T256: return run_mfma(W, X, Y, M, N, K, 256, stream);
         case JQ4K_PATH_SKINNY: return run_skinny(W, X, Y, M, N, K, stream);
         case JQ4K_PATH_MFMA_BIG: return run_mfma(W, X, Y, M, N, K, jq4k::kTileBig, stream);
+        case JQ4K_PATH_MFMA_RW: return run_mfma(W, X, Y, M, N, K, jq4k::kTileRw, stream);
         default:
             if (M == 1 && K <= JQ4K_GEMV_MAX_K) return run_gemv(W, X, Y, N, K, 0, stream);
             return run_mfma_auto(W, X, Y, M, N, K, stream);

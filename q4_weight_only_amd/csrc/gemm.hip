@@ -296,6 +296,10 @@ hipError_t launch_gemm_big(const uint8_t* const* W, const uint16_t* const* X, fl
                            const int* M, const int* N, const int* K, int count,
                            hipStream_t stream);
 constexpr int kTileBig = 512;   // tile code of the 256 x 256 kernel (gemm_big.hip)
+hipError_t launch_gemm_rw(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
+                          const int* M, const int* N, const int* K, int count,
+                          hipStream_t stream);
+constexpr int kTileRw = 1024;   // tile code of the register-W 256 x 256 kernel (gemm_rw.hip)
 
 hipError_t launch_gemm_ws_pair(const uint8_t* Wg, const uint8_t* Wu, const uint16_t* X, float* H,
                                int M, int N, int K, hipStream_t stream);
@@ -319,8 +323,8 @@ long gemm_swiglu_launch_size(int M, int N) {
 // when splits is given, plus idle workgroups at the ends of XCD shares).
 long gemm_launch_size(const int* M, const int* N, int count, int tile,
                       const int* splits) {
-    const int bm = tile == kTileBig ? 256 : tile;
-    const int bn = tile == 64 ? 64 : tile == kTileBig ? 256 : 128;
+    const int bm = tile == kTileBig || tile == kTileRw ? 256 : tile;
+    const int bn = tile == 64 ? 64 : tile == kTileBig || tile == kTileRw ? 256 : 128;
     TileSched s;
     return tile_sched_init(s, M, N, splits, count, bm, bn, 1);
 }
@@ -344,6 +348,7 @@ hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, f
     if (tile == 64) return launch_cfg<64, 64, 2, 2>(W, X, Y, M, N, K, count, stream);
     if (tile == 256) return launch_gemm_ws(W, X, Y, M, N, K, count, stream);
     if (tile == kTileBig) return launch_gemm_big(W, X, Y, M, N, K, count, stream);
+    if (tile == kTileRw) return launch_gemm_rw(W, X, Y, M, N, K, count, stream);
     return launch_cfg<128, 128, 2, 2>(W, X, Y, M, N, K, count, stream);
 }
 

@@ -66,7 +66,7 @@ def test_gemv_requires_one_token_and_bounded_k(L):
 
 
 def test_unknown_path_is_rejected(L):
-    for path in (-1, 8, 99):
+    for path in (-1, jq4k.PATH_MFMA_RW + 1, 99):
         assert L.jq4k_gemm_path(ALIGNED, ALIGNED2, ALIGNED3, 4, 8, 256, path,
                                 None) == jq4k.EINVAL
     # the small-M kernel takes M <= 64 only

@@ -327,14 +327,15 @@ def test_gemv_batched_decode_layer(gpu):
 
 # ------------------------------------------------------------ M > 1 (MFMA)
 
-PATHS = ["mfma64", "mfma128", "mfma256", "mfma_big", "skinny"]
+PATHS = ["mfma64", "mfma128", "mfma256", "mfma_big", "mfma_rw", "skinny"]
 
 
 def _path(name):
     import q4_weight_only_amd as jq4k
     return {"mfma": jq4k.PATH_MFMA, "mfma64": jq4k.PATH_MFMA_T64,
             "mfma128": jq4k.PATH_MFMA_T128, "mfma256": jq4k.PATH_MFMA_T256,
-            "skinny": jq4k.PATH_SKINNY, "mfma_big": jq4k.PATH_MFMA_BIG}[name]
+            "skinny": jq4k.PATH_SKINNY, "mfma_big": jq4k.PATH_MFMA_BIG,
+            "mfma_rw": jq4k.PATH_MFMA_RW}[name]
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -549,6 +550,18 @@ def test_big_tile_m2048_full(gpu):
         y = run_gemm(W, X, N, K, path=_path("mfma_big"))
         Y, A = _oracle_cached(("m2048", p), W, X, N, K)
         parity(y, Y, A, f"big tile M=2048 {name}")
+
+
+def test_register_w_m2048_full(gpu):
+    """The register-W kernel (256 x 256 tiles, W dequantised into operand registers) at
+    M = 2048 on the gate (K = 2560) and down (K = 9728) projections: every
+    output against the oracle."""
+    for p in (4, 6):
+        name, N, K, W, X = qi.prefill_projection(3, 0, p, 2048)
+        announce(f"register-W tile M=2048 {name}, every output")
+        y = run_gemm(W, X, N, K, path=_path("mfma_rw"))
+        Y, A = _oracle_cached(("m2048", p), W, X, N, K)
+        parity(y, Y, A, f"register-W tile M=2048 {name}")
 
 
 def test_prefill_m33_all_layers_full(gpu):
