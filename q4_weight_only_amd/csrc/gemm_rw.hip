@@ -34,13 +34,19 @@
 // 4 (kk / 2) + 2 kh + kk % 2 of the row's 64 values, so an A operand is one
 // 16-byte read.
 //
-// Pipeline (per stage s, k-steps in the order 0, 2, 1, 3):
-//   k-steps 0, 2   B of k-steps 1 and 3 of stage s dequantised; X of stage
-//                  s + 2 copied into the third LDS buffer (global to LDS,
-//                  no registers); on a block's first stage, the whole next
-//                  block of W requested
-//   k-steps 1, 3   B of k-steps 0 and 2 of stage s + 1 dequantised
-//   then one barrier.  The A operands of a k-step are read one k-step ahead.
+// Pipeline (per stage s, k-steps in the order 0, 2, 1, 3; X of stage s in
+// LDS buffer s % 4):
+//   k-steps 0, 2   B of k-steps 1 and 3 of stage s dequantised; A of
+//                  k-steps 2 and 1 read
+//   barrier        X of stage s + 1 has landed, and every wave is done
+//                  with the buffer of stage s - 1
+//   k-steps 1, 3   B of k-steps 0 and 2 of stage s + 1 dequantised; A of
+//                  k-step 3 and of k-step 0 of stage s + 1 read; X of stage
+//                  s + 3 copied into the buffer of stage s - 1 (global to
+//                  LDS, no registers); on a block's first stage, the whole
+//                  next block of W requested first
+// so no operand read waits on the barrier: they are all issued half a stage
+// or more before their matrix instructions.
 // Vector work sits between the matrix instructions (scheduling groups):
 // the wave issues in order and a matrix instruction occupies the matrix
 // core for 32 cycles, so only interleaved vector work runs under it.
@@ -84,7 +90,7 @@ struct RwBlock {
 
 __global__ __launch_bounds__(kRwThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void q4k_gemm_rw_kernel(const GemmBatch batch, uint32_t qmask) {
-    __shared__ uint4 xs[3][kRwBM * kRwRowChunks];
+    __shared__ uint4 xs[4][kRwBM * kRwRowChunks];
 
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
@@ -102,7 +108,7 @@ void q4k_gemm_rw_kernel(const GemmBatch batch, uint32_t qmask) {
 
     // ---- X: copied from global memory straight into LDS (buffer loads with
     // the LDS bit: the 64 lanes of one instruction fill 1 KB of LDS in lane
-    // order, no registers), three buffers deep.  Wave w fills chunks
+    // order, no registers), four buffers deep.  Wave w fills chunks
     // 512 w + 64 j + lane (j < 8) of a stage's slab: row c / 8, slot c % 8,
     // which holds operand chunk slot ^ f(row) (rw_chunk's swizzle).  Rows
     // past M read zeros (the buffer ends at row M - 1).
@@ -211,33 +217,48 @@ void q4k_gemm_rw_kernel(const GemmBatch batch, uint32_t qmask) {
                 __builtin_amdgcn_sched_group_barrier(0x090, 2, 0);  // DS / VMEM
         }
     };
-    // One stage, quarter c (compile-time) of block b = s / 4: multiply stage
-    // s from buffer cur (its k-step 0 operands already in a0, B of k-steps 0
-    // and 2 already in bq), copy X of stage s + 2 into buffer xdma, and
-    // dequantise half 1 of stage s and half 0 of stage s + 1.  At c = 0 the
-    // block ring turns (W of block b moves to cur_b) and block b + 1 is
-    // requested into nxt_b.  Two scheduling regions of 32 matrix
-    // instructions each.
+    // One stage, quarter c (compile-time) of block b = s / 4, X in buffer c:
+    // multiply stage s (its k-step 0 operands already in a0, B of k-steps 0
+    // and 2 already in bq), dequantise half 1 of stage s and half 0 of stage
+    // s + 1, read the k-step 0 operands of stage s + 1 and copy X of stage
+    // s + 3.  At c = 0 the block ring turns (W of block b moves to cur_b) and
+    // block b + 1 is requested into nxt_b.  Two scheduling regions of 32
+    // matrix instructions each, with the barrier between them.
     RwBlock cur_b, nxt_b;
-    auto stage = [&](int s, auto c_c, const uint4* cur, const uint4* nxt, uint4* xdma) {
+    auto stage = [&](int s, auto c_c) {
         constexpr int c = decltype(c_c)::value;
+        const uint4* cur = xs[c];
+        const uint4* nxt = xs[(c + 1) & 3];
+        uint4* xdma = xs[(c + 3) & 3];
         if constexpr (c == 0) cur_b = nxt_b;
-        // region 1: k-steps 0 and 2, with half 1 of this stage dequantised,
-        // the k-step 1 operands read, X of stage s + 2 copied
+        // region 1: k-steps 0 and 2, half 1 of this stage dequantised, the
+        // k-step 1 operands read
         read_a(cur, 2, a1);
         mma(0, a0);
         dequant_half(cur_b, c, 1);
         read_a(cur, 1, a0);
         mma(2, a1);
-        dma_x(s + 2, xdma);
         interleave(std::integral_constant<int, 8>{}, std::integral_constant<int, 3>{},
                    std::integral_constant<int, 8>{});
+        fence();
+        // X of stage s + 1 (copied in the second region of stage s - 2) has
+        // landed.  Issued after it: at c = 1 the block loads of stage s - 1
+        // (10) and the X copy of stage s - 1 (8); else that X copy alone.  A
+        // bare barrier: __syncthreads would also wait for the loads still in
+        // flight.  Past it every wave is done with the buffer of stage s - 1.
+        if constexpr (c == 1)
+            asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
         fence();
         if constexpr (c == 0) {
             load_block((s >> 2) + 1, nxt_b);
             fence();
         }
-        // region 2: k-steps 1 and 3, with half 0 of the next stage dequantised
+        // region 2: k-steps 1 and 3, half 0 of the next stage dequantised,
+        // the operands of k-step 3 and of the next stage's k-step 0 read, X
+        // of stage s + 3 copied into the buffer stage s - 1 used
         read_a(cur, 3, a1);
         mma(1, a0);
         if constexpr (c < 3) {
@@ -247,20 +268,11 @@ void q4k_gemm_rw_kernel(const GemmBatch batch, uint32_t qmask) {
             scales(nxt_b, 0);
             dequant_half(nxt_b, 0, 0);
         }
-        mma(3, a1);
-        interleave(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{},
-                   std::integral_constant<int, 0>{});
-        fence();
-        // X of stage s + 1 (copied a stage ago) has landed.  Issued after it:
-        // the block loads of the last and this stage when their c was 0 (10
-        // each) and this stage's X copy (8).  A bare barrier: __syncthreads
-        // would also wait for the loads still in flight.
-        if constexpr (c == 0 || c == 1)
-            asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
         read_a(nxt, 0, a0);
+        mma(3, a1);
+        dma_x(s + 3, xdma);
+        interleave(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{},
+                   std::integral_constant<int, 16>{});
         fence();
     };
     using C0 = std::integral_constant<int, 0>;
@@ -271,28 +283,19 @@ void q4k_gemm_rw_kernel(const GemmBatch batch, uint32_t qmask) {
     load_block(0, nxt_b);
     dma_x(0, xs[0]);
     dma_x(1, xs[1]);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    dma_x(2, xs[2]);
+    // W block 0 and this wave's part of X stage 0 have landed (the copies of
+    // stages 1 and 2, 16 instructions, may still be in flight)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     scales(nxt_b, 0);
     dequant_half(nxt_b, 0, 0);
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
     read_a(xs[0], 0, a0);
-    // buffers: stage s reads s % 3, fills (s + 2) % 3 with stage s + 2
-    int b0 = 0, b1 = 1, b2 = 2;
-    auto turn = [&] {
-        const int t0 = b0;
-        b0 = b1;
-        b1 = b2;
-        b2 = t0;
-    };
     for (int s = 0; s < nstage; s += 4) {
-        stage(s, C0{}, xs[b0], xs[b1], xs[b2]);
-        turn();
-        stage(s + 1, C1{}, xs[b0], xs[b1], xs[b2]);
-        turn();
-        stage(s + 2, C2{}, xs[b0], xs[b1], xs[b2]);
-        turn();
-        stage(s + 3, C3{}, xs[b0], xs[b1], xs[b2]);
-        turn();
+        stage(s, C0{});
+        stage(s + 1, C1{});
+        stage(s + 2, C2{});
+        stage(s + 3, C3{});
     }
 
     // ---- Y: lane holds D[m][n] for n = 32 jb + lane % 32 and
