@@ -49,12 +49,18 @@ DEPENDENCY_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]   # q|k|v, o, gate|up, down
 # The kernel each timed leg's launches run (for the kernel-trace lookup).
 GEMV_KERNEL = "jq4k::q4k_gemv_kernel"
 GEMV_BATCHED_KERNEL = "jq4k::q4k_gemv_batched_kernel"
-WS_KERNEL = "jq4k::q4k_gemm_ws_kernel<false>"
+RW_KERNEL = "jq4k::q4k_gemm_rw_kernel"
+# Untimed launches before a matrix-core leg's timed ones: after the leg's
+# set-up the GPU needs a few hundred microseconds of load to reach its
+# sustained clock (the M = 2048 layer measured 483 us per launch over 10
+# steps after 2 warm-up launches, 422 us over 40).
+MFMA_WARMUP = 10
 SKINNY_KERNEL = "jq4k::q4k_gemm_skinny_kernel<3>"
 # Marker launches of the probe kernel separate the legs of a --profile run:
 # a read of 16 bytes with PROFILE_MARKER + leg index workgroups.
 PROFILE_MARKER = 1000
-PROFILE_LEGS = ["copy_512MiB", "single", "decode", "lm_head", "m33", "prefill", "lm_head_m512"]
+PROFILE_LEGS = ["copy_512MiB", "single", "decode", "lm_head", "m33", "prefill", "lm_head_m512",
+                "warmup"]
 
 
 def parse():
@@ -62,7 +68,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--only", default="",
@@ -338,11 +344,11 @@ def prefill_leg(torch, jq4k, args, traces):
 
     graph = graph_ok(args, True)
     steps = args.prefill_steps
-    secs = timed(torch, step_batched, steps, 2, graph)
+    secs = timed(torch, step_batched, steps, MFMA_WARMUP, graph)
     modes = {}
     for name, fn, launches in (("batched_1", None, 1), ("dependency_4", step_grouped, 4),
                                ("separate_7", step_separate, 7)):
-        t = secs if fn is None else timed(torch, fn, steps, 2, graph)
+        t = secs if fn is None else timed(torch, fn, steps, MFMA_WARMUP, graph)
         modes[name] = {"launches_per_step": launches, "us_per_step": round(t / steps * 1e6, 1),
                        "TFLOP_s": round(flops * steps / t / 1e12, 1)}
     per_proj = {}
@@ -350,7 +356,7 @@ def prefill_leg(torch, jq4k, args, traces):
         def one(i, p=p, N=N, K=K):
             check(jq4k, L.jq4k_gemm(Ws[i % copies][p].data_ptr(), Xs[p].data_ptr(),
                                     Ys[p].data_ptr(), M, N, K, stream_ptr(torch)))
-        t = timed(torch, one, steps, 1, graph)
+        t = timed(torch, one, steps, MFMA_WARMUP, graph)
         per_proj[name] = {"N": N, "K": K, "us": round(t / steps * 1e6, 2),
                           "TFLOP_s": round(2.0 * M * N * K * steps / t / 1e12, 1)}
     t1 = secs / steps
@@ -358,7 +364,7 @@ def prefill_leg(torch, jq4k, args, traces):
                         "jq4k_gemm_batched launch per step (the seven are independent here)",
             "value": round(flops / t1 / 1e12, 1), "unit": "TFLOP/s", "steps": steps,
             "ms_per_step": round(t1 * 1e3, 4), "rotation_copies": copies,
-            "roofline": roofline("mfma", flops, t1, WS_KERNEL, "prefill", traces,
+            "roofline": roofline("mfma", flops, t1, RW_KERNEL, "prefill", traces,
                                  "flops_per_launch"),
             "modes": modes, "per_projection": per_proj}
 
@@ -431,12 +437,12 @@ def lm_head_m512_leg(torch, jq4k, args, traces):
         check(jq4k, L.jq4k_gemm(Wd[i % copies].data_ptr(), Xd.data_ptr(), Yd.data_ptr(), M, N, K,
                                 stream_ptr(torch)))
     steps = max(5, args.prefill_steps)
-    t = timed(torch, one, steps, 2, graph_ok(args, True)) / steps
+    t = timed(torch, one, steps, MFMA_WARMUP, graph_ok(args, True)) / steps
     flops = 2.0 * M * N * K
     return {"workload": "Qwen3-4B-shaped LM head as Q4_K, N=151936 x K=2560, M=512, seed 4",
             "N": N, "K": K, "M": M, "rotation_copies": copies, "us": round(t * 1e6, 1),
             "TFLOP_s": round(flops / t / 1e12, 1),
-            "roofline": roofline("mfma", flops, t, WS_KERNEL, "lm_head_m512", traces,
+            "roofline": roofline("mfma", flops, t, RW_KERNEL, "lm_head_m512", traces,
                                  "flops_per_launch")}
 
 
@@ -486,8 +492,9 @@ def swiglu_leg(torch, jq4k, args, traces):
         def grouped(i):
             check(jq4k, grouped_fn(ctypes.addressof(descs[i % copies]), 2, stream_ptr(torch)))
         steps = args.steps if M == 1 else args.prefill_steps
-        tf = timed(torch, fused, steps, 3, graph_ok(args, True)) / steps
-        tg = timed(torch, grouped, steps, 3, graph_ok(args, True)) / steps
+        w = 3 if M == 1 else MFMA_WARMUP
+        tf = timed(torch, fused, steps, w, graph_ok(args, True)) / steps
+        tg = timed(torch, grouped, steps, w, graph_ok(args, True)) / steps
         if M == 1:
             out["m1"] = {"N": N, "K": K, "weight_bytes": wbytes, "fused_us": round(tf * 1e6, 2),
                          "fused_GB_s": round(wbytes / tf / 1e9, 1),
@@ -754,16 +761,25 @@ def profile_run(torch, jq4k):
             garr[p] = jq4k.GemmDesc(Wc[p].data_ptr(), Xg[p].data_ptr(), Yg[p].data_ptr(), 2048,
                                     N, K)
         garrs.append(garr)
+    # the matrix-core legs start warm, as the benchmark times them (the
+    # warm-up launches under a marker of their own)
+    marker("warmup")
+    for i in range(MFMA_WARMUP):
+        check(jq4k, L.jq4k_gemm_batched(ctypes.addressof(garrs[i % len(garrs)]), 7, s))
     marker("prefill")
-    for i in range(4):
+    for i in range(8):
         check(jq4k, L.jq4k_gemm_batched(ctypes.addressof(garrs[i % len(garrs)]), 7, s))
     torch.cuda.synchronize()
     del Wg, Xg, Yg, garrs
 
     X512 = to_dev(torch, X.view(np.int16))
     Y512 = torch.empty((512, 151936), dtype=torch.float32, device="cuda:0")
+    marker("warmup")
+    for i in range(MFMA_WARMUP):
+        check(jq4k, L.jq4k_gemm(Wr[i % len(Wr)][0].data_ptr(), X512.data_ptr(), Y512.data_ptr(),
+                                512, 151936, 2560, s))
     marker("lm_head_m512")
-    for i in range(4):
+    for i in range(8):
         check(jq4k, L.jq4k_gemm(Wr[i % len(Wr)][0].data_ptr(), X512.data_ptr(), Y512.data_ptr(),
                                 512, 151936, 2560, s))
     torch.cuda.synchronize()

@@ -129,7 +129,8 @@ def traffic(fetch_dir, write_dir, out, cmd):
 
 MARKER_KERNEL = "probe_read_kernel"
 MARKER_BASE = 1000
-PROFILE_LEGS = ["copy_512MiB", "single", "decode", "lm_head", "m33", "prefill", "lm_head_m512"]
+PROFILE_LEGS = ["copy_512MiB", "single", "decode", "lm_head", "m33", "prefill", "lm_head_m512",
+                "warmup"]
 
 
 def _segments(rows, key, wg_of, name_of):

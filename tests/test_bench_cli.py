@@ -24,7 +24,7 @@ def test_entry_points_defined():
                  "cpu_baseline_prefill", "main"):
         assert callable(getattr(b, name)), name
     assert set(b.LEGS) >= {"single", "decode", "m33", "prefill", "lm_head", "lm_head_m512"}
-    assert b.WS_KERNEL.startswith("jq4k::q4k_gemm_")
+    assert b.RW_KERNEL.startswith("jq4k::q4k_gemm_")
 
 
 def test_roofline_object_from_events_and_trace():
