@@ -140,10 +140,11 @@ int gemv_batch_rows(int N, int K) {
 }
 
 // MFMA tile (rows of M per workgroup) for the largest M of a launch: 64 up
-// to M = 64; then 128; 256 (the wave-specialised kernel) from M = 2048 for a
-// single matmul and from M = 512 for a grouped launch, whose several
-// problems fill the GPU with fewer, larger tiles.  Measured on the Qwen3-4B
-// projections at M = 128 .. 4096.
+// to M = 64; then 128; 256 from M = 2048 for a single matmul and from M = 512
+// for a grouped launch, whose several problems fill the GPU with fewer,
+// larger tiles (measured on the Qwen3-4B projections at M = 128 .. 4096).
+// A 256-row launch runs the wave-specialised 256 x 128 kernel, or the
+// register-W 256 x 256 one where rw_pays (below).
 int mfma_tile_for(int M, bool grouped) {
     if (M <= 64) return 64;
     return M >= (grouped ? 512 : 2048) ? 256 : 128;

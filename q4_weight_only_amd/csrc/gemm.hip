@@ -337,11 +337,13 @@ long gemm_splitk_plan(const int* M, const int* N, const int* K, int count, long 
     return splitk_workspace_bytes(M, N, splits, count, 64, 64);
 }
 
-// tile: 64, 128 or 256 rows of M per workgroup, for the whole batch.  The
-// 64-row tile is 64 columns wide: at M <= 64 the matmul streams W like a
-// GEMV, and narrow tiles give it four times the workgroups of 256-wide ones
-// (1.9x faster on a Qwen3-4B layer at M = 33).  The 256-row tile is the
-// wave-specialised kernel of gemm_ws.hip.
+// tile: 64, 128 or 256 rows of M per workgroup, or one of the 256 x 256
+// codes, for the whole batch.  The 64-row tile is 64 columns wide: at
+// M <= 64 the matmul streams W like a GEMV, and narrow tiles give it four
+// times the workgroups of 256-wide ones (1.9x faster on a Qwen3-4B layer at
+// M = 33).  256 is the wave-specialised 256 x 128 kernel of gemm_ws.hip;
+// kTileRw the register-W kernel of gemm_rw.hip; kTileBig the single-role
+// kernel of gemm_big.hip (by explicit path only).
 hipError_t launch_gemm_mfma(const uint8_t* const* W, const uint16_t* const* X, float* const* Y,
                             const int* M, const int* N, const int* K, int count, int tile,
                             hipStream_t stream) {
