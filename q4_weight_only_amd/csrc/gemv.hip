@@ -4,16 +4,15 @@
 // README, "At a glance": INT4 dequant-fused GEMV).  HBM-bound: every byte of
 // W is read once (0.5625 B per weight); no weight is ever formed.
 //
-// Arithmetic: the factored form on the matrix cores, certified per row.
-// Sub-block s of a block adds ds_s * S1_s - dm_s * S0_s to its row, with
-// ds = d*sc and dm = dmin*m (exact in fp32: at most 11 + 6 significant
-// bits), S1 = sum q x over the sub-block's 32 weights and S0 = sum x.  The
-// 4-bit codes go into v_mfma_f32_16x16x32_f16 as they sit in the block: a
-// nibble masked in place in a 16-bit half reads as the binary16 subnormal
-// q * 2^-24 (low nibble) or q * 2^-20 (high nibble), exactly.  x is staged
-// as binary16 times 2^-sh per block of 256 values (sh from the block's
-// largest exponent), so every product q * x is exact and the matrix cores
-// sum them in fp32.
+// Arithmetic: the factored form, certified per row.  Sub-block s of a block
+// adds ds_s * S1_s - dm_s * S0_s to its row, with ds = d*sc and dm = dmin*m
+// (exact in fp32: at most 11 + 6 significant bits), S1 = sum q x over the
+// sub-block's 32 weights and S0 = sum x.  The 4-bit codes go into
+// v_dot2_f32_f16 as they sit in the block: a nibble masked in place in a
+// 16-bit half reads as the binary16 subnormal q * 2^-24 (low nibble) or
+// q * 2^-20 (high nibble), exactly.  x is staged as binary16 times 2^-sh per
+// block of 256 values (sh from the block's largest exponent), so every
+// product q * x is exact and each dot2 step sums two of them into fp32.
 //
 // The factored form loses accuracy where ds*S1 and dm*S0 cancel (weights
 // near zero against large scales), so every row also carries a bound on its
@@ -21,28 +20,32 @@
 // does not certify the accuracy contract is recomputed exactly (below).
 // Rows of randomly drawn blocks certify with a margin of about 8.
 //
-// Matrix-core tile: 16 rows of W at one block column kb.  B column n is
-// block (row n, kb); lane 16c + n holds 8 codes of its quarter c (the
-// quarter's code bytes pair sub-blocks 2c and 2c+1).  Row m < 8 of A is
-// sub-block m of x: lane 16c + m supplies its values where sub-block m is
-// the one k-group c covers in the instruction (2c for the instructions on
-// low nibbles, 2c+1 for high) and zeros otherwise; rows 8..15 are zero.
-// Eight instructions per tile (4 code pairs x low/high nibbles) leave
-// D[s][n] = S1_s of block n (scaled) in lane 16 (s / 4) + n, accumulator
-// s % 4: lanes 0..31 ("S lanes") hold sub-blocks 0..3 / 4..7 of block n.
+// Work decomposition.  A workgroup owns R consecutive rows, R*nb
+// consecutive blocks of W: one contiguous span of memory (for a gate/up
+// pair, the span of the second matrix follows the first's in the task
+// list).  The span is cut into tasks of one quarter block (the header and
+// the 32 code bytes of sub-blocks 2c and 2c+1: 64 weights); the 256 threads
+// sweep the tasks in rounds, lanes 4j .. 4j+3 of a round taking the four
+// quarters of one block, so every round reads 64 consecutive blocks.  A
+// thread's quarter c = t & 3 never changes; two rounds of loads are in
+// flight per thread.
 //
-// Per tile, every S lane combines its four sub-blocks: a = dm S0,
-// r = ds D - a, and sums r (the output) and |r| (L: sum over sub-blocks of
-// |sum w x| <= sum |w x|).  Lanes 32..63 ("T lanes", D = 0) sum the error
-// scale B = sum over sub-blocks of (15 |ds| + |dm|) T0 with T0 = sum |x|,
-// which bounds sum (|ds| q + |dm|) |x| and with it every rounding error.
-// S0 and T0 are staged with x.  Each tile's sums are scaled by 2^sh_kb.
+// Per quarter, each sub-block gives r = ds S1 - dm S0 (one fma after the
+// exact dm S0 rounding), and the quarter adds r_2c + r_2c+1 (the output),
+// |r_2c| + |r_2c+1| (L: at most sum |w x|) and the error scale
+// B = sum over its sub-blocks of (15 |ds| + |dm|) T0, T0 = sum |x|, which
+// bounds sum (|ds| q + |dm|) |x| and with it every rounding error.  S0 and
+// T0 are staged with x.  The three sums are scaled by 2^sh_kb, added over
+// the block's quarters with two DPP steps (the same bits in all four lanes)
+// and left in LDS per block; each row then adds its nb blocks in order.
+// A row's sums therefore do not depend on R or on the launch: the same bits
+// for every grouping of the rows (no atomics on values).
 //
 // Certificate.  With u = 2^-24, every rounding error of the row is at most
-// E = (192 + nb) u B: the matrix cores' fp32 sums (at most 2u per addition
-// of 32 exact products: 64u, taken twice), the staged S0 and T0 (9
-// additions), the combine (3 roundings) and the row's sums (fewer than
-// 8 + nb additions deep).  The row is accepted when
+// E = (192 + nb) u B: the dot2 chains (16 steps of two exact products per
+// sub-block, at most two roundings a step: 32u; the budget allows 128u),
+// the staged S0 and T0 (9 additions), the combine (3 roundings) and the
+// row's sums (fewer than 8 + nb additions deep).  The row is accepted when
 //     E <= 1.9e-3 * max(L - 2E, |y| - E) + 0.99e-5,
 // the slack to 2e-3 and 1e-5 covering w against the fp32 weight (u |w|) and
 // the rounding of E itself.  Otherwise -- and for every row when some x is
@@ -51,54 +54,45 @@
 // weight (d*sc*q - dmin*m rounded once) times x, summed in fp64, rounded
 // once to fp32.
 //
-// Work decomposition.  A workgroup owns R consecutive rows (ceil(R/16)
-// groups of 16) of each of its matrices.  Its tiles (group g, column kb) are
-// numbered g*nb + kb and wave w takes tiles w, w+4, w+8, ..., so the four
-// waves sweep the same 16 rows at neighbouring columns; three tiles per lane
-// are in flight.  Within a group a wave's tiles share kb mod 4 (its
-// "class"); each lane sums its tiles of the group in order and leaves the
-// sums in LDS under (row, class), and each row adds its four classes in
-// order: deterministic, and the same bits whatever R or the launch (no
-// atomics on values).
-//
-// LDS layout of the staged x, per block kb (40 chunks of 16 B): chunk
-// 5 s + p holds the binary16 x of sub-block s, values 8p + {0,2,1,3,4,6,5,7}
-// (the order of the codes as masked from two consecutive code dwords: bytes
-// 0, 2, 1, 3 of each); the stride of 5 puts the four sub-blocks an
-// instruction reads on different banks.
+// LDS layout of the staged x.  Chunk g holds the binary16 x[8g .. 8g+7] in
+// the order 0, 2, 1, 3, 4, 6, 5, 7 (the order of the codes as masked from
+// two consecutive code dwords: bytes 0, 2, 1, 3 of each).  The 8 chunks a
+// quarter task reads (g = 32 kb + 8 c + i: i = 0..3 sub-block 2c, 4..7
+// sub-block 2c+1) sit at 9 (4 kb + c) + i.  The 64 lanes of a round read
+// one chunk index i of 64 consecutive groups, and the stride of 9 spreads
+// them over the banks without conflicts; a thread's 8 reads are one base
+// address plus immediate offsets.
 #include "q4k_device.h"
 
 namespace jq4k {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvBatchMax = 16;  // problems per batched launch
-constexpr int kGemvDepth = 3;      // tiles in flight per lane
+constexpr int kGemvDepth = 2;      // rounds of quarter loads in flight per thread
 constexpr int kGemvMaxK = 16384;
 constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
-constexpr int kSubChunks = 5;   // LDS chunk stride of a sub-block's 4 chunks of x
-constexpr int kXaChunks = 40;   // LDS chunks per block of x (8 sub-blocks)
+constexpr int kXGroupStride = 9;   // LDS chunk stride of a quarter's 8 chunks of x
 
-typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
 typedef __attribute__((ext_vector_type(4))) float float4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 
 __host__ __device__ constexpr int gemv_shift_words(int nb) { return (nb + 3) & ~3; }
-__host__ __device__ constexpr int gemv_groups(int R) { return (R + 15) >> 4; }
+__device__ __forceinline__ int x_group_base(int kb, int c) { return (4 * kb + c) * kXGroupStride; }
+__device__ __forceinline__ int x_chunk_phys(int g) { return (g >> 3) * kXGroupStride + (g & 7); }
 
 // LDS of a workgroup with R rows of each of `mats` matrices (bytes):
-//   staged x              nb * 40 chunks
-//   zeros                 4 chunks (the A values of inactive lanes)
-//   S0[8], T0[8]          per block, 16 floats
+//   staged x              nb * 36 chunks of 16 B
+//   S0, T0                per (block, quarter) a float4 {S0 2c, S0 2c+1, T0 2c, T0 2c+1}
 //   sh                    per block, one int (padded to 16 B)
-//   row partials          mats * 16 ceil(R/16) rows x 4 classes x 4 lane slots x 2 floats
+//   block partials        3 x mats * R * nb floats (the sums y, L, B of each block)
 //   row results           mats * R floats
 //   recompute list        1 + mats * R ints (count, then rows)
 __host__ __device__ constexpr size_t gemv_lds_layout(int nb, int R, int mats) {
-    return static_cast<size_t>(nb) * kXaChunks * 16 + 64 + static_cast<size_t>(nb) * 64 +
+    return static_cast<size_t>(nb) * 4 * kXGroupStride * 16 + static_cast<size_t>(nb) * 64 +
            static_cast<size_t>(gemv_shift_words(nb)) * 4 +
-           static_cast<size_t>(mats) * gemv_groups(R) * 16 * 16 * 8 +
-           static_cast<size_t>(mats) * R * 4 + (1 + static_cast<size_t>(mats) * R) * 4;
+           3 * static_cast<size_t>(mats) * R * nb * 4 + static_cast<size_t>(mats) * R * 4 +
+           (1 + static_cast<size_t>(mats) * R) * 4;
 }
 
 size_t gemv_lds_bytes(int nb, int R, int mats) { return gemv_lds_layout(nb, R, mats); }
@@ -136,9 +130,24 @@ __device__ __forceinline__ float pow2f(int e) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(127 + e) << 23);
 }
 
-struct TileLoad {
-    uint4 hdr, qa, qb;   // header; code dwords 0..3 and 4..7 of the lane's quarter
+// Two binary16 codes (as masked in place) times two staged binary16 x, added
+// to an fp32 sum.
+__device__ __forceinline__ float dot2_codes(uint32_t codes, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, codes),
+                                  __builtin_bit_cast(half2_t, x), acc, false);
+}
+
+struct QuarterLoad {
+    uint4 hdr, qa, qb;   // header; code dwords 0..3 and 4..7 of the quarter
 };
+
+__device__ __forceinline__ QuarterLoad load_quarter(const uint8_t* blk, int c) {
+    QuarterLoad r;
+    r.hdr = load16(blk);
+    r.qa = load16(blk + 16 + 32 * c);
+    r.qb = load16(blk + 32 + 32 * c);
+    return r;
+}
 
 // One row recomputed by one wave, lane l taking sub-block l / 8, weights
 // 4 (l % 8) .. + 3 of every block: each fp32 weight (one rounding of
@@ -190,7 +199,7 @@ __device__ float exact_row(const uint8_t* rowp, int nb, const uint4* __restrict_
 }
 
 // One workgroup's share of a GEMV: rows [tile * R, tile * R + R) of W.
-// kPair: the same rows of a second matrix W2 follow in the tile list (the
+// kPair: the same rows of a second matrix W2 follow in the task list (the
 // gate and up projections of an MLP), and the row's output is
 // silu(gate) * up (SwiGLU) instead of the dot product.
 // kNorm: x is RMS-normalised while it is staged, x_hat = bf16(x / sqrt(
@@ -207,44 +216,39 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int c = t & 3;
     const long row0 = tile * R;
     const int rows = static_cast<int>(min(static_cast<long>(R), N - row0));
-    const int G = gemv_groups(rows);            // row groups per matrix here
-    const int Gt = kMats * G;
-    const int Gl = gemv_groups(R);              // ... in a full workgroup (LDS carve)
+    const int nblk = rows * nb;                 // blocks per matrix here
+    const int nblk_all = kMats * nblk;
+    const int pstride = kMats * R * nb;         // one of the three partial arrays
 
-    uint4* xa = smem;
-    uint4* zero4 = xa + nb * kXaChunks;
-    float* zs = reinterpret_cast<float*>(zero4 + 4);
-    int* xsh = reinterpret_cast<int*>(zs + nb * 16);
-    float2* part = reinterpret_cast<float2*>(xsh + gemv_shift_words(nb));
-    float* yrow = reinterpret_cast<float*>(part + kMats * Gl * 16 * 16);
+    uint4* xs = smem;
+    float4_t* zq = reinterpret_cast<float4_t*>(xs + nb * 4 * kXGroupStride);
+    int* xsh = reinterpret_cast<int*>(zq + nb * 4);
+    float* part = reinterpret_cast<float*>(xsh + gemv_shift_words(nb));
+    float* yrow = part + 3 * pstride;
     int* flist = reinterpret_cast<int*>(yrow + kMats * R);
 
-    // Lane roles.  As an A/B lane: k-group c, row / column m of the tile.
-    const int c = lane >> 4, m = lane & 15;
-    const bool act_lo = m == 2 * c, act_hi = m == 2 * c + 1;   // rows 8..15: never
-    const int zero_chunk = nb * kXaChunks;
-    const int alo_base = act_lo ? kSubChunks * m : zero_chunk;
-    const int ahi_base = act_hi ? kSubChunks * m : zero_chunk;
-    const int alo_stride = act_lo ? kXaChunks : 0;
-    const int ahi_stride = act_hi ? kXaChunks : 0;
-    // As a D lane: S (lanes 0..31: D = S1) or T (32..63: D = 0), sub-blocks
-    // 4 half + 0..3 of block (row m, kb)
-    const bool laneT = lane >= 32;
-    const bool half = ((lane >> 4) & 1) != 0;
-    const int zoff = (laneT ? 8 : 0) + (half ? 4 : 0);
-    // scale bytes of sub-blocks 4 half + 0..3 (Q4_K packing): half 0 the low
-    // six bits of scales[i] and scales[4+i]; half 1 the nibbles of
-    // scales[8+i] plus bits 6..7 of scales[i] and scales[4+i] as bits 4..5.
-    // One branch-free formula with lane-constant masks.
-    const uint32_t low_mask = half ? 0x0F0F0F0Fu : 0x3F3F3F3Fu;
-    const uint32_t top_mask = half ? 0x30303030u : 0u;
-    const int qoff = 16 + 32 * c;
+    const uint8_t* Wt = W + row0 * nb * kBlockBytes;
+    const uint8_t* Wt2 = kPair ? W2 + row0 * nb * kBlockBytes : nullptr;
+    // block b of the task list: W's span, then (kPair) W2's
+    auto blk_ptr = [&](int b) {
+        if (kPair && b >= nblk) return Wt2 + static_cast<long>(b - nblk) * kBlockBytes;
+        return Wt + static_cast<long>(b) * kBlockBytes;
+    };
+    const int b0 = t >> 2;  // this thread's first block; +64 per round
 
-    // x first, then the first tiles of weights (vmcnt retires in order), so
-    // that staging x waits only for x.
+    // Memory requests in the order they are needed (vmcnt retires in order):
+    // x first, then the first kGemvDepth rounds of weights, so that staging
+    // x waits only for x and each round waits only for its own weights.
+    // Every load is unconditional, past the end a repeat of the last chunk
+    // or block: with loads under branches the compiler's count of loads in
+    // flight turns pessimistic at the joins and it waits for all of them,
+    // which undoes the prefetch.
     const int nxc = nb * 32;  // 16-byte chunks of x, at most 2048 (K <= 16384)
+    const int nround = (nblk_all + 63) >> 6;   // the same for every thread
+    auto round_block = [&](int round) { return min(b0 + 64 * round, nblk_all - 1); };
     uint4 xv[kGemvMaxXChunksPerThread];
     uint4 gv[kNorm ? kGemvMaxXChunksPerThread : 1];
 #pragma unroll
@@ -256,55 +260,10 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
             if constexpr (kNorm) gv[q] = gamma[g];
         }
     }
-
-    // This wave's tiles: w, w + 4, ... of the Gt * nb.  Loads past the last
-    // tile repeat it (every load below is unconditional: with loads under
-    // branches the compiler's count of loads in flight turns pessimistic at
-    // the joins and it waits for all of them, which undoes the prefetch).
-    const int ntiles = Gt * nb;
-    const int mine = ntiles > wave ? (ntiles - wave + 3) >> 2 : 0;
-    auto group_row = [&](int g) {
-        const bool second = kPair && g >= G;
-        const int gg = second ? g - G : g;
-        const long r = row0 + min(16 * gg + m, rows - 1);
-        return (second ? W2 : W) + r * nb * kBlockBytes + qoff;
-    };
-    int pi = 0, pg = 0, pkb = wave;
-    while (pkb >= nb) {
-        pkb -= nb;
-        ++pg;
-    }
-    const uint8_t* prow = group_row(pg);
-    auto issue = [&](TileLoad& l) {
-        const uint8_t* p = prow + pkb * kBlockBytes;
-        l.qa = load16(p);
-        l.qb = load16(p + 16);
-        l.hdr = load16(p - qoff);
-        if (pi + 1 < mine) {
-            ++pi;
-            pkb += 4;
-            const int g0 = pg;
-            while (pkb >= nb) {
-                pkb -= nb;
-                ++pg;
-            }
-            if (pg != g0) prow = group_row(pg);
-        }
-    };
-    // Two tiles go out before x is staged, the third after: a smaller first
-    // burst of weight loads lets x (queued behind it) arrive sooner
-    // (measured: 2 best of 0..3 on the decode layer and the LM head).
-    constexpr int kEarly = 2;
-    TileLoad ld[kGemvDepth];
-    if (mine > 0) {
+    QuarterLoad ld[kGemvDepth];
 #pragma unroll
-        for (int u = 0; u < kEarly; ++u) issue(ld[u]);
-    }
+    for (int u = 0; u < kGemvDepth; ++u) ld[u] = load_quarter(blk_ptr(round_block(u)), c);
 
-    // LDS that is read before it is written: the zeros, the partials (a
-    // class without blocks, when nb < 4, stays zero) and the list's count.
-    if (t < 4) zero4[t] = make_uint4(0u, 0u, 0u, 0u);
-    for (int i = t; i < Gt * 16 * 16; i += kGemvThreads) part[i] = make_float2(0.f, 0.f);
     if (t == 0) flist[0] = 0;
 
     float rnorm = 0.f;
@@ -322,7 +281,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
         __shared__ float wave_ss[kGemvThreads / 64];
-        if ((t & 63) == 0) wave_ss[t >> 6] = ss;
+        if (lane == 0) wave_ss[wave] = ss;
         __syncthreads();
         const float total = (wave_ss[0] + wave_ss[1]) + (wave_ss[2] + wave_ss[3]);
         rnorm = rsqrtf(total / static_cast<float>(nb * kQK) + eps);
@@ -399,133 +358,93 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
             t0 = quad_sum(t0);
             if (g < nxc) {
                 inexact |= bad;
-                const int kb = g >> 5, s = (g >> 2) & 7, p = g & 3;
-                xa[kb * kXaChunks + kSubChunks * s + p] = make_uint4(h0, h1, h2, h3);
-                if (p == 0) {
-                    zs[kb * 16 + s] = s0;
-                    zs[kb * 16 + 8 + s] = t0;
+                xs[x_chunk_phys(g)] = make_uint4(h0, h1, h2, h3);
+                if ((g & 3) == 0) {
+                    // sub-block s = 2 (s / 2) + (s & 1): quarter s / 2, slot s & 1
+                    const int s = (g >> 2) & 7;
+                    float* z = reinterpret_cast<float*>(zq + (g >> 5) * 4 + (s >> 1));
+                    z[s & 1] = s0;
+                    z[2 + (s & 1)] = t0;
                 }
-                if ((g & 31) == 0) xsh[kb] = sh;
+                if ((g & 31) == 0) xsh[g >> 5] = sh;
             }
         }
     }
     const bool x_inexact = __syncthreads_or(inexact) != 0;
-    if (mine > 0) {
-#pragma unroll
-        for (int u = kEarly; u < kGemvDepth; ++u) issue(ld[u]);
-    }
 
-    // The tiles.  The lane's running sums over the tiles of its group, all
-    // of one class kb mod 4 (each (group, class) belongs to one wave):
-    //   S lanes   v1 = sum r (the output), v2 = sum |r| (L)
-    //   T lanes   v2 = sum |dm| T0, v3 = sum 15 |d sc| T0 (v2 + v3 = B)
-    // each tile's sums scaled by 2^sh_kb.  They go to slot lane / 16 of
-    // (row, class) in `part` when the wave moves to the next group, so a
-    // row's sums do not depend on R or on which wave ran which tile.
-    int cg = 0, ckb = wave;
-    while (ckb >= nb) {
-        ckb -= nb;
-        ++cg;
-    }
-    const int slot = lane >> 4;
-    float v1 = 0.f, v2 = 0.f, v3 = 0.f;
-    auto flush = [&](int g, int kb) {
-        part[((g * 16 + m) * 4 + (kb & 3)) * 4 + slot] = make_float2(v1, laneT ? v2 + v3 : v2);
-        v1 = 0.f;
-        v2 = 0.f;
-        v3 = 0.f;
-    };
-    auto compute = [&](const TileLoad& l) {
-        const uint4* alo = xa + alo_base + __umul24(ckb, alo_stride);
-        const uint4* ahi = xa + ahi_base + __umul24(ckb, ahi_stride);
+    // The tasks.  A round past the thread's last task (the last round of a
+    // span whose block count is not a multiple of 64) computes on a repeated
+    // block and stores nothing; the four lanes of a block agree, so the quad
+    // sums see only their own block.  The loop runs whole groups of
+    // kGemvDepth rounds without a branch; the remaining rounds follow it,
+    // without prefetch.
+    const int kb_step = 64 % nb;
+    int kb = b0 % nb;
+    auto task = [&](int round, QuarterLoad& l, bool prefetch) {
+        const int b = b0 + 64 * round;
+        const uint4* xg = xs + x_group_base(kb, c);
         const uint32_t qw[8] = {l.qa.x, l.qa.y, l.qa.z, l.qa.w, l.qb.x, l.qb.y, l.qb.z, l.qb.w};
-        float4_t dlo = {0.f, 0.f, 0.f, 0.f}, dhi = {0.f, 0.f, 0.f, 0.f};
+        // S1 of sub-blocks 2c (low nibbles, codes q 2^-24) and 2c+1 (high
+        // nibbles, q 2^-20), scaled by 2^-sh like x
+        float s1e = 0.f, s1o = 0.f;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const uint32_t v0 = qw[2 * p], u1 = qw[2 * p + 1];
-            const uint32_t s0 = v0 >> 8, s1 = u1 >> 8;
-            const uint4 blo = make_uint4(v0 & 0x000F000Fu, s0 & 0x000F000Fu,
-                                         u1 & 0x000F000Fu, s1 & 0x000F000Fu);
-            const uint4 bhi = make_uint4(v0 & 0x00F000F0u, s0 & 0x00F000F0u,
-                                         u1 & 0x00F000F0u, s1 & 0x00F000F0u);
-            dlo = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, alo[p]),
-                                                         __builtin_bit_cast(half8_t, blo), dlo,
-                                                         0, 0, 0);
-            dhi = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ahi[p]),
-                                                         __builtin_bit_cast(half8_t, bhi), dhi,
-                                                         0, 0, 0);
+            const uint4 xl = xg[p], xh = xg[4 + p];
+            const uint32_t v = qw[2 * p], u = qw[2 * p + 1];
+            const uint32_t vs = v >> 8, us = u >> 8;
+            s1e = dot2_codes(v & 0x000F000Fu, xl.x, s1e);
+            s1e = dot2_codes(vs & 0x000F000Fu, xl.y, s1e);
+            s1e = dot2_codes(u & 0x000F000Fu, xl.z, s1e);
+            s1e = dot2_codes(us & 0x000F000Fu, xl.w, s1e);
+            s1o = dot2_codes(v & 0x00F000F0u, xh.x, s1o);
+            s1o = dot2_codes(vs & 0x00F000F0u, xh.y, s1o);
+            s1o = dot2_codes(u & 0x00F000F0u, xh.z, s1o);
+            s1o = dot2_codes(us & 0x00F000F0u, xh.w, s1o);
         }
-        // sub-blocks 4 half + i: even ones from the low-nibble instructions
-        // (codes q 2^-24), odd ones from the high-nibble ones (q 2^-20)
-        const float D[4] = {dlo[0], dhi[1], dlo[2], dhi[3]};
+        const float4_t z = zq[kb * 4 + c];   // S0 2c, S0 2c+1, T0 2c, T0 2c+1
+        const int sh = xsh[kb];
         const uint4 h = l.hdr;
         const float d = half_bits_to_float(h.x & 0xFFFFu);
         const float dmin = half_bits_to_float(h.x >> 16);
-        const float dE = d * 0x1p24f, dO = d * 0x1p20f, d15 = fabsf(d) * 15.0f;
-        const uint32_t sc_src = half ? h.w : h.y;
-        const uint32_t m_src = half ? h.w >> 4 : h.z;
-        const uint32_t scb = (sc_src & low_mask) | ((h.y >> 2) & top_mask);
-        const uint32_t mb = (m_src & low_mask) | ((h.z >> 2) & top_mask);
-        const float4_t Z = *reinterpret_cast<const float4_t*>(zs + ckb * 16 + zoff);
-        const float sc[4] = {ubyte_to_float<0>(scb), ubyte_to_float<1>(scb),
-                             ubyte_to_float<2>(scb), ubyte_to_float<3>(scb)};
-        const float mm[4] = {ubyte_to_float<0>(mb), ubyte_to_float<1>(mb),
-                             ubyte_to_float<2>(mb), ubyte_to_float<3>(mb)};
-        float r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ds = ((i & 1) ? dO : dE) * sc[i];
-            const float a = (dmin * mm[i]) * Z[i];
-            r[i] = __builtin_fmaf(ds, D[i], -a);
-        }
-        const float zsc = ((sc[0] * Z[0] + sc[1] * Z[1]) + (sc[2] * Z[2] + sc[3] * Z[3]));
-        const int sh = xsh[ckb];
-        v1 += __builtin_amdgcn_ldexpf((r[0] + r[1]) + (r[2] + r[3]), sh);
-        v2 += __builtin_amdgcn_ldexpf((fabsf(r[0]) + fabsf(r[1])) + (fabsf(r[2]) + fabsf(r[3])),
-                                      sh);
-        v3 += __builtin_amdgcn_ldexpf(d15 * zsc, sh);
-        // next tile of this wave
-        const int kb0 = ckb;
-        ckb += 4;
-        const int g0 = cg;
-        while (ckb >= nb) {
-            ckb -= nb;
-            ++cg;
-        }
-        if (cg != g0) flush(g0, kb0);
+        uint32_t scp, mp;
+        scale_min_pair(static_cast<uint32_t>(c), h.y, h.z, h.w, &scp, &mp);
+        const float sc0 = ubyte_to_float<0>(scp), sc1 = ubyte_to_float<1>(scp);
+        const float m0 = ubyte_to_float<0>(mp), m1 = ubyte_to_float<1>(mp);
+        const float re = __builtin_fmaf((d * 0x1p24f) * sc0, s1e, -((dmin * m0) * z[0]));
+        const float ro = __builtin_fmaf((d * 0x1p20f) * sc1, s1o, -((dmin * m1) * z[1]));
+        const float bq = (15.0f * fabsf(d)) * (sc0 * z[2] + sc1 * z[3]) +
+                         fabsf(dmin) * (m0 * z[2] + m1 * z[3]);
+        const float y = quad_sum(__builtin_amdgcn_ldexpf(re + ro, sh));
+        const float L = quad_sum(__builtin_amdgcn_ldexpf(fabsf(re) + fabsf(ro), sh));
+        const float B = quad_sum(__builtin_amdgcn_ldexpf(bq, sh));
+        // lane c of the block stores sum c (y, L, B; lane 3 none)
+        if (c < 3 && b < nblk_all) part[c * pstride + b] = c == 0 ? y : (c == 1 ? L : B);
+        if (prefetch) l = load_quarter(blk_ptr(round_block(round + kGemvDepth)), c);
+        kb += kb_step;
+        if (kb >= nb) kb -= nb;
     };
-    if (mine > 0) {
-        int i = 0;
-        for (; i + kGemvDepth <= mine; i += kGemvDepth) {
+    int r0 = 0;
+    for (; r0 + kGemvDepth <= nround; r0 += kGemvDepth) {
 #pragma unroll
-            for (int u = 0; u < kGemvDepth; ++u) {
-                compute(ld[u]);
-                issue(ld[u]);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u + 1 < kGemvDepth; ++u)
-            if (i + u < mine) compute(ld[u]);
-        // the last group, unless its last tile ended it (then cg >= Gt and
-        // the group was flushed in compute)
-        if (cg < Gt) flush(cg, ckb);
+        for (int u = 0; u < kGemvDepth; ++u) task(r0 + u, ld[u], true);
     }
+#pragma unroll
+    for (int u = 0; u + 1 < kGemvDepth; ++u)
+        if (r0 + u < nround) task(r0 + u, ld[u], false);
     __syncthreads();
 
-    // Rows: the classes' sums in a fixed order, the certificate, and the list
-    // of rows to recompute (the list's order does not matter: a row's
-    // recomputation is the same whichever wave runs it).
+    // Rows: the blocks' sums in order, the certificate, and the list of rows
+    // to recompute (the list's order does not matter: a row's recomputation
+    // is the same whichever wave runs it).  Row q of the task list (W's rows,
+    // then W2's) owns blocks q nb .. q nb + nb - 1.
     const float kE = (192.0f + static_cast<float>(nb)) * 0x1p-24f;
     for (int q = t; q < kMats * rows; q += kGemvThreads) {
-        const int mat = (kPair && q >= rows) ? 1 : 0;
-        const int qq = q - mat * rows;
-        const float2* pr = part + (mat * G * 16 + qq) * 16;
+        const float* pr = part + q * nb;
         float y = 0.f, L = 0.f, B = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            y += pr[4 * k].x + pr[4 * k + 1].x;
-            L += pr[4 * k].y + pr[4 * k + 1].y;
-            B += pr[4 * k + 2].y + pr[4 * k + 3].y;
+        for (int j = 0; j < nb; ++j) {
+            y += pr[j];
+            L += pr[pstride + j];
+            B += pr[2 * pstride + j];
         }
         const float E = kE * B;
         const float lb = fmaxf(L - 2.0f * E, fabsf(y) - E);
