@@ -122,7 +122,7 @@ int jq4k_gemv(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
  * workgroup (a tuning knob; 0 picks the same value jq4k_gemv uses).  Larger
  * values stage x fewer times, smaller ones spread a small matrix over more
  * compute units.  JQ4K_EINVAL for rows_per_block < 0 or a value whose LDS
- * need exceeds 64 KiB; otherwise the same rules as jq4k_gemv with M = 1. */
+ * need exceeds 96 KiB; otherwise the same rules as jq4k_gemv with M = 1. */
 int jq4k_gemv_rows(const block_q4_K *W, const jq4k_bf16 *X, float *Y,
                    int N, int K, int rows_per_block, hipStream_t stream);
 

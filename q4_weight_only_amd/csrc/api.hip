@@ -68,8 +68,8 @@ constexpr int kGemvSmallRowsPerCu = 64;  // below this many rows per CU: small-m
 // seven projections of a decode layer: 1002 workgroups, all resident at once)
 constexpr int kGemvLargeBlocksPerWg = 480;
 constexpr int kGemvBatchBlocksPerWg = 512;
-// x staged as binary16 with its magnitudes takes 1088 B of LDS per 256
-// values (74 KB at the largest K); rows add 2 KB per group of 16
+// x staged as binary16 with its sums takes 608 B of LDS per 256 values
+// (38 KB at the largest K); each block of W a workgroup owns adds 16 B
 constexpr size_t kGemvLdsLimit = 96 * 1024;
 
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -99,22 +99,41 @@ int check_matmul(const void* W, const void* X, const void* Y, int M, int N, int 
     return 0;
 }
 
-// Rows per workgroup of the GEMV, in whole matrix-core tiles of 16 rows.
-// Matrices of up to kGemvSmallRowsPerCu rows per compute unit take one tile
-// of rows per workgroup (the most workgroups); larger ones about
-// kGemvLargeBlocksPerWg blocks of W per workgroup (measured best on the
-// 151936 x 2560 LM head: 48 rows, against 32, 64 and 128).  Bounded by the
-// LDS budget.
-int gemv_rows_per_block(int N, int K) {
+// Rows per workgroup for about `per_wg` blocks of W of K-long rows (the
+// nearest whole number of rows, at least `min_rows`), within N and the LDS
+// budget.
+int gemv_rows_for(int per_wg, int min_rows, int N, int K, int mats) {
     const int nb = K / jq4k::kQK;
-    const long cus = cu_count();
-    long R = 16;
-    if (N > kGemvSmallRowsPerCu * cus) R = ((kGemvLargeBlocksPerWg / nb + 8) / 16) * 16;
-    if (R < 16) R = 16;
+    long R = (2L * per_wg / nb + 1) / 2;
+    if (R < min_rows) R = min_rows;
+    if (R > N) R = N;
     if (R > kGemvMaxRows) R = kGemvMaxRows;
-    while (R > 16 && jq4k::gemv_lds_bytes(nb, static_cast<int>(R), 1) > kGemvLdsLimit) R -= 16;
+    if (R < 1) R = 1;
+    while (R > 1 && jq4k::gemv_lds_bytes(nb, static_cast<int>(R), mats) > kGemvLdsLimit) --R;
     return static_cast<int>(R);
 }
+
+// Rows per workgroup of the GEMV.  Matrices of up to kGemvSmallRowsPerCu
+// rows per compute unit take 16 rows per workgroup (the most workgroups);
+// larger ones about kGemvLargeBlocksPerWg blocks of W per workgroup (the
+// 151936 x 2560 LM head: 48 rows; 38 to 64, and rows chosen to fill whole
+// rounds of the CUs, measured within noise of it).  Bounded by the LDS
+// budget.
+int gemv_rows_per_block(int N, int K) {
+    const int nb = K / jq4k::kQK;
+    if (N <= kGemvSmallRowsPerCu * static_cast<long>(cu_count())) return gemv_rows_for(16 * nb, 1, N, K, 1);
+    return gemv_rows_for(kGemvLargeBlocksPerWg, 1, N, K, 1);
+}
+
+// Rows per workgroup inside a batched launch: the whole batch fills the GPU,
+// so each workgroup takes about kGemvBatchBlocksPerWg blocks of W whatever
+// the row length, and at least 16 rows (the decode layer: 51 rows at
+// K = 2560, 32 at 4096, 16 at 9728, 745 workgroups, all resident at once:
+// 14.0 us.  Measured slower: 13 rows at K = 9728 (782 workgroups, 17.0 us),
+// 52/33/14 rows (756, 15.5), more blocks for longer rows (55/36/17 to
+// 67/48/29, 15.3-17.1), 384 and 640 blocks, LDS padded to hold at most 3
+// or 4 workgroups per CU (19.5, 15.5)).
+int gemv_batch_rows(int N, int K) { return gemv_rows_for(kGemvBatchBlocksPerWg, 16, N, K, 1); }
 
 int run_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K, int R,
              hipStream_t stream) {
@@ -122,21 +141,6 @@ int run_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K, in
     const hipError_t e = jq4k::launch_gemv(reinterpret_cast<const uint8_t*>(W), X, Y, N, K, R,
                                            stream);
     return static_cast<int>(e);
-}
-
-// Rows per workgroup inside a batched launch: the whole batch fills the GPU,
-// so each workgroup takes about kGemvBatchBlocksPerWg blocks of W whatever
-// the row length, in whole tiles of 16 rows (the decode layer: 48 rows at
-// K = 2560, 32 at 4096, 16 at 9728, 776 workgroups, all resident at once;
-// 384 and 768 blocks measured slower).
-int gemv_batch_rows(int N, int K) {
-    const int nb = K / jq4k::kQK;
-    // whole matrix-core tiles of 16 rows, the nearest multiple to the target
-    int R = (kGemvBatchBlocksPerWg / nb + 8) & ~15;
-    if (R < 16) R = 16;
-    if (R > N) R = N;
-    while (R > 16 && jq4k::gemv_lds_bytes(nb, R, 1) > kGemvLdsLimit) R -= 16;
-    return R;
 }
 
 // MFMA tile (rows of M per workgroup) for the largest M of a launch: 64 up
@@ -371,11 +375,13 @@ int jq4k_gemv_batched(const jq4k_gemv_desc* problems, int count, hipStream_t str
         Y[live] = d.Y;
         N[live] = d.N;
         K[live] = d.K;
-        R[live] = gemv_batch_rows(d.N, d.K);
-        wgs += (static_cast<long>(d.N) + R[live] - 1) / R[live];
         ++live;
     }
     if (live == 0) return JQ4K_OK;
+    for (int i = 0; i < live; ++i) {
+        R[i] = gemv_batch_rows(N[i], K[i]);
+        wgs += (static_cast<long>(N[i]) + R[i] - 1) / R[i];
+    }
     if (wgs > 0x7FFFFFFFL) return JQ4K_EINVAL;
     return static_cast<int>(jq4k::launch_gemv_batched(W, X, Y, N, K, R, live, stream));
 }
@@ -460,13 +466,9 @@ int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16
     const uint8_t* wg = reinterpret_cast<const uint8_t*>(Wg);
     const uint8_t* wu = reinterpret_cast<const uint8_t*>(Wu);
     if (M == 1 && K <= JQ4K_GEMV_MAX_K) {
-        // R rows of each matrix per workgroup, whole tiles of 16: about as
-        // many blocks of the two matrices together as a workgroup of a
-        // grouped launch streams
-        const int nb = K / jq4k::kQK;
-        int R = ((kGemvBatchBlocksPerWg / 2 / nb + 8) / 16) * 16;
-        if (R < 16) R = 16;
-        while (R > 16 && jq4k::gemv_lds_bytes(nb, R, 2) > kGemvLdsLimit) R -= 16;
+        // R rows of each matrix per workgroup: about as many blocks of the
+        // two matrices together as a workgroup of a grouped launch streams
+        const int R = gemv_rows_for(kGemvBatchBlocksPerWg / 2, 8, N, K, 2);
         return static_cast<int>(jq4k::launch_gemv_swiglu(wg, wu, X, H, N, K, R, stream));
     }
     if (K > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;

@@ -23,23 +23,24 @@
 // Work decomposition.  A workgroup owns R consecutive rows, R*nb
 // consecutive blocks of W: one contiguous span of memory (for a gate/up
 // pair, the span of the second matrix follows the first's in the task
-// list).  The span is cut into tasks of one quarter block (the header and
-// the 32 code bytes of sub-blocks 2c and 2c+1: 64 weights); the 256 threads
-// sweep the tasks in rounds, lanes 4j .. 4j+3 of a round taking the four
-// quarters of one block, so every round reads 64 consecutive blocks.  A
-// thread's quarter c = t & 3 never changes; two rounds of loads are in
-// flight per thread.
+// list).  The span is cut into tasks of one half block (the header and the
+// 64 code bytes of sub-blocks 4h .. 4h+3: 128 weights); the 256 threads
+// sweep the tasks in rounds, lanes 2j and 2j+1 of a round taking the two
+// halves of one block, so every round reads 128 consecutive blocks.  A
+// thread's half h = t & 1 never changes; the next round's loads are in
+// flight while a round is computed (one round per thread: 20 registers, and
+// six waves per SIMD; two rounds measured slower at the occupancy they cost).
 //
-// Per quarter, each sub-block gives r = ds S1 - dm S0 (one fma after the
-// exact dm S0 rounding), and the quarter adds r_2c + r_2c+1 (the output),
-// |r_2c| + |r_2c+1| (L: at most sum |w x|) and the error scale
-// B = sum over its sub-blocks of (15 |ds| + |dm|) T0, T0 = sum |x|, which
-// bounds sum (|ds| q + |dm|) |x| and with it every rounding error.  S0 and
-// T0 are staged with x.  The three sums are scaled by 2^sh_kb, added over
-// the block's quarters with two DPP steps (the same bits in all four lanes)
-// and left in LDS per block; each row then adds its nb blocks in order.
-// A row's sums therefore do not depend on R or on the launch: the same bits
-// for every grouping of the rows (no atomics on values).
+// Per half block, each sub-block gives r = ds S1 - dm S0 (one fma after the
+// exact dm S0 rounding), and the half adds its four r (the output), their
+// magnitudes (L: at most sum |w x|) and the error scale B = sum over its
+// sub-blocks of (15 |ds| + |dm|) T0, T0 = sum |x|, which bounds
+// sum (|ds| q + |dm|) |x| and with it every rounding error.  S0 and T0 are
+// staged with x.  The two halves' sums are added with one DPP step (the same
+// bits in both lanes), scaled by 2^sh_kb and left in LDS per block; each row
+// then adds its nb blocks in order.  A row's sums therefore do not depend on
+// R or on the launch: the same bits for every grouping of the rows (no
+// atomics on values).
 //
 // Certificate.  With u = 2^-24, every rounding error of the row is at most
 // E = (192 + nb) u B: the dot2 chains (16 steps of two exact products per
@@ -56,42 +57,44 @@
 //
 // LDS layout of the staged x.  Chunk g holds the binary16 x[8g .. 8g+7] in
 // the order 0, 2, 1, 3, 4, 6, 5, 7 (the order of the codes as masked from
-// two consecutive code dwords: bytes 0, 2, 1, 3 of each).  The 8 chunks a
-// quarter task reads (g = 32 kb + 8 c + i: i = 0..3 sub-block 2c, 4..7
-// sub-block 2c+1) sit at 9 (4 kb + c) + i.  The 64 lanes of a round read
-// one chunk index i of 64 consecutive groups, and the stride of 9 spreads
-// them over the banks without conflicts; a thread's 8 reads are one base
-// address plus immediate offsets.
+// two consecutive code dwords: bytes 0, 2, 1, 3 of each).  The 16 chunks a
+// half-block task reads (g = 32 kb + 16 h + i: sub-block 4h + i / 4) sit at
+// 19 (2 kb + h) + i, followed by two chunks of that half's S0 and T0.  The
+// lanes of a round read one chunk index i of consecutive groups, and the odd
+// stride of 19 spreads them over the banks without conflicts; a thread's
+// reads are one base address plus immediate offsets.
 #include "q4k_device.h"
 
 namespace jq4k {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvBatchMax = 16;  // problems per batched launch
-constexpr int kGemvDepth = 2;      // rounds of quarter loads in flight per thread
+constexpr int kGemvDepth = 1;      // rounds of half-block loads in flight per thread
 constexpr int kGemvMaxK = 16384;
 constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
-constexpr int kXGroupStride = 9;   // LDS chunk stride of a quarter's 8 chunks of x
+constexpr int kXGroupStride = 19;  // LDS chunks per (block, half): 16 of x, S0, T0, one spare
+constexpr int kRoundBlocks = kGemvThreads / 2;   // blocks per round
 
 typedef __attribute__((ext_vector_type(4))) float float4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 
 __host__ __device__ constexpr int gemv_shift_words(int nb) { return (nb + 3) & ~3; }
-__device__ __forceinline__ int x_group_base(int kb, int c) { return (4 * kb + c) * kXGroupStride; }
-__device__ __forceinline__ int x_chunk_phys(int g) { return (g >> 3) * kXGroupStride + (g & 7); }
+__device__ __forceinline__ int x_group_base(int kb, int h) { return (2 * kb + h) * kXGroupStride; }
+__device__ __forceinline__ int x_chunk_phys(int g) { return (g >> 4) * kXGroupStride + (g & 15); }
 
 // LDS of a workgroup with R rows of each of `mats` matrices (bytes):
-//   staged x              nb * 36 chunks of 16 B
-//   S0, T0                per (block, quarter) a float4 {S0 2c, S0 2c+1, T0 2c, T0 2c+1}
+//   staged x              nb * 2 groups of 19 chunks of 16 B: 16 chunks of x,
+//                         then S0 and T0 of the half's four sub-blocks
 //   sh                    per block, one int (padded to 16 B)
-//   block partials        3 x mats * R * nb floats (the sums y, L, B of each block)
+//   block partials        mats * R * nb + 1 float4 {y, L, B, -} (the last slot
+//                         takes the stores of lanes past the last block)
 //   row results           mats * R floats
 //   recompute list        1 + mats * R ints (count, then rows)
 __host__ __device__ constexpr size_t gemv_lds_layout(int nb, int R, int mats) {
-    return static_cast<size_t>(nb) * 4 * kXGroupStride * 16 + static_cast<size_t>(nb) * 64 +
+    return static_cast<size_t>(nb) * 2 * kXGroupStride * 16 +
            static_cast<size_t>(gemv_shift_words(nb)) * 4 +
-           3 * static_cast<size_t>(mats) * R * nb * 4 + static_cast<size_t>(mats) * R * 4 +
+           (static_cast<size_t>(mats) * R * nb + 1) * 16 + static_cast<size_t>(mats) * R * 4 +
            (1 + static_cast<size_t>(mats) * R) * 4;
 }
 
@@ -122,6 +125,13 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v;
 }
 
+// Sum over the two lanes of a pair, the same bits in both (fp32 addition
+// commutes).
+__device__ __forceinline__ float pair_sum(float v) {
+    const int i = __builtin_bit_cast(int, v);
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(i, i, 0xB1, 0xF, 0xF, true));
+}
+
 // The scale exponent of a block of x whose largest exponent field is e:
 // x * 2^-sh stays below 2^15 in magnitude (binary16 overflows at 65520),
 // and 2^-sh is a normal fp32 (sh in [-126, 114]; e = 255 is Inf or NaN).
@@ -137,16 +147,36 @@ __device__ __forceinline__ float dot2_codes(uint32_t codes, uint32_t x, float ac
                                   __builtin_bit_cast(half2_t, x), acc, false);
 }
 
-struct QuarterLoad {
-    uint4 hdr, qa, qb;   // header; code dwords 0..3 and 4..7 of the quarter
+struct HalfLoad {
+    uint4 hdr;     // d, dmin, scales
+    uint4 q[4];    // code bytes 64 h .. 64 h + 63: quarters 2h and 2h+1
 };
 
-__device__ __forceinline__ QuarterLoad load_quarter(const uint8_t* blk, int c) {
-    QuarterLoad r;
+__device__ __forceinline__ HalfLoad load_half(const uint8_t* blk, int h) {
+    HalfLoad r;
     r.hdr = load16(blk);
-    r.qa = load16(blk + 16 + 32 * c);
-    r.qb = load16(blk + 32 + 32 * c);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.q[k] = load16(blk + 16 + 64 * h + 16 * k);
     return r;
+}
+
+// S1 of one sub-block (32 weights) from its 8 code dwords' nibbles (low
+// nibbles: mask 0x000F000F, codes q 2^-24; high: 0x00F000F0, q 2^-20) and
+// its 4 chunks of staged x.
+template <uint32_t kMask>
+__device__ __forceinline__ float sub_block_sum(const uint4& qa, const uint4& qb, const uint4* xc) {
+    const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint4 x = xc[p];
+        const uint32_t v = qw[2 * p], u = qw[2 * p + 1];
+        acc = dot2_codes(v & kMask, x.x, acc);
+        acc = dot2_codes((v >> 8) & kMask, x.y, acc);
+        acc = dot2_codes(u & kMask, x.z, acc);
+        acc = dot2_codes((u >> 8) & kMask, x.w, acc);
+    }
+    return acc;
 }
 
 // One row recomputed by one wave, lane l taking sub-block l / 8, weights
@@ -216,28 +246,32 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int c = t & 3;
+    const int h = t & 1;
     const long row0 = tile * R;
     const int rows = static_cast<int>(min(static_cast<long>(R), N - row0));
     const int nblk = rows * nb;                 // blocks per matrix here
     const int nblk_all = kMats * nblk;
-    const int pstride = kMats * R * nb;         // one of the three partial arrays
 
     uint4* xs = smem;
-    float4_t* zq = reinterpret_cast<float4_t*>(xs + nb * 4 * kXGroupStride);
-    int* xsh = reinterpret_cast<int*>(zq + nb * 4);
-    float* part = reinterpret_cast<float*>(xsh + gemv_shift_words(nb));
-    float* yrow = part + 3 * pstride;
+    int* xsh = reinterpret_cast<int*>(xs + nb * 2 * kXGroupStride);
+    float4_t* part = reinterpret_cast<float4_t*>(xsh + gemv_shift_words(nb));
+    const int spare = kMats * R * nb;           // the partials' spare slot
+    float* yrow = reinterpret_cast<float*>(part + spare + 1);
     int* flist = reinterpret_cast<int*>(yrow + kMats * R);
 
     const uint8_t* Wt = W + row0 * nb * kBlockBytes;
     const uint8_t* Wt2 = kPair ? W2 + row0 * nb * kBlockBytes : nullptr;
-    // block b of the task list: W's span, then (kPair) W2's
+    // block b of the task list: W's span, then (kPair) W2's (a single
+    // matrix: a 32-bit offset from the workgroup's base)
     auto blk_ptr = [&](int b) {
-        if (kPair && b >= nblk) return Wt2 + static_cast<long>(b - nblk) * kBlockBytes;
-        return Wt + static_cast<long>(b) * kBlockBytes;
+        if constexpr (kPair) {
+            if (b >= nblk) return Wt2 + static_cast<long>(b - nblk) * kBlockBytes;
+            return Wt + static_cast<long>(b) * kBlockBytes;
+        } else {
+            return Wt + static_cast<uint32_t>(b) * static_cast<uint32_t>(kBlockBytes);
+        }
     };
-    const int b0 = t >> 2;  // this thread's first block; +64 per round
+    const int b0 = t >> 1;  // this thread's first block; + kRoundBlocks per round
 
     // Memory requests in the order they are needed (vmcnt retires in order):
     // x first, then the first kGemvDepth rounds of weights, so that staging
@@ -247,8 +281,8 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     // flight turns pessimistic at the joins and it waits for all of them,
     // which undoes the prefetch.
     const int nxc = nb * 32;  // 16-byte chunks of x, at most 2048 (K <= 16384)
-    const int nround = (nblk_all + 63) >> 6;   // the same for every thread
-    auto round_block = [&](int round) { return min(b0 + 64 * round, nblk_all - 1); };
+    const int nround = (nblk_all + kRoundBlocks - 1) / kRoundBlocks;   // the same for every thread
+    auto round_block = [&](int round) { return min(b0 + kRoundBlocks * round, nblk_all - 1); };
     uint4 xv[kGemvMaxXChunksPerThread];
     uint4 gv[kNorm ? kGemvMaxXChunksPerThread : 1];
 #pragma unroll
@@ -260,9 +294,9 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
             if constexpr (kNorm) gv[q] = gamma[g];
         }
     }
-    QuarterLoad ld[kGemvDepth];
+    HalfLoad ld[kGemvDepth];
 #pragma unroll
-    for (int u = 0; u < kGemvDepth; ++u) ld[u] = load_quarter(blk_ptr(round_block(u)), c);
+    for (int u = 0; u < kGemvDepth; ++u) ld[u] = load_half(blk_ptr(round_block(u)), h);
 
     if (t == 0) flist[0] = 0;
 
@@ -360,11 +394,12 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
                 inexact |= bad;
                 xs[x_chunk_phys(g)] = make_uint4(h0, h1, h2, h3);
                 if ((g & 3) == 0) {
-                    // sub-block s = 2 (s / 2) + (s & 1): quarter s / 2, slot s & 1
+                    // sub-block s: slot s % 4 of the S0 and T0 chunks of
+                    // group (block, half s / 4)
+                    float* z = reinterpret_cast<float*>(xs + x_chunk_phys(g | 15) + 1);
                     const int s = (g >> 2) & 7;
-                    float* z = reinterpret_cast<float*>(zq + (g >> 5) * 4 + (s >> 1));
-                    z[s & 1] = s0;
-                    z[2 + (s & 1)] = t0;
+                    z[s & 3] = s0;
+                    z[4 + (s & 3)] = t0;
                 }
                 if ((g & 31) == 0) xsh[g >> 5] = sh;
             }
@@ -373,55 +408,68 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     const bool x_inexact = __syncthreads_or(inexact) != 0;
 
     // The tasks.  A round past the thread's last task (the last round of a
-    // span whose block count is not a multiple of 64) computes on a repeated
-    // block and stores nothing; the four lanes of a block agree, so the quad
-    // sums see only their own block.  The loop runs whole groups of
-    // kGemvDepth rounds without a branch; the remaining rounds follow it,
-    // without prefetch.
-    const int kb_step = 64 % nb;
+    // span whose block count is not a multiple of kRoundBlocks) computes on
+    // a repeated block and stores into the spare slot; the two lanes of a
+    // block agree, so the pair sums see only their own block.  The loop runs
+    // whole groups of kGemvDepth rounds without a branch; the remaining
+    // rounds follow it, without prefetch.
+    const int kb_step = kRoundBlocks % nb;
     int kb = b0 % nb;
-    auto task = [&](int round, QuarterLoad& l, bool prefetch) {
-        const int b = b0 + 64 * round;
-        const uint4* xg = xs + x_group_base(kb, c);
-        const uint32_t qw[8] = {l.qa.x, l.qa.y, l.qa.z, l.qa.w, l.qb.x, l.qb.y, l.qb.z, l.qb.w};
-        // S1 of sub-blocks 2c (low nibbles, codes q 2^-24) and 2c+1 (high
-        // nibbles, q 2^-20), scaled by 2^-sh like x
-        float s1e = 0.f, s1o = 0.f;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint4 xl = xg[p], xh = xg[4 + p];
-            const uint32_t v = qw[2 * p], u = qw[2 * p + 1];
-            const uint32_t vs = v >> 8, us = u >> 8;
-            s1e = dot2_codes(v & 0x000F000Fu, xl.x, s1e);
-            s1e = dot2_codes(vs & 0x000F000Fu, xl.y, s1e);
-            s1e = dot2_codes(u & 0x000F000Fu, xl.z, s1e);
-            s1e = dot2_codes(us & 0x000F000Fu, xl.w, s1e);
-            s1o = dot2_codes(v & 0x00F000F0u, xh.x, s1o);
-            s1o = dot2_codes(vs & 0x00F000F0u, xh.y, s1o);
-            s1o = dot2_codes(u & 0x00F000F0u, xh.z, s1o);
-            s1o = dot2_codes(us & 0x00F000F0u, xh.w, s1o);
-        }
-        const float4_t z = zq[kb * 4 + c];   // S0 2c, S0 2c+1, T0 2c, T0 2c+1
+    int gq = x_group_base(kb, h);   // the LDS chunk of group (kb, h)
+    // scale bytes of sub-blocks 4h + 0..3 (Q4_K packing): half 0 the low six
+    // bits of scales[j] and scales[4+j]; half 1 the nibbles of scales[8+j]
+    // plus bits 6..7 of scales[j] and scales[4+j] as bits 4..5
+    const uint32_t low_mask = h ? 0x0F0F0F0Fu : 0x3F3F3F3Fu;
+    const uint32_t top_mask = h ? 0x30303030u : 0u;
+    auto task = [&](int round, HalfLoad& l, bool prefetch) {
+        const int b = b0 + kRoundBlocks * round;
+        const uint4* xg = xs + gq;
+        // S1 of sub-blocks 4h + j, scaled by 2^-sh like x: even j from the
+        // low nibbles of quarter 2h + j / 2, odd j from its high nibbles
+        float s1[4];
+        s1[0] = sub_block_sum<0x000F000Fu>(l.q[0], l.q[1], xg);
+        s1[1] = sub_block_sum<0x00F000F0u>(l.q[0], l.q[1], xg + 4);
+        s1[2] = sub_block_sum<0x000F000Fu>(l.q[2], l.q[3], xg + 8);
+        s1[3] = sub_block_sum<0x00F000F0u>(l.q[2], l.q[3], xg + 12);
+        const float4_t S0 = *reinterpret_cast<const float4_t*>(xg + 16);
+        const float4_t T0 = *reinterpret_cast<const float4_t*>(xg + 17);
         const int sh = xsh[kb];
-        const uint4 h = l.hdr;
-        const float d = half_bits_to_float(h.x & 0xFFFFu);
-        const float dmin = half_bits_to_float(h.x >> 16);
-        uint32_t scp, mp;
-        scale_min_pair(static_cast<uint32_t>(c), h.y, h.z, h.w, &scp, &mp);
-        const float sc0 = ubyte_to_float<0>(scp), sc1 = ubyte_to_float<1>(scp);
-        const float m0 = ubyte_to_float<0>(mp), m1 = ubyte_to_float<1>(mp);
-        const float re = __builtin_fmaf((d * 0x1p24f) * sc0, s1e, -((dmin * m0) * z[0]));
-        const float ro = __builtin_fmaf((d * 0x1p20f) * sc1, s1o, -((dmin * m1) * z[1]));
-        const float bq = (15.0f * fabsf(d)) * (sc0 * z[2] + sc1 * z[3]) +
-                         fabsf(dmin) * (m0 * z[2] + m1 * z[3]);
-        const float y = quad_sum(__builtin_amdgcn_ldexpf(re + ro, sh));
-        const float L = quad_sum(__builtin_amdgcn_ldexpf(fabsf(re) + fabsf(ro), sh));
-        const float B = quad_sum(__builtin_amdgcn_ldexpf(bq, sh));
-        // lane c of the block stores sum c (y, L, B; lane 3 none)
-        if (c < 3 && b < nblk_all) part[c * pstride + b] = c == 0 ? y : (c == 1 ? L : B);
-        if (prefetch) l = load_quarter(blk_ptr(round_block(round + kGemvDepth)), c);
+        const uint4 hd = l.hdr;
+        const float d = half_bits_to_float(hd.x & 0xFFFFu);
+        const float dmin = half_bits_to_float(hd.x >> 16);
+        const uint32_t sc_src = h ? hd.w : hd.y;
+        const uint32_t m_src = h ? hd.w >> 4 : hd.z;
+        const uint32_t scb = (sc_src & low_mask) | ((hd.y >> 2) & top_mask);
+        const uint32_t mb = (m_src & low_mask) | ((hd.z >> 2) & top_mask);
+        const float sc[4] = {ubyte_to_float<0>(scb), ubyte_to_float<1>(scb),
+                             ubyte_to_float<2>(scb), ubyte_to_float<3>(scb)};
+        const float mm[4] = {ubyte_to_float<0>(mb), ubyte_to_float<1>(mb),
+                             ubyte_to_float<2>(mb), ubyte_to_float<3>(mb)};
+        const float dE = d * 0x1p24f, dO = d * 0x1p20f;
+        float r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            r[j] = __builtin_fmaf(((j & 1) ? dO : dE) * sc[j], s1[j], -((dmin * mm[j]) * S0[j]));
+        const float bq = (15.0f * fabsf(d)) * ((sc[0] * T0[0] + sc[1] * T0[1]) +
+                                               (sc[2] * T0[2] + sc[3] * T0[3])) +
+                         fabsf(dmin) * ((mm[0] * T0[0] + mm[1] * T0[1]) +
+                                        (mm[2] * T0[2] + mm[3] * T0[3]));
+        // the block's sums (the two halves added, the same bits in both
+        // lanes), scaled by 2^sh; half 0 stores {y, L}, half 1 B
+        const float y = pair_sum((r[0] + r[1]) + (r[2] + r[3]));
+        const float L = pair_sum((fabsf(r[0]) + fabsf(r[1])) + (fabsf(r[2]) + fabsf(r[3])));
+        const float B = pair_sum(bq);
+        const int slot = b < nblk_all ? b : spare;
+        float2* dst = reinterpret_cast<float2*>(part + slot) + h;
+        *dst = h ? make_float2(__builtin_amdgcn_ldexpf(B, sh), 0.f)
+                 : make_float2(__builtin_amdgcn_ldexpf(y, sh), __builtin_amdgcn_ldexpf(L, sh));
+        if (prefetch) l = load_half(blk_ptr(round_block(round + kGemvDepth)), h);
         kb += kb_step;
-        if (kb >= nb) kb -= nb;
+        gq += kb_step * 2 * kXGroupStride;
+        if (kb >= nb) {
+            kb -= nb;
+            gq -= nb * 2 * kXGroupStride;
+        }
     };
     int r0 = 0;
     for (; r0 + kGemvDepth <= nround; r0 += kGemvDepth) {
@@ -439,12 +487,13 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     // then W2's) owns blocks q nb .. q nb + nb - 1.
     const float kE = (192.0f + static_cast<float>(nb)) * 0x1p-24f;
     for (int q = t; q < kMats * rows; q += kGemvThreads) {
-        const float* pr = part + q * nb;
+        const float4_t* pr = part + q * nb;
         float y = 0.f, L = 0.f, B = 0.f;
         for (int j = 0; j < nb; ++j) {
-            y += pr[j];
-            L += pr[pstride + j];
-            B += pr[2 * pstride + j];
+            const float4_t v = pr[j];
+            y += v[0];
+            L += v[1];
+            B += v[2];
         }
         const float E = kE * B;
         const float lb = fmaxf(L - 2.0f * E, fabsf(y) - E);
@@ -453,7 +502,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     }
     __syncthreads();
     const int nredo = flist[0];
-    for (int e = wave; e < nredo; e += 4) {
+    for (int e = wave; e < nredo; e += kGemvThreads / 64) {
         const int q = flist[1 + e];
         const int mat = (kPair && q >= rows) ? 1 : 0;
         const int qq = q - mat * rows;
