@@ -907,7 +907,7 @@ def main():
             "rotation_copies": dec["rotation_copies"],
             "launch": "eager" if args.eager else "hip-graph",
             "arithmetic": "bf16 activations staged as binary16 (exact), 4-bit codes as "
-                          "binary16 on the matrix cores, fp32 sums, per-row certified bound",
+                          "binary16 in v_dot2_f32_f16, fp32 sums, per-row certified bound",
             "device": torch.cuda.get_device_name(0),
         },
         "roofline": dec["roofline"],

@@ -42,9 +42,9 @@
  *   zero against large scales, e.g. d*sc*q = dmin*m) is recomputed in the
  *   same launch from the fp32 weights with fp64 sums, as are all rows when
  *   an activation is not exact in its staged binary16 (a value below 2^-31
- *   of its block's largest magnitude, Inf, NaN).  The bound assumes the
- *   matrix cores add exact binary16 products in fp32 with at most 2^-23
- *   relative error per addition.  Rows of randomly drawn Q4_K blocks
+ *   of its block's largest magnitude, Inf, NaN).  The bound assumes each
+ *   dot-product step adds its two exact binary16 products to the fp32 sum
+ *   with at most two roundings.  Rows of randomly drawn Q4_K blocks
  *   certify with a margin of about 8 and are never recomputed.
  *   M > 1: the matrix-core kernels contract bfloat16 tiles of w
  *   (round-to-nearest-even of the fp32 weight, exactly what
