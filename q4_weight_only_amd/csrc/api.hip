@@ -113,21 +113,43 @@ int gemv_rows_for(int per_wg, int min_rows, int N, int K, int mats) {
     return static_cast<int>(R);
 }
 
+// Rows spreading `blocks` blocks of W (`problems` problems, `mats` matrices
+// per row) over about one workgroup per CU: for launches whose usual rows
+// leave CUs idle.  A small launch is latency-bound, and every CU streaming
+// part of it beats fewer, longer workgroups (the 2560 x 2560 GEMV: 4.9 ->
+// 4.2 us with 11 rows instead of 16; a decode step of four dependent
+// grouped launches: 33.4 -> 29.8 us; two to four workgroups per CU
+// measured slower).
+int gemv_spread_rows(long blocks, int problems, int N, int K, int mats) {
+    const int nb = K / jq4k::kQK;
+    const long slots = static_cast<long>(cu_count()) - problems;
+    const long per_wg = slots > 0 ? (blocks + slots - 1) / slots : blocks;
+    long R = (per_wg + static_cast<long>(mats) * nb - 1) / (static_cast<long>(mats) * nb);
+    if (R < 1) R = 1;
+    if (R > N) R = N;
+    while (R > 1 && jq4k::gemv_lds_bytes(nb, static_cast<int>(R), mats) > kGemvLdsLimit) --R;
+    return static_cast<int>(R);
+}
+
 // Rows per workgroup of the GEMV.  Matrices of up to kGemvSmallRowsPerCu
-// rows per compute unit take 16 rows per workgroup (the most workgroups);
+// rows per compute unit take 16 rows per workgroup, or fewer where that
+// leaves CUs idle (gemv_spread_rows);
 // larger ones about kGemvLargeBlocksPerWg blocks of W per workgroup (the
 // 151936 x 2560 LM head: 48 rows; 38 to 64, and rows chosen to fill whole
 // rounds of the CUs, measured within noise of it).  Bounded by the LDS
 // budget.
 int gemv_rows_per_block(int N, int K) {
     const int nb = K / jq4k::kQK;
-    if (N <= kGemvSmallRowsPerCu * static_cast<long>(cu_count())) return gemv_rows_for(16 * nb, 1, N, K, 1);
+    if (N <= kGemvSmallRowsPerCu * static_cast<long>(cu_count())) {
+        if ((N + 15) / 16 < cu_count()) return gemv_spread_rows(static_cast<long>(N) * nb, 1, N, K, 1);
+        return gemv_rows_for(16 * nb, 1, N, K, 1);
+    }
     return gemv_rows_for(kGemvLargeBlocksPerWg, 1, N, K, 1);
 }
 
-// Rows per workgroup inside a batched launch: the whole batch fills the GPU,
-// so each workgroup takes about kGemvBatchBlocksPerWg blocks of W whatever
-// the row length, and at least 16 rows (the decode layer: 51 rows at
+// Rows per workgroup inside a batched launch: a batch that fills the GPU
+// takes about kGemvBatchBlocksPerWg blocks of W per workgroup whatever the
+// row length, and at least 16 rows (a smaller one is spread over the CUs) (the decode layer: 51 rows at
 // K = 2560, 32 at 4096, 16 at 9728, 745 workgroups, all resident at once:
 // 14.0 us.  Measured slower: 13 rows at K = 9728 (782 workgroups, 17.0 us),
 // 52/33/14 rows (756, 15.5), more blocks for longer rows (55/36/17 to
@@ -382,6 +404,15 @@ int jq4k_gemv_batched(const jq4k_gemv_desc* problems, int count, hipStream_t str
         R[i] = gemv_batch_rows(N[i], K[i]);
         wgs += (static_cast<long>(N[i]) + R[i] - 1) / R[i];
     }
+    if (wgs < cu_count()) {
+        long blocks = 0;
+        for (int i = 0; i < live; ++i) blocks += static_cast<long>(N[i]) * (K[i] / jq4k::kQK);
+        wgs = 0;
+        for (int i = 0; i < live; ++i) {
+            R[i] = gemv_spread_rows(blocks, live, N[i], K[i], 1);
+            wgs += (static_cast<long>(N[i]) + R[i] - 1) / R[i];
+        }
+    }
     if (wgs > 0x7FFFFFFFL) return JQ4K_EINVAL;
     return static_cast<int>(jq4k::launch_gemv_batched(W, X, Y, N, K, R, live, stream));
 }
@@ -468,7 +499,9 @@ int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16
     if (M == 1 && K <= JQ4K_GEMV_MAX_K) {
         // R rows of each matrix per workgroup: about as many blocks of the
         // two matrices together as a workgroup of a grouped launch streams
-        const int R = gemv_rows_for(kGemvBatchBlocksPerWg / 2, 8, N, K, 2);
+        int R = gemv_rows_for(kGemvBatchBlocksPerWg / 2, 8, N, K, 2);
+        if ((N + R - 1) / R < cu_count())
+            R = gemv_spread_rows(2L * N * (K / jq4k::kQK), 1, N, K, 2);
         return static_cast<int>(jq4k::launch_gemv_swiglu(wg, wu, X, H, N, K, R, stream));
     }
     if (K > JQ4K_MFMA_MAX_K) return JQ4K_EINVAL;
