@@ -69,7 +69,6 @@ namespace jq4k {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvBatchMax = 16;  // problems per batched launch
-constexpr int kGemvDepth = 1;      // rounds of half-block loads in flight per thread
 constexpr int kGemvMaxK = 16384;
 constexpr int kGemvMaxXChunksPerThread = kGemvMaxK / 8 / kGemvThreads;
 constexpr int kXGroupStride = 19;  // LDS chunks per (block, half): 16 of x, S0, T0, one spare
@@ -274,8 +273,8 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     const int b0 = t >> 1;  // this thread's first block; + kRoundBlocks per round
 
     // Memory requests in the order they are needed (vmcnt retires in order):
-    // x first, then the first kGemvDepth rounds of weights, so that staging
-    // x waits only for x and each round waits only for its own weights.
+    // x first, then the first round of weights, so that staging x waits only
+    // for x and each round waits only for its own weights.
     // Every load is unconditional, past the end a repeat of the last chunk
     // or block: with loads under branches the compiler's count of loads in
     // flight turns pessimistic at the joins and it waits for all of them,
@@ -294,9 +293,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
             if constexpr (kNorm) gv[q] = gamma[g];
         }
     }
-    HalfLoad ld[kGemvDepth];
-#pragma unroll
-    for (int u = 0; u < kGemvDepth; ++u) ld[u] = load_half(blk_ptr(round_block(u)), h);
+    HalfLoad la = load_half(blk_ptr(round_block(0)), h);
 
     if (t == 0) flist[0] = 0;
 
@@ -410,9 +407,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     // The tasks.  A round past the thread's last task (the last round of a
     // span whose block count is not a multiple of kRoundBlocks) computes on
     // a repeated block and stores into the spare slot; the two lanes of a
-    // block agree, so the pair sums see only their own block.  The loop runs
-    // whole groups of kGemvDepth rounds without a branch; the remaining
-    // rounds follow it, without prefetch.
+    // block agree, so the pair sums see only their own block.
     const int kb_step = kRoundBlocks % nb;
     int kb = b0 % nb;
     int gq = x_group_base(kb, h);   // the LDS chunk of group (kb, h)
@@ -421,7 +416,7 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
     // plus bits 6..7 of scales[j] and scales[4+j] as bits 4..5
     const uint32_t low_mask = h ? 0x0F0F0F0Fu : 0x3F3F3F3Fu;
     const uint32_t top_mask = h ? 0x30303030u : 0u;
-    auto task = [&](int round, HalfLoad& l, bool prefetch) {
+    auto task = [&](int round, const HalfLoad& l) {
         const int b = b0 + kRoundBlocks * round;
         const uint4* xg = xs + gq;
         // S1 of sub-blocks 4h + j, scaled by 2^-sh like x: even j from the
@@ -463,7 +458,6 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
         float2* dst = reinterpret_cast<float2*>(part + slot) + h;
         *dst = h ? make_float2(__builtin_amdgcn_ldexpf(B, sh), 0.f)
                  : make_float2(__builtin_amdgcn_ldexpf(y, sh), __builtin_amdgcn_ldexpf(L, sh));
-        if (prefetch) l = load_half(blk_ptr(round_block(round + kGemvDepth)), h);
         kb += kb_step;
         gq += kb_step * 2 * kXGroupStride;
         if (kb >= nb) {
@@ -471,14 +465,21 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ W,
             gq -= nb * 2 * kXGroupStride;
         }
     };
+    // Two register sets take the rounds in turn: the next round's loads go
+    // into one while the other is computed (one round in flight), and no
+    // set is copied into the other.  A set is reloaded only after its round
+    // is computed (the scheduling barrier keeps the load there; moved above
+    // the round it would need a third set).  The last round's reload asks
+    // for a repeated block.
     int r0 = 0;
-    for (; r0 + kGemvDepth <= nround; r0 += kGemvDepth) {
-#pragma unroll
-        for (int u = 0; u < kGemvDepth; ++u) task(r0 + u, ld[u], true);
+    for (; r0 + 2 <= nround; r0 += 2) {
+        const HalfLoad lb = load_half(blk_ptr(round_block(r0 + 1)), h);
+        task(r0, la);
+        __builtin_amdgcn_sched_barrier(0);
+        la = load_half(blk_ptr(round_block(r0 + 2)), h);
+        task(r0 + 1, lb);
     }
-#pragma unroll
-    for (int u = 0; u + 1 < kGemvDepth; ++u)
-        if (r0 + u < nround) task(r0 + u, ld[u], false);
+    if (r0 < nround) task(r0, la);
     __syncthreads();
 
     // Rows: the blocks' sums in order, the certificate, and the list of rows
