@@ -28,8 +28,9 @@
 // sweep the tasks in rounds, lanes 2j and 2j+1 of a round taking the two
 // halves of one block, so every round reads 128 consecutive blocks.  A
 // thread's half h = t & 1 never changes; the next round's loads are in
-// flight while a round is computed (one round per thread: 20 registers, and
-// six waves per SIMD; two rounds measured slower at the occupancy they cost).
+// flight while a round is computed (two sets of 20 registers take the
+// rounds in turn: 79 VGPRs, six waves per SIMD; two rounds in flight, or
+// three for small launches, measured slower).
 //
 // Per half block, each sub-block gives r = ds S1 - dm S0 (one fma after the
 // exact dm S0 rounding), and the half adds its four r (the output), their
