@@ -325,6 +325,31 @@ def test_gemv_batched_decode_layer(gpu):
         assert np.array_equal(host(y).view(np.uint32), host(Yb[i]).view(np.uint32)), probs[i][0]
 
 
+def test_gemv_batched_decode_step_groups(gpu):
+    """The four dependent launches of a decode step (q|k|v, o, gate|up, down),
+    each its own batched launch.  The smaller ones give fewer workgroups than
+    CUs at the batch's usual rows and are spread over every CU with fewer
+    rows per workgroup; every output still equals the per-problem GEMV bit
+    for bit (a row's sums do not depend on the rows per workgroup) and meets
+    the oracle bound."""
+    layer = qi.decode_layer(1, 0, 1)
+    for group in ((0, 1, 2), (3,), (4, 5), (6,)):
+        probs = [layer[i] for i in group]
+        Wd = [dev(W) for _, N, K, W, _ in probs]
+        Xd = [dev(X).view(torch.bfloat16) for *_, X in probs]
+        Yb = [torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda:0")
+              for _, N, *_ in probs]
+        announce(f"gemv batched decode-step group {[p[0] for p in probs]}")
+        gpu.gemv_batched(list(zip(Wd, Xd, Yb)))
+        for (name, N, K, W, X), wd, xd, yb in zip(probs, Wd, Xd, Yb):
+            ys = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+            gpu.gemv(wd, xd, ys)
+            got, single = host(yb), host(ys)
+            assert np.array_equal(got.view(np.uint32), single.view(np.uint32)), name
+            Y, A = oracle.gemm(W, X, N, K)
+            parity(got, Y, A, f"decode-step group {name}")
+
+
 # ------------------------------------------------------------ M > 1 (MFMA)
 
 PATHS = ["mfma64", "mfma128", "mfma256", "mfma_big", "mfma_rw", "skinny"]
