@@ -8,6 +8,13 @@
 // step is one IEEE operation (correctly rounded division and product), so the
 // codes, scales and fp16 values are fixed bit for bit.
 //
+// The codes without a division per value.  With y = 1/s correctly rounded
+// (one division per lane), q0 = v*y rounded, the residual r = v - q0*s (one
+// fma) and q1 = q0 + r*y (one fma), rint(q1) equals rint(v / s) for every
+// binary16 v and every binary16 max|v| >= |v| (an exhaustive check over all
+// such pairs, run by the tests on the CPU).  A vector whose scale is zero or
+// infinite takes the division.
+//
 // Both directions stream: 3 + 4/dim bytes per value.  A vector is handled by
 // G lanes (G = the power of two >= dim / 8, at most 64): lane j of the group
 // owns values 8j .. 8j + 7 (one 16-byte fp16 load, one 8-byte code store),
@@ -48,10 +55,19 @@ __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(const uint16_t* __
     for (int o = G / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, G));
     if (!live) return;
     const float s = amax / 127.0f;
+    const float y = 1.0f / s;
+    const bool finite = s != 0.0f && s < __builtin_inff();
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float c = s != 0.0f ? rintf(x[i] / s) : 0.0f;
+        float c;
+        if (finite) {
+            const float q0 = __fmul_rn(x[i], y);
+            const float r = __builtin_fmaf(-q0, s, x[i]);
+            c = rintf(__builtin_fmaf(r, y, q0));
+        } else {
+            c = s != 0.0f ? rintf(x[i] / s) : 0.0f;
+        }
         c = fminf(fmaxf(c, -127.0f), 127.0f);
         const uint32_t b = static_cast<uint32_t>(static_cast<int>(c)) & 0xFFu;
         packed[i >> 2] |= b << (8 * (i & 3));
