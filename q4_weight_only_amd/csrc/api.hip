@@ -133,11 +133,10 @@ int gemv_spread_rows(long blocks, int problems, int N, int K, int mats) {
 
 // Rows per workgroup of the GEMV.  Matrices of up to kGemvSmallRowsPerCu
 // rows per compute unit take 16 rows per workgroup, or fewer where that
-// leaves CUs idle (gemv_spread_rows);
-// larger ones about kGemvLargeBlocksPerWg blocks of W per workgroup (the
-// 151936 x 2560 LM head: 48 rows; 38 to 64, and rows chosen to fill whole
-// rounds of the CUs, measured within noise of it).  Bounded by the LDS
-// budget.
+// leaves CUs idle (gemv_spread_rows); larger ones about
+// kGemvLargeBlocksPerWg blocks of W per workgroup (the 151936 x 2560 LM
+// head: 48 rows; 38 to 99, and rows chosen to fill whole rounds of the CUs,
+// measured within noise of it).  Bounded by the LDS budget.
 int gemv_rows_per_block(int N, int K) {
     const int nb = K / jq4k::kQK;
     if (N <= kGemvSmallRowsPerCu * static_cast<long>(cu_count())) {
@@ -147,14 +146,15 @@ int gemv_rows_per_block(int N, int K) {
     return gemv_rows_for(kGemvLargeBlocksPerWg, 1, N, K, 1);
 }
 
-// Rows per workgroup inside a batched launch: a batch that fills the GPU
+// Rows per workgroup inside a batched launch.  A batch that fills the GPU
 // takes about kGemvBatchBlocksPerWg blocks of W per workgroup whatever the
-// row length, and at least 16 rows (a smaller one is spread over the CUs) (the decode layer: 51 rows at
-// K = 2560, 32 at 4096, 16 at 9728, 745 workgroups, all resident at once:
-// 14.0 us.  Measured slower: 13 rows at K = 9728 (782 workgroups, 17.0 us),
-// 52/33/14 rows (756, 15.5), more blocks for longer rows (55/36/17 to
-// 67/48/29, 15.3-17.1), 384 and 640 blocks, LDS padded to hold at most 3
-// or 4 workgroups per CU (19.5, 15.5)).
+// row length, and at least 16 rows; a smaller one is spread over the CUs.
+// The decode layer: 51 rows at K = 2560, 32 at 4096, 16 at 9728, 745
+// workgroups, all resident at once, 14.0 us.  Measured no better: 14 or 15
+// rows at K = 9728; slower: 13 (782 workgroups, 17.0 us, with an earlier
+// kernel), 52/33/14 rows (756, 15.5), more blocks for longer rows (55/36/17
+// to 67/48/29, 15.3-17.1), 384 and 640 blocks, LDS padded to hold at most 3
+// or 4 workgroups per CU (19.5, 15.5).
 int gemv_batch_rows(int N, int K) { return gemv_rows_for(kGemvBatchBlocksPerWg, 16, N, K, 1); }
 
 int run_gemv(const block_q4_K* W, const jq4k_bf16* X, float* Y, int N, int K, int R,
