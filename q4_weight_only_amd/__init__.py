@@ -200,6 +200,17 @@ def gemv(W, X, Y, stream=None):
     return Y
 
 
+def gemv_rows(W, X, Y, rows_per_block, stream=None):
+    """jq4k_gemv with an explicit number of rows of W per workgroup (0: the
+    library's choice); the results do not depend on it."""
+    M, N, K = _shapes(W, X, Y)
+    if M != 1:
+        raise ValueError("gemv_rows takes one token (M = 1)")
+    _check(_load().jq4k_gemv_rows(W.data_ptr(), X.data_ptr(), Y.data_ptr(), N, K,
+                                  int(rows_per_block), _stream(stream)), "jq4k_gemv_rows")
+    return Y
+
+
 def gemv_descs(problems):
     """ctypes array of GemvDesc from (W, X, Y) torch tensor triples."""
     arr = (GemvDesc * max(len(problems), 1))()

@@ -350,6 +350,59 @@ def test_gemv_batched_decode_step_groups(gpu):
             parity(got, Y, A, f"decode-step group {name}")
 
 
+def test_gemv_rows_per_block_any(gpu):
+    """jq4k_gemv_rows at row counts from 1 (a workgroup's rounds mostly idle
+    lanes, whose stores go to the spare slot) to the LDS budget's range:
+    every output equals jq4k_gemv's bit for bit (a row's sums do not depend
+    on the rows per workgroup) and meets the oracle bound."""
+    import q4_weight_only_amd as jq4k
+    g = np.random.default_rng(131)
+    # rows within the 96 KiB LDS budget: up to ~560 at K = 2560, ~120 at 9728
+    for N, K, rows in ((517, 2560, (1, 3, 16, 51, 200, 500)), (130, 9728, (1, 3, 16, 51, 120))):
+        W = qi.weight_bytes(g, N, K)
+        X = qi.activations(g, 1, K)
+        wd, xd = dev(W), dev(X).view(torch.bfloat16)
+        ref = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+        gpu.gemv(wd, xd, ref)
+        Y, A = oracle.gemm(W, X, N, K)
+        parity(host(ref), Y, A, f"gemv N={N} K={K}")
+        for R in rows:
+            announce(f"gemv_rows N={N} K={K} R={R}")
+            y = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda:0")
+            gpu.gemv_rows(wd, xd, y, R)
+            assert np.array_equal(host(y).view(np.uint32), host(ref).view(np.uint32)), (N, K, R)
+        # past the budget: refused before any launch
+        with pytest.raises(jq4k.Jq4kError):
+            gpu.gemv_rows(wd, xd, torch.empty((1, N), dtype=torch.float32, device="cuda:0"), 5000)
+
+
+def test_gemv_batched_sixteen_problems(gpu):
+    """A batched launch at its limit of 16 problems, of mixed shapes (rows 1
+    to 3000, K 256 to 16384, a repeated x): each output equals the
+    per-problem GEMV bit for bit and meets the oracle bound."""
+    g = np.random.default_rng(132)
+    shapes = [(1, 256), (2, 16384), (3000, 2560), (17, 768), (300, 4096), (64, 9728), (5, 512),
+              (1000, 1024), (129, 2560), (7, 7680), (2048, 256), (31, 3072), (256, 5120),
+              (90, 2560), (1, 1024), (700, 2304)]
+    shared_x = qi.activations(g, 1, 2560)
+    probs = []
+    for N, K in shapes:
+        X = shared_x if K == 2560 else qi.activations(g, 1, K)
+        probs.append((N, K, qi.weight_bytes(g, N, K), X))
+    Wd = [dev(W) for *_, W, _ in probs]
+    Xd = [dev(X).view(torch.bfloat16) for *_, X in probs]
+    Yb = [torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda:0")
+          for N, *_ in probs]
+    announce("gemv batched, 16 problems")
+    gpu.gemv_batched(list(zip(Wd, Xd, Yb)))
+    for (N, K, W, X), wd, xd, yb in zip(probs, Wd, Xd, Yb):
+        ys = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+        gpu.gemv(wd, xd, ys)
+        assert np.array_equal(host(yb).view(np.uint32), host(ys).view(np.uint32)), (N, K)
+        Y, A = oracle.gemm(W, X, N, K)
+        parity(host(yb), Y, A, f"batched N={N} K={K}")
+
+
 # ------------------------------------------------------------ M > 1 (MFMA)
 
 PATHS = ["mfma64", "mfma128", "mfma256", "mfma_big", "mfma_rw", "skinny"]
