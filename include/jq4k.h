@@ -228,7 +228,7 @@ int jq4k_gemm_batched_ws(const jq4k_gemm_desc *problems, int count, void *worksp
  * results and errors as jq4k_gemm_batched_ws (bit-identical outputs), plus
  * JQ4K_ESCRATCH, with nothing launched, when jq4k_gemm_workspace_size would
  * exceed JQ4K_SCRATCH_BYTES for these problems (a Qwen3-4B layer at M <= 64
- * needs 1.3 MB, its down projection alone 6.6 MB).  Every call on one GPU
+ * needs 1.8 MB, its down projection alone 6.6 MB).  Every call on one GPU
  * shares that GPU's buffer: calls that may overlap on one GPU (other streams,
  * other threads) race and must be serialised by the caller. */
 int jq4k_gemm_batched_noalloc(const jq4k_gemm_desc *problems, int count, hipStream_t stream);

@@ -209,7 +209,7 @@ def _ws_size(L, arr, count):
 
 def test_gemm_workspace_size(L):
     """Host-side sizing of the split-K workspace: the M = 33 layer splits
-    down in 2 (with 256 compute units, the count this host assumes without a
+    down and v in 2 (with 256 compute units, the count this host assumes without a
     GPU); M > 64 or one short problem needs none."""
     A, B, C = ALIGNED, ALIGNED2, ALIGNED3
     layer = _gemm_descs(*[(A, B, C, 33, n, k) for n, k in
@@ -217,7 +217,7 @@ def test_gemm_workspace_size(L):
                            (9728, 2560), (9728, 2560), (2560, 9728))])
     rc, n = _ws_size(L, layer, 7)
     assert rc == jq4k.OK
-    assert n == (40 * 4 + 255) // 256 * 256 + 40 * 2 * 64 * 64 * 4
+    assert n == (56 * 4 + 255) // 256 * 256 + (16 + 40) * 2 * 64 * 64 * 4
     for rows in (((A, B, C, 65, 4096, 9728),), ((A, B, C, 8, 64, 256),), ()):
         rc, n = _ws_size(L, _gemm_descs(*rows), len(rows))
         assert (rc, n) == (jq4k.OK, 0), rows

@@ -650,7 +650,7 @@ def test_register_w_m2048_full(gpu):
 
 def test_prefill_m33_all_layers_full(gpu):
     """M = 33 through all 36 layers (252 matmuls), each layer one grouped
-    split-K launch with a workspace (down in 2 K ranges): every output of
+    split-K launch with a workspace (down and v in 2 K ranges): every output of
     every projection against the oracle."""
     for layer in range(36):
         projs = [qi.prefill_projection(2, layer, p, 33) for p in range(7)]

@@ -135,18 +135,22 @@ def test_split_ranges_adjacent_on_one_xcd(driver):
                 i += S
 
 
+LAYER_M33 = [(33, 4096, 2560), (33, 1024, 2560), (33, 1024, 2560), (33, 2560, 4096),
+             (33, 9728, 2560), (33, 9728, 2560), (33, 2560, 9728)]
+
+
 def test_splitk_plan(driver):
     """The seven projections of a Qwen3-4B layer at M = 33: ranges of about
-    twice the shortest whole K (80 stages): every projection keeps whole K
-    but down, which splits in 2 (76 stages each); 560 workgroups, and a
-    workspace of one counter and S partial 64 x 64 tiles per split tile."""
-    layer = [(33, 4096, 2560), (33, 1024, 2560), (33, 1024, 2560), (33, 2560, 4096),
-             (33, 9728, 2560), (33, 9728, 2560), (33, 2560, 9728)]
-    S, items, ws = plan(driver, 64, 64, 512, layer)
-    assert S == [1, 1, 1, 1, 1, 1, 2]
-    assert items == 64 + 16 + 16 + 40 + 152 + 152 + 40 * 2
-    counters = 40
-    assert ws == (counters * 4 + 255) // 256 * 256 + 40 * 2 * 64 * 64 * 4
+    twice the shortest whole K (80 stages): down splits in 2 (76 stages
+    each).  That queues 65 entries per XCD against 64 resident workgroups,
+    so v (2 tiles per XCD, K = 2560) also splits in 2 and its half ranges
+    fill the last round: 536 workgroups, and a workspace of one counter and
+    S partial 64 x 64 tiles per split tile."""
+    S, items, ws = plan(driver, 64, 64, 512, LAYER_M33)
+    assert S == [1, 1, 2, 1, 1, 1, 2]
+    assert items == 64 + 16 + 16 * 2 + 40 + 152 + 152 + 40 * 2
+    counters = 16 + 40
+    assert ws == (counters * 4 + 255) // 256 * 256 + (16 * 2 + 40 * 2) * 64 * 64 * 4
     # down alone: too few tiles, so the target halves down to 16 stages
     S, items, _ = plan(driver, 64, 64, 512, [(33, 2560, 9728)])
     assert S == [10] and items == 400
@@ -164,3 +168,43 @@ def test_splitk_plan(driver):
         lens = [k / 64 / s for s, (_, _, k) in zip(S, shapes)]
         if min(k for _, _, k in shapes) >= 16 * 64 * 2:
             assert max(lens) <= 3 * min(lens) + 16
+
+
+def test_splitk_last_round(driver):
+    """The last-round rule of splitk_plan.  On the M = 33 layer the entries of
+    each XCD's queue past its 64 resident workgroups are all half ranges of
+    the problem it split (queued last, longest range first).  It leaves the
+    plan alone when no entry runs past a whole round, when no problem with
+    whole K covers the overflow in at most a quarter round of tiles, when
+    the halves would not be the shortest ranges, and for a single problem."""
+    S, items, _ = plan(driver, 64, 64, 512, LAYER_M33)
+    # the launch queues the problems longest K range first (stable)
+    order = sorted(range(7), key=lambda q: -LAYER_M33[q][2] / S[q])
+    shapes = [LAYER_M33[q][:2] for q in order]
+    splits = [S[q] for q in order]
+    rows = schedule(driver, 64, 64, 4, shapes, splits)
+    check(rows, 64, 64, shapes, splits)
+    for x in range(8):
+        queue = [r for r in rows[x::8] if r != (-1,)]
+        assert len(queue) == 67
+        assert all(order[i] == 2 and splits[i] == 2 for i, *_ in queue[64:])
+    # an exact round: 64 entries per XCD (512 tiles of one K), no change
+    S, items, ws = plan(driver, 64, 64, 512, [(33, 64 * 256, 2560), (33, 64 * 256, 2560)])
+    assert S == [1, 1] and items == 512 and ws == 0
+    # overflow of 8 per XCD, every problem too large to cover it in a
+    # quarter round (17 tiles per XCD): no change
+    shapes = [(33, 64 * 136, 2560)] * 4
+    S, items, ws = plan(driver, 64, 64, 512, shapes)
+    assert S == [1, 1, 1, 1] and items == 544 and ws == 0
+    # the problem with the fewest tiles (K = 5120) would halve to 2560, not
+    # shorter than the K = 2560 problems' whole ranges: the next one is split
+    shapes = [(33, 64 * 8 * 2, 5120), (33, 64 * 8 * 61, 2560), (33, 64 * 8 * 3, 2560)]
+    S, items, _ = plan(driver, 64, 64, 512, shapes)
+    assert S == [1, 1, 2] and items == 8 * (2 + 61 + 2 * 3)
+    # ties: the last given of the problems with the fewest tiles per XCD
+    shapes = [(33, 64 * 8 * 61, 2560), (33, 64 * 8 * 2, 2560), (33, 64 * 8 * 2, 2560)]
+    S, _, _ = plan(driver, 64, 64, 512, shapes)
+    assert S == [1, 1, 2]
+    # one problem past a round: never split by this rule (its own plan only)
+    S, _, _ = plan(driver, 64, 64, 512, [(33, 151936, 2560)])
+    assert S == [1]
