@@ -197,7 +197,9 @@ int jq4k_gemm_batched(const jq4k_gemm_desc *problems, int count, hipStream_t str
  * prefill, here at the short-prompt sizes).  There each output tile is only
  * 64 wide and a long row of W (K = 9728, say) would keep one workgroup busy
  * after the others finish; instead the K of such problems is cut into ranges
- * of whole blocks, one workgroup each.  Each range writes an fp32 partial tile
+ * of whole blocks, one workgroup each (and a small problem may be cut in two
+ * so that the workgroups left after the last full round of resident ones
+ * are half ranges, not whole tiles).  Each range writes an fp32 partial tile
  * to the workspace and the last to finish adds them in range order, so the
  * result is the same whichever finishes last, run to run.  Same problems,
  * results and errors as jq4k_gemm_batched; when no problem is split (M > 64,
