@@ -9,7 +9,7 @@ figure.  Every other workload of the benchmark suite is a leg of the same
 run: the single 2560 x 2560 GEMV, the 33-token prefill through 36 layers,
 the 2048-token layer, the LM head at M = 1 and M = 512, the fused SwiGLU and
 RMSNorm variants, the KV-cache convert, and the measured ceilings of this
-GPU (a streaming read and a matrix-instruction loop).
+GPU (streaming reads in two patterns and a matrix-instruction loop).
 
 Protocol.  Inputs are seeded synthetic tensors resident in HBM before timing.
 Weights rotate over enough identical copies (>= 1 GiB) that no step finds its
@@ -600,10 +600,13 @@ def kv_leg(torch, jq4k, args, traces):
 
 
 def ceilings_leg(torch, jq4k, args, traces):
-    """What this GPU reaches, beside the published peaks: a streaming read
-    (jq4k_probe_read, 16 bytes per load) of 1 GiB, and of the decode layer's
-    and the LM head's sizes rotated through 1 GiB, and a loop of
-    v_mfma_f32_32x32x16_bf16 on register operands (jq4k_probe_mfma)."""
+    """What this GPU reaches, beside the published peaks: streaming reads of
+    1 GiB, and of the decode layer's and the LM head's sizes rotated through
+    1 GiB, in two patterns (read_*: jq4k_probe_read, a grid striding over the
+    buffer with plain 16-byte loads; stream_*: jq4k_probe_stream, one
+    short-lived workgroup per 36 KB with non-temporal loads, the faster one
+    here), and a loop of v_mfma_f32_32x32x16_bf16 on register operands
+    (jq4k_probe_mfma)."""
     L = jq4k.raw()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wgs = 8 * cus
@@ -619,10 +622,15 @@ def ceilings_leg(torch, jq4k, args, traces):
             off = (i % pieces) * nbytes
             check(jq4k, L.jq4k_probe_read(buf.data_ptr() + off, nbytes, sink.data_ptr(), wgs,
                                           stream_ptr(torch)))
+        def st(i, nbytes=nbytes, pieces=pieces):
+            off = (i % pieces) * nbytes
+            check(jq4k, L.jq4k_probe_stream(buf.data_ptr() + off, nbytes, sink.data_ptr(),
+                                            stream_ptr(torch)))
         steps = 20 if nbytes == ROTATION_BYTES else 100
-        t = timed(torch, rd, steps, 3, not args.eager) / steps
-        out[name] = {"bytes": nbytes, "us": round(t * 1e6, 2), "GB_s": round(nbytes / t / 1e9, 1),
-                     "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        for key, fn in ((name, rd), (name.replace("read_", "stream_"), st)):
+            t = timed(torch, fn, steps, 3, not args.eager) / steps
+            out[key] = {"bytes": nbytes, "us": round(t * 1e6, 2), "GB_s": round(nbytes / t / 1e9, 1),
+                        "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
     iters = 4096
     mwgs = 4 * cus       # four workgroups of four waves per CU: four waves per SIMD
 

@@ -25,6 +25,15 @@ typedef struct ihipStream_t *hipStream_t;
 int jq4k_probe_read(const void *p, size_t bytes, uint32_t *sink, int workgroups,
                     hipStream_t stream);
 
+/* Streaming read of `bytes` (a multiple of 16) at device pointer p (16-byte
+ * aligned) in the pattern that reads HBM fastest here: one workgroup of 256
+ * threads per 36 KB, each thread nine non-temporal 16-byte loads in flight,
+ * every wave instruction 1 KB of consecutive bytes.  sink: device, at least
+ * 256 uint32, written only when the XOR of a thread's bytes has one magic
+ * value (it keeps the loads live).  Returns 0, -1 for a bad argument
+ * (nothing launched), or the launch's hipError_t. */
+int jq4k_probe_stream(const void *p, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* `iters` rounds of eight independent v_mfma_f32_32x32x16_bf16 (2 * 32 * 32 *
  * 16 flops each) per wave, register operands, `workgroups` workgroups of four
  * waves.  sink: device, one float per thread.  Returns 0, -1 for a bad

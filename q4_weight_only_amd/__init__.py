@@ -101,6 +101,8 @@ def _load():
         L.jq4k_dequant_bf16.restype = i
         L.jq4k_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i, vp]
         L.jq4k_probe_read.restype = i
+        L.jq4k_probe_stream.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.jq4k_probe_stream.restype = i
         L.jq4k_probe_mfma.argtypes = [l, vp, i, vp]
         L.jq4k_probe_mfma.restype = i
         L.jq4k_probe_mmq.argtypes = [l, vp, i, vp]
