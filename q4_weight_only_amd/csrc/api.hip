@@ -63,10 +63,11 @@ constexpr int kMaxDevices = 64;
 constexpr int kQuickReturn = 1;
 constexpr int kGemvMaxRows = 1024;
 constexpr int kGemvSmallRowsPerCu = 64;  // below this many rows per CU: small-matrix rule
-// blocks of W per workgroup for large single GEMVs (measured best on the
-// 151936 x 2560 LM head) and inside batched launches (measured best on the
-// seven projections of a decode layer: 1002 workgroups, all resident at once)
-constexpr int kGemvLargeBlocksPerWg = 480;
+// blocks of W per workgroup for large single GEMVs, at most (measured best
+// on the 151936 x 2560 LM head), and about, inside batched launches
+// (measured best on the seven projections of a decode layer: 745
+// workgroups, all resident at once)
+constexpr int kGemvLargeBlocksPerWg = 240;
 constexpr int kGemvBatchBlocksPerWg = 512;
 // x staged as binary16 with its sums takes 608 B of LDS per 256 values
 // (38 KB at the largest K); each block of W a workgroup owns adds 16 B
@@ -133,17 +134,22 @@ int gemv_spread_rows(long blocks, int problems, int N, int K, int mats) {
 
 // Rows per workgroup of the GEMV.  Matrices of up to kGemvSmallRowsPerCu
 // rows per compute unit take 16 rows per workgroup, or fewer where that
-// leaves CUs idle (gemv_spread_rows); larger ones about
-// kGemvLargeBlocksPerWg blocks of W per workgroup (the 151936 x 2560 LM
-// head: 48 rows; 38 to 99, and rows chosen to fill whole rounds of the CUs,
-// measured within noise of it).  Bounded by the LDS budget.
+// leaves CUs idle (gemv_spread_rows); larger ones as many whole rows as fit
+// in kGemvLargeBlocksPerWg blocks of W (the kernel's rounds take 128 blocks:
+// just under two rounds, short-lived workgroups).  The 151936 x 2560 LM
+// head: 24 rows, 39.6-39.9 us against 40.5-41.1 us with 48 (480 blocks,
+// the earlier rule; 36 to 76 rows measured 40.3-41.1).  A workgroup whose
+// blocks run just past a whole number of rounds pays a nearly empty round:
+// 26 rows (260 blocks) 46 us, 13 rows (130) 64 us.  Bounded by the LDS
+// budget.
 int gemv_rows_per_block(int N, int K) {
     const int nb = K / jq4k::kQK;
     if (N <= kGemvSmallRowsPerCu * static_cast<long>(cu_count())) {
         if ((N + 15) / 16 < cu_count()) return gemv_spread_rows(static_cast<long>(N) * nb, 1, N, K, 1);
         return gemv_rows_for(16 * nb, 1, N, K, 1);
     }
-    return gemv_rows_for(kGemvLargeBlocksPerWg, 1, N, K, 1);
+    const int R = kGemvLargeBlocksPerWg / nb;
+    return gemv_rows_for(R > 0 ? R * nb : nb, 1, N, K, 1);
 }
 
 // Rows per workgroup inside a batched launch.  A batch that fills the GPU
