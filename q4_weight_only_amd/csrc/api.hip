@@ -120,12 +120,19 @@ int gemv_rows_for(int per_wg, int min_rows, int N, int K, int mats) {
 // part of it beats fewer, longer workgroups (the 2560 x 2560 GEMV: 4.9 ->
 // 4.2 us with 11 rows instead of 16; a decode step of four dependent
 // grouped launches: 33.4 -> 29.8 us; two to four workgroups per CU
-// measured slower).
+// measured slower).  The rows then fill the kernel rounds (128 blocks)
+// that share needs, so that no round runs nearly empty: the same time per
+// workgroup, fewer workgroups (decode step 28.8 -> 28.3 us, 2560 x 2560
+// GEMV 3.94 -> 3.88 us; one round fewer and more workgroups measured
+// slower).
 int gemv_spread_rows(long blocks, int problems, int N, int K, int mats) {
     const int nb = K / jq4k::kQK;
     const long slots = static_cast<long>(cu_count()) - problems;
     const long per_wg = slots > 0 ? (blocks + slots - 1) / slots : blocks;
-    long R = (per_wg + static_cast<long>(mats) * nb - 1) / (static_cast<long>(mats) * nb);
+    const long row_blocks = static_cast<long>(mats) * nb;
+    const long rounds = (per_wg + 127) / 128;
+    long R = rounds * 128 / row_blocks;
+    if (R < 1) R = (per_wg + row_blocks - 1) / row_blocks;
     if (R < 1) R = 1;
     if (R > N) R = N;
     while (R > 1 && jq4k::gemv_lds_bytes(nb, static_cast<int>(R), mats) > kGemvLdsLimit) --R;
