@@ -62,7 +62,6 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int kQuickReturn = 1;
 constexpr int kGemvMaxRows = 1024;
-constexpr int kGemvSmallRowsPerCu = 64;  // below this many rows per CU: small-matrix rule
 // blocks of W per workgroup for large single GEMVs, at most (measured best
 // on the 151936 x 2560 LM head), and about, inside batched launches
 // (measured best on the seven projections of a decode layer: 745
@@ -139,24 +138,29 @@ int gemv_spread_rows(long blocks, int problems, int N, int K, int mats) {
     return static_cast<int>(R);
 }
 
-// Rows per workgroup of the GEMV.  Matrices of up to kGemvSmallRowsPerCu
-// rows per compute unit take 16 rows per workgroup, or fewer where that
-// leaves CUs idle (gemv_spread_rows); larger ones as many whole rows as fit
-// in kGemvLargeBlocksPerWg blocks of W (the kernel's rounds take 128 blocks:
-// just under two rounds, short-lived workgroups).  The 151936 x 2560 LM
-// head: 24 rows, 39.6-39.9 us against 40.5-41.1 us with 48 (480 blocks,
-// the earlier rule; 36 to 76 rows measured 40.3-41.1).  A workgroup whose
-// blocks run just past a whole number of rounds pays a nearly empty round:
-// 26 rows (260 blocks) 46 us, 13 rows (130) 64 us.  Bounded by the LDS
+// Rows per workgroup of the GEMV.  A matrix that 16-row workgroups would
+// not spread over every CU takes the spread rule (gemv_spread_rows); a
+// larger one as many whole rows as fit in kGemvLargeBlocksPerWg blocks of W,
+// or 16 rows when that leaves CUs without a workgroup (4096 x 2560: 4.74 us
+// with 16 rows, 4.82 spread).  The
+// kernel's rounds take 128 blocks, so the budget is just under two rounds:
+// short-lived workgroups, none paying for a nearly empty round.  Measured:
+// the 151936 x 2560 LM head with 24 rows 39.6-39.9 us against 40.5-41.1 us
+// with 48 (480 blocks, the earlier rule; 36 to 76 rows 40.3-41.1); a
+// 9728 x 2560 projection alone 6.4 us against 8.0 with 16 rows (160 blocks,
+// 1.25 rounds), and with its RMSNorm fused 6.7 against 8.6.  The LM head
+// with 26 rows (260 blocks, just past two rounds) takes 46 us, with 13 rows
+// (130) 64 us.  The spread rule stays better for the 2560-row projections
+// (2560 x 9728: 7.05 us against 7.34 with 6 rows).  Bounded by the LDS
 // budget.
 int gemv_rows_per_block(int N, int K) {
     const int nb = K / jq4k::kQK;
-    if (N <= kGemvSmallRowsPerCu * static_cast<long>(cu_count())) {
-        if ((N + 15) / 16 < cu_count()) return gemv_spread_rows(static_cast<long>(N) * nb, 1, N, K, 1);
-        return gemv_rows_for(16 * nb, 1, N, K, 1);
-    }
-    const int R = kGemvLargeBlocksPerWg / nb;
-    return gemv_rows_for(R > 0 ? R * nb : nb, 1, N, K, 1);
+    const long spread_blocks = static_cast<long>(N) * nb;
+    if ((N + 15) / 16 < cu_count()) return gemv_spread_rows(spread_blocks, 1, N, K, 1);
+    int R = kGemvLargeBlocksPerWg / nb;
+    R = gemv_rows_for((R < 1 ? 1 : R) * nb, 1, N, K, 1);
+    if ((N + R - 1) / R >= cu_count()) return R;
+    return gemv_rows_for(16 * nb, 1, N, K, 1);
 }
 
 // Rows per workgroup inside a batched launch.  A batch that fills the GPU
@@ -512,6 +516,8 @@ int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16
     if (M == 1 && K <= JQ4K_GEMV_MAX_K) {
         // R rows of each matrix per workgroup: about as many blocks of the
         // two matrices together as a workgroup of a grouped launch streams
+        // (the 9728 x 2560 pair: 26 rows, 10.0 us; 12 rows, within the
+        // single GEMV's 240 blocks, 10.9 us)
         int R = gemv_rows_for(kGemvBatchBlocksPerWg / 2, 8, N, K, 2);
         if ((N + R - 1) / R < cu_count())
             R = gemv_spread_rows(2L * N * (K / jq4k::kQK), 1, N, K, 2);
