@@ -514,11 +514,14 @@ int jq4k_gemm_swiglu(const block_q4_K* Wg, const block_q4_K* Wu, const jq4k_bf16
     const uint8_t* wg = reinterpret_cast<const uint8_t*>(Wg);
     const uint8_t* wu = reinterpret_cast<const uint8_t*>(Wu);
     if (M == 1 && K <= JQ4K_GEMV_MAX_K) {
-        // R rows of each matrix per workgroup: about as many blocks of the
-        // two matrices together as a workgroup of a grouped launch streams
-        // (the 9728 x 2560 pair: 26 rows, 10.0 us; 12 rows, within the
-        // single GEMV's 240 blocks, 10.9 us)
-        int R = gemv_rows_for(kGemvBatchBlocksPerWg / 2, 8, N, K, 2);
+        // R rows of each matrix per workgroup: as many whole rows as fit,
+        // both matrices' blocks together, in the blocks a workgroup of a
+        // grouped launch streams (the 9728 x 2560 pair: 25 rows, 500 blocks,
+        // 9.2 us; 24 rows 9.2; 26 rows, 520 blocks just past four rounds,
+        // 10.1-10.2; 12 rows, the single GEMV's 240 blocks, 10.9)
+        const int nb = K / jq4k::kQK;
+        const int fit = kGemvBatchBlocksPerWg / (2 * nb);
+        int R = gemv_rows_for((fit < 1 ? 1 : fit) * nb, 8, N, K, 2);
         if ((N + R - 1) / R < cu_count())
             R = gemv_spread_rows(2L * N * (K / jq4k::kQK), 1, N, K, 2);
         return static_cast<int>(jq4k::launch_gemv_swiglu(wg, wu, X, H, N, K, R, stream));
